@@ -1,0 +1,99 @@
+"""Flattened, padded, sharded parameter layout -- the oracle's own version.
+
+What the pages fix:
+  * ZeRO: the model states are cut into N parts by data-parallel rank, and
+    each rank keeps and updates only its own 1/N ("dp-zero-fsdp", concepts,
+    "ZeRO-1 / 2 / 3").
+  * FSDP splits the model into units (e.g. one layer each) and gathers /
+    frees one unit at a time ("dp-zero-fsdp", concepts "FSDP" and figure 2).
+  * FSDP1 flattens a group of parameters, concatenates them into one flat
+    parameter and then shards that ("dp-zero-fsdp", follow-up "FSDP2 vs
+    FSDP1").
+  * A reduce-scatter gives each rank its slice of the summed buffer; an
+    all-gather concatenates the slices back ("dp-zero-fsdp", concepts
+    "reduce-scatter and all-gather"; "Behind the scenes...", section "ZeRO:
+    The Dial Between DDP and FSDP").
+
+Readings taken (where the pages are silent):
+  * Each unit of n elements is padded with zeros at its tail to the next
+    multiple of N, L = ceil(n / N) * N, and rank r owns the contiguous slice
+    [r * L/N, (r + 1) * L/N) of that unit.  Units are laid out one after the
+    other in the flat buffer.  A gradient bucket is such a unit.
+  * DDP has no sharding: the single "shard" is the whole buffer.
+"""
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+
+@dataclass(frozen=True)
+class Unit:
+    numel: int      # n_u, unpadded
+    padded: int     # L_u = ceil(n_u / N) * N
+    shard: int      # s_u = L_u / N
+    flat_off: int   # F_u = sum of L_j for j < u
+    shard_off: int  # R_u = sum of s_j for j < u
+
+
+@dataclass(frozen=True)
+class Layout:
+    n_ranks: int          # N (for DDP the number of replicas that average)
+    rank: int             # r
+    sharded: bool         # False for DDP
+    units: Tuple[Unit, ...]
+
+    @property
+    def flat_len(self) -> int:
+        return sum(u.padded for u in self.units)
+
+    @property
+    def shard_len(self) -> int:
+        return sum(u.shard for u in self.units)
+
+    def owned(self, u: int) -> Tuple[int, int]:
+        """Flat [begin, end) of this rank's slice of unit u."""
+        U = self.units[u]
+        b = U.flat_off + self.rank * U.shard
+        return b, b + U.shard
+
+    def owned_runs(self) -> List[Tuple[int, int, int]]:
+        """(flat_begin, shard_begin, length) for each unit, in unit order."""
+        return [(self.owned(i)[0], U.shard_off, U.shard) for i, U in enumerate(self.units)]
+
+
+def plan(unit_numel: Sequence[int], n_ranks: int, rank: int, sharded: bool = True) -> Layout:
+    if n_ranks < 1 or not (0 <= rank < n_ranks):
+        raise ValueError("need N >= 1 and 0 <= rank < N")
+    if len(unit_numel) < 1 or any(int(n) < 0 for n in unit_numel):
+        raise ValueError("need at least one unit, each of size >= 0")
+    parts = n_ranks if sharded else 1
+    units = []
+    flat = 0
+    shard = 0
+    for n in unit_numel:
+        n = int(n)
+        padded = -(-n // parts) * parts
+        s = padded // parts
+        units.append(Unit(n, padded, s, flat, shard))
+        flat += padded
+        shard += s
+    return Layout(n_ranks, rank if sharded else 0, sharded, tuple(units))
+
+
+def owner_of(layout: Layout, flat_index: int) -> Optional[Tuple[int, int, int]]:
+    """(rank, unit, index-within-the-rank's-unit-shard) that owns a flat
+    index, by walking the units; None if outside the buffer."""
+    for u, U in enumerate(layout.units):
+        if U.flat_off <= flat_index < U.flat_off + U.padded:
+            local = flat_index - U.flat_off
+            if not layout.sharded:
+                return 0, u, local
+            return local // U.shard, u, local % U.shard
+    return None
+
+
+def padding_mask(layout: Layout):
+    """Boolean list over the flat buffer: True at padding positions."""
+    mask = []
+    for U in layout.units:
+        mask.extend([False] * U.numel + [True] * (U.padded - U.numel))
+    return mask
