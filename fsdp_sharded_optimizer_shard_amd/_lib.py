@@ -1,0 +1,232 @@
+"""ctypes binding of libzeroshard (include/zero_shard.h).  Argument
+marshalling only: every step of the path runs in the HIP library.
+
+Buffers may be given as torch tensors (their data_ptr() is passed) or as raw
+integer device addresses.  `stream` defaults to torch's current stream on the
+current device.  Errors raise ZeroShardError with the library's message.
+There is no fallback: if the library is missing this module fails to import.
+"""
+import ctypes
+import os
+from typing import Optional, Sequence
+
+# torch first: its ROCm build ships its own HIP runtime (same soname,
+# libamdhip64.so.7).  Loading torch before the library makes the library bind
+# to that runtime, so device pointers and streams from torch are valid in it;
+# loading the library first would put a second HIP runtime in the process.
+import torch  # noqa: E402,F401
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libzeroshard.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+        "python -m fsdp_sharded_optimizer_shard_amd.build")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# enums (zero_shard.h)
+OK, ERR_INVALID_ARG, ERR_ALIGNMENT, ERR_OOM, ERR_HIP, ERR_UNSUPPORTED = range(6)
+DDP, STAGE1, STAGE2, STAGE3, FSDP, MEGATRON_DO = range(6)
+BF16, FP32 = 0, 1
+INDEX_FULL, INDEX_SHARD = 0, 1
+MAX_RANKS_PER_CALL = 64
+
+STRATEGY = {"ddp": DDP, "zero1": STAGE1, "zero1_allreduce": STAGE1, "zero2": STAGE2,
+            "zero3": STAGE3, "fsdp": FSDP, "megatron_do": MEGATRON_DO}
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+
+
+class _Grads(ctypes.Structure):
+    _fields_ = [("ptrs", ctypes.POINTER(ctypes.c_void_p)), ("index", ctypes.POINTER(ctypes.c_uint8)),
+                ("n", _I32), ("dtype", _I32), ("index_all", _I32), ("_reserved", _I32)]
+
+
+class AdamCfg(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("decoupled", _I32), ("step", _I64)]
+
+
+def adam_cfg(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, decoupled=False,
+             step=1) -> AdamCfg:
+    return AdamCfg(lr, beta1, beta2, eps, weight_decay, int(bool(decoupled)), int(step))
+
+
+_lib.zero_shard_init.argtypes = [ctypes.POINTER(_P), _I32, _I32, _I32, _I32, ctypes.POINTER(_I64)]
+_lib.zero_shard_init.restype = _I32
+_lib.zero_shard_destroy.argtypes = [_P]
+_lib.zero_shard_destroy.restype = None
+_lib.zero_layout_info.argtypes = [_P] + [ctypes.POINTER(_I64)] * 2 + [ctypes.POINTER(_I32)] * 4
+_lib.zero_layout_info.restype = _I32
+_lib.zero_layout_query.argtypes = [_P, _I32] + [ctypes.POINTER(_I64)] * 6
+_lib.zero_layout_query.restype = _I32
+_lib.zero_reduce_shard.argtypes = [_P, _I32, _I32, ctypes.POINTER(_Grads), _P, _P, _I64, _P]
+_lib.zero_reduce_shard.restype = _I32
+_lib.zero_reduce_partials_count.argtypes = [_P, _I32, _I32]
+_lib.zero_reduce_partials_count.restype = _I64
+_lib.zero_clip_coef.argtypes = [_P, _I64, ctypes.c_float, _P, _P, _P]
+_lib.zero_clip_coef.restype = _I32
+_lib.zero_adam_step.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _P, _P,
+                                ctypes.POINTER(_Grads), _P, _P, _P, _P, _I32, _P]
+_lib.zero_adam_step.restype = _I32
+_lib.zero_gather_params.argtypes = [_P, _I32, _I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P]
+_lib.zero_gather_params.restype = _I32
+_lib.zero_grad_accumulate.argtypes = [_P, _P, _I64, _P]
+_lib.zero_grad_accumulate.restype = _I32
+_lib.zero_status_str.argtypes = [_I32]
+_lib.zero_status_str.restype = ctypes.c_char_p
+_lib.zero_last_error.argtypes = []
+_lib.zero_last_error.restype = ctypes.c_char_p
+
+EXPORTS = ("zero_shard_init", "zero_shard_destroy", "zero_layout_info", "zero_layout_query",
+           "zero_reduce_shard", "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
+           "zero_gather_params", "zero_grad_accumulate", "zero_status_str", "zero_last_error")
+
+
+class ZeroShardError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        msg = _lib.zero_last_error().decode(errors="replace")
+        super().__init__(f"{fn}: {_lib.zero_status_str(status).decode()} ({status}): {msg}")
+
+
+def _check(status: int, fn: str) -> None:
+    if status != OK:
+        raise ZeroShardError(status, fn)
+
+
+def _addr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Layout:
+    """An owned zero_layout (host memory).  Use shard_init() to make one."""
+
+    def __init__(self, handle: int, units: Sequence[int]):
+        self._h = handle
+        self.units = list(units)
+
+    @property
+    def handle(self) -> int:
+        if not self._h:
+            raise ValueError("layout is destroyed")
+        return self._h
+
+    def destroy(self) -> None:
+        if self._h:
+            _lib.zero_shard_destroy(self._h)
+            self._h = None
+
+    __del__ = destroy
+
+    def info(self) -> dict:
+        f, s = _I64(), _I64()
+        nu, wn, r, st = _I32(), _I32(), _I32(), _I32()
+        _check(_lib.zero_layout_info(self.handle, ctypes.byref(f), ctypes.byref(s), ctypes.byref(nu),
+                                     ctypes.byref(wn), ctypes.byref(r), ctypes.byref(st)),
+               "zero_layout_info")
+        return {"flat_len": f.value, "shard_len": s.value, "n_units": nu.value,
+                "world_n": wn.value, "rank": r.value, "strategy": st.value}
+
+    def query(self, unit: int) -> dict:
+        v = [_I64() for _ in range(6)]
+        _check(_lib.zero_layout_query(self.handle, unit, *[ctypes.byref(x) for x in v]),
+               "zero_layout_query")
+        keys = ("numel", "padded_len", "flat_off", "shard_len", "shard_off", "rank_flat_off")
+        return dict(zip(keys, (x.value for x in v)))
+
+    @property
+    def flat_len(self) -> int:
+        return self.info()["flat_len"]
+
+    @property
+    def shard_len(self) -> int:
+        return self.info()["shard_len"]
+
+
+def shard_init(strategy, world_n: int, rank: int, unit_numel: Sequence[int]) -> Layout:
+    s = STRATEGY[strategy] if isinstance(strategy, str) else int(strategy)
+    arr = (_I64 * len(unit_numel))(*[int(u) for u in unit_numel]) if len(unit_numel) else None
+    h = _P()
+    _check(_lib.zero_shard_init(ctypes.byref(h), s, world_n, rank, len(unit_numel), arr),
+           "zero_shard_init")
+    return Layout(h.value, unit_numel)
+
+
+class Grads:
+    """Marshalled zero_grads; keeps its ctypes arrays alive."""
+
+    def __init__(self, bufs, dtype: int = BF16, index=INDEX_FULL):
+        ptrs = [_addr(b) for b in bufs]
+        self._ptrs = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+        self._index = None
+        idx_all = INDEX_FULL
+        if isinstance(index, int):
+            idx_all = index
+        else:
+            self._index = (ctypes.c_uint8 * len(index))(*[int(i) for i in index])
+        self.s = _Grads(self._ptrs, self._index, len(ptrs), dtype, idx_all, 0)
+
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def reduce_partials_count(layout: Layout, unit_begin: int, unit_end: int) -> int:
+    return _lib.zero_reduce_partials_count(layout.handle, unit_begin, unit_end)
+
+
+def reduce_shard(layout: Layout, unit_begin: int, unit_end: int, grads: Grads, out,
+                 sumsq_partials=None, n_partials: int = 0, stream=None) -> None:
+    _check(_lib.zero_reduce_shard(layout.handle, unit_begin, unit_end, grads.ref() if grads else None,
+                                  _addr(out), _addr(sumsq_partials), n_partials, _stream(stream)),
+           "zero_reduce_shard")
+
+
+def clip_coef(partials, n: int, max_norm: float, coef_out, norm_out=None, stream=None) -> None:
+    _check(_lib.zero_clip_coef(_addr(partials), n, max_norm, _addr(coef_out), _addr(norm_out),
+                               _stream(stream)), "zero_clip_coef")
+
+
+def adam_step(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, master, m, v,
+              param_out, param_index: int = INDEX_FULL, grad_fp32=None, clip_coef=None,
+              grads: Optional[Grads] = None, stream=None) -> None:
+    _check(_lib.zero_adam_step(layout.handle, unit_begin, unit_end, ctypes.byref(cfg),
+                               _addr(grad_fp32), _addr(clip_coef), grads.ref() if grads else None,
+                               _addr(master), _addr(m), _addr(v), _addr(param_out), param_index,
+                               _stream(stream)), "zero_adam_step")
+
+
+def gather_params(layout: Layout, unit_begin: int, unit_end: int, shards, param_full,
+                  stream=None) -> None:
+    ptrs = [_addr(s) for s in shards]
+    arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
+    _check(_lib.zero_gather_params(layout.handle, unit_begin, unit_end, arr, len(ptrs),
+                                   _addr(param_full), _stream(stream)), "zero_gather_params")
+
+
+def grad_accumulate(main_grad, micro_bf16, n: int, stream=None) -> None:
+    _check(_lib.zero_grad_accumulate(_addr(main_grad), _addr(micro_bf16), n, _stream(stream)),
+           "zero_grad_accumulate")
+
+
+def raw():
+    """The ctypes library object (for tests of the exported symbols)."""
+    return _lib

@@ -1,0 +1,238 @@
+/*
+ * zero_shard.h -- C ABI of the per-rank sharded mixed-precision optimizer
+ * step for one AMD Instinct MI355X (gfx950) GPU.
+ *
+ * One data-parallel rank's step, seen from its own GPU, with the N ranks'
+ * gradient buffers resident in this GPU's memory:
+ *   reduce    the N ranks' gradients into this rank's 1/N slice, in fp32,
+ *             divided by N -- the arithmetic of a reduce-scatter
+ *             ("DP, ZeRO-1/2/3, FSDP" notes, concepts "reduce-scatter and
+ *             all-gather"; "Data Parallel, ZeRO and FSDP", plain DDP);
+ *   adam      Adam / AdamW on the slice's fp32 master, m and v (the 12 bytes
+ *             per parameter that ZeRO shards; "DP, ZeRO-1/2/3, FSDP" notes,
+ *             concepts "Model states" and "ZeRO-1 / 2 / 3"); the update
+ *             equations are Kingma & Ba (2015) Algorithm 1, with
+ *             Loshchilov & Hutter (2019) decoupled decay for AdamW;
+ *   cast      the new master rounded to bf16 (round to nearest even) and
+ *             stored at the rank's offsets of the flat parameter buffer;
+ *   gather    the other ranks' bf16 slices packed into the full flat buffer
+ *             -- the data movement of an all-gather.
+ * Plus the DDP variant (no sharding: every replica averages and updates the
+ * whole buffer) and the Megatron distributed-optimizer pieces (fp32 main
+ * gradient accumulation; fp32 gradients reduced; "DP, ZeRO-1/2/3, FSDP"
+ * notes, worked example, note under the Megatron row).
+ *
+ * LAYOUT (FSDP1-style flat parameter; "DP, ZeRO-1/2/3, FSDP" notes,
+ * follow-up "FSDP2 vs FSDP1"): the parameters form units u = 0..U-1 of n_u
+ * elements (a layer, or a gradient bucket).  Each unit is padded with zeros
+ * at its tail to L_u = ceil(n_u / N) * N and the units are concatenated:
+ *     F_u = sum_{j<u} L_j          (flat offset of unit u)
+ *     s_u = L_u / N                (each rank's slice of unit u)
+ *     R_u = sum_{j<u} s_j          (offset of unit u in a rank's shard)
+ * Rank r owns flat elements [F_u + r*s_u, F_u + (r+1)*s_u) of every unit.
+ * Under ZERO_DDP nothing is sharded: s_u = L_u = n_u and every rank "owns"
+ * the whole buffer.
+ *
+ * RANGES AND INDEXING.  Every compute call covers a contiguous range of
+ * units [unit_begin, unit_end) and every buffer pointer passed to it
+ * addresses the first element of that range:
+ *   ZERO_INDEX_FULL  buffer over the flat layout: element j of rank q's
+ *                    slice of unit u is at (F_u - F_begin) + q*s_u + j;
+ *   ZERO_INDEX_SHARD buffer over one rank's shard: element j of unit u is at
+ *                    (R_u - R_begin) + j.
+ * With unit_begin = 0 these are plain whole-buffer offsets; with a single
+ * unit they address per-unit buffers (FSDP's gather / free per unit).
+ * fp32 master, m and v are always shard-indexed.
+ *
+ * CONVENTIONS.
+ *   - Lengths are element counts (int64_t).  Data pointers are DEVICE
+ *     pointers owned by the caller; pointer ARRAYS (rank lists) and config
+ *     structs are HOST memory, read during the call only.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every compute call
+ *     only enqueues work on it and never synchronises.
+ *   - Arguments are validated on the host before anything is launched; on
+ *     any error nothing is launched and no buffer is touched.  Launch
+ *     failures return ZERO_ERR_HIP.  zero_last_error() returns a text
+ *     description of the last error on the calling thread.
+ *   - The library allocates no device memory; a layout is host memory only
+ *     and is immutable after init (safe to share between threads).
+ *   - Calls that write disjoint buffers may run concurrently on different
+ *     streams.  An fp32 buffer pointer must be 4-byte aligned and a bf16
+ *     one 2-byte aligned; 16-byte aligned buffers with slice offsets that are
+ *     multiples of 8 take the 128-bit vector path, others a scalar path with
+ *     identical results.
+ *   - At most ZERO_MAX_RANKS_PER_CALL rank buffers per reduce call.
+ *   - Arithmetic: fp32, one IEEE-754 rounding per operation, no fused
+ *     multiply-add; the N ranks are summed in ascending rank order from +0
+ *     and the sum divided by N; results do not depend on the launch shape.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZERO_MAX_RANKS_PER_CALL 64
+
+typedef enum zero_status {
+    ZERO_OK = 0,
+    ZERO_ERR_INVALID_ARG = 1, /* null / out-of-range / inconsistent argument */
+    ZERO_ERR_ALIGNMENT = 2,   /* pointer not aligned to its element size     */
+    ZERO_ERR_OOM = 3,         /* host allocation failed                       */
+    ZERO_ERR_HIP = 4,         /* a HIP runtime call or launch failed          */
+    ZERO_ERR_UNSUPPORTED = 5  /* valid request outside this library's limits  */
+} zero_status;
+
+/* Who holds what ("DP, ZeRO-1/2/3, FSDP" notes, figure 1 and worked example;
+   "Data Parallel, ZeRO and FSDP", ZeRO/FSDP table).  Only ZERO_DDP changes
+   the layout (unsharded); the others record the caller's strategy. */
+typedef enum zero_strategy {
+    ZERO_DDP = 0,
+    ZERO_STAGE1 = 1,
+    ZERO_STAGE2 = 2,
+    ZERO_STAGE3 = 3,
+    ZERO_FSDP = 4,
+    ZERO_MEGATRON_DO = 5
+} zero_strategy;
+
+typedef enum zero_dtype { ZERO_BF16 = 0, ZERO_FP32 = 1 } zero_dtype;
+
+typedef enum zero_index { ZERO_INDEX_FULL = 0, ZERO_INDEX_SHARD = 1 } zero_index;
+
+typedef struct zero_layout zero_layout;
+
+/* The N ranks' gradient buffers for one call, all of one dtype (bf16 as raw
+   uint16 bit patterns, or fp32). */
+typedef struct zero_grads {
+    const void *const *ptrs; /* host array of n device pointers, rank order;
+                                a NULL entry is an error (missing replica)  */
+    const uint8_t *index;    /* host array of n zero_index values, or NULL
+                                for all `index_all`                          */
+    int32_t n;               /* must equal the layout's world_n             */
+    int32_t dtype;           /* zero_dtype                                  */
+    int32_t index_all;       /* zero_index used when `index` is NULL        */
+    int32_t _reserved;
+} zero_grads;
+
+/* Adam / AdamW hyper-parameters of one step.  The step scalars 1 - beta1,
+   1 - beta2, 1 - beta1^t, 1 - beta2^t and 1 - lr*wd are evaluated in fp64
+   from these fp32 values and rounded once to fp32. */
+typedef struct zero_adam_cfg {
+    float lr;
+    float beta1;        /* in [0, 1) */
+    float beta2;        /* in [0, 1) */
+    float eps;          /* >= 0 */
+    float weight_decay; /* >= 0; 0 disables both decay forms */
+    int32_t decoupled;  /* 1: AdamW, p *= 1 - lr*wd; 0: L2, g += wd*p */
+    int64_t step;       /* t >= 1, supplied by the caller every call */
+} zero_adam_cfg;
+
+/* ------------------------------------------------------------ layout -- */
+
+/* Plan the layout of one rank: `n_units` units of unpadded sizes
+   `unit_numel` (host array, each >= 0, at least one unit), `world_n` >= 1
+   ranks, this rank `rank` in [0, world_n).  Host memory only; no HIP call.
+   *out receives a layout to free with zero_shard_destroy. */
+zero_status zero_shard_init(zero_layout **out, zero_strategy strategy,
+                            int32_t world_n, int32_t rank, int32_t n_units,
+                            const int64_t *unit_numel);
+
+void zero_shard_destroy(zero_layout *layout);
+
+/* Whole-layout sizes: padded flat length sum L_u, this rank's shard length
+   sum s_u.  Any output pointer may be NULL. */
+zero_status zero_layout_info(const zero_layout *layout, int64_t *flat_len,
+                             int64_t *shard_len, int32_t *n_units,
+                             int32_t *world_n, int32_t *rank,
+                             int32_t *strategy);
+
+/* Per-unit numbers (see LAYOUT): n_u, L_u, F_u, s_u, R_u and the rank's
+   flat offset F_u + r*s_u.  Any output pointer may be NULL. */
+zero_status zero_layout_query(const zero_layout *layout, int32_t unit,
+                              int64_t *numel, int64_t *padded_len,
+                              int64_t *flat_off, int64_t *shard_len,
+                              int64_t *shard_off, int64_t *rank_flat_off);
+
+/* ------------------------------------------------------------ reduce -- */
+
+/* Reduce-scatter arithmetic: for every element of this rank's slices of
+   units [unit_begin, unit_end),
+       out[i] = (G_0[i] + G_1[i] + ... + G_{N-1}[i]) / N      (fp32)
+   with G_q indexed as grads->index says.  `out` is shard-indexed fp32.
+   If `sumsq_partials` is non-NULL it receives exactly
+   zero_reduce_partials_count(...) fp64 partial sums of out[i]^2 (summed
+   exactly from fp32 squares), for the global-norm clip; `n_partials` is the
+   capacity of that buffer. */
+zero_status zero_reduce_shard(const zero_layout *layout, int32_t unit_begin,
+                              int32_t unit_end, const zero_grads *grads,
+                              float *out, double *sumsq_partials,
+                              int64_t n_partials, void *stream);
+
+/* Number of fp64 partials zero_reduce_shard writes for a range (a fixed
+   function of the range; independent of the device). */
+int64_t zero_reduce_partials_count(const zero_layout *layout,
+                                   int32_t unit_begin, int32_t unit_end);
+
+/* Global gradient-norm clip coefficient (not defined on the pages; PyTorch
+   clip_grad_norm_ semantics): norm = sqrt(sum of the n partials, added in
+   index order in fp64), *coef_out = min(1, fp32(max_norm / (norm + 1e-6))).
+   `partials`, `coef_out` (one float) and `norm_out` (one double, may be
+   NULL) are device pointers.  n >= 1, max_norm > 0. */
+zero_status zero_clip_coef(const double *partials, int64_t n, float max_norm,
+                           float *coef_out, double *norm_out, void *stream);
+
+/* --------------------------------------------------------- Adam step -- */
+
+/* Adam / AdamW on this rank's slices of units [unit_begin, unit_end), then
+   bf16 rounding of the new master into `param_out`.
+   Gradient source, exactly one of:
+     grad_fp32 != NULL: shard-indexed fp32 averaged gradient (from
+                        zero_reduce_shard), multiplied by *clip_coef (a
+                        device float; NULL means 1);
+     grads != NULL:     fused path -- the N ranks' buffers are reduced
+                        (as zero_reduce_shard) in the same pass, so each
+                        byte crosses HBM once.  clip_coef must be NULL.
+   master, m, v: shard-indexed fp32, updated in place.
+   param_out: bf16 (uint16) written at the rank's offsets; `param_index`
+   says whether it is the full flat buffer (ZERO_INDEX_FULL: elements of
+   the other ranks are not touched) or the rank's own shard buffer
+   (ZERO_INDEX_SHARD, ZeRO-3 / FSDP). */
+zero_status zero_adam_step(const zero_layout *layout, int32_t unit_begin,
+                           int32_t unit_end, const zero_adam_cfg *cfg,
+                           const float *grad_fp32, const float *clip_coef,
+                           const zero_grads *grads, float *master, float *m,
+                           float *v, uint16_t *param_out, int32_t param_index,
+                           void *stream);
+
+/* ------------------------------------------------------------ gather -- */
+
+/* All-gather data movement: for every rank q < n with shards[q] != NULL
+   and every element j of rank q's slice of unit u in the range,
+       param_full[(F_u - F_begin) + q*s_u + j] = shards[q][(R_u - R_begin) + j]
+   Bit copies.  `shards` is a host array of n = world_n device pointers
+   (NULL entries are skipped -- typically this rank's own, already written by
+   zero_adam_step); param_full is the full flat bf16 buffer of the range. */
+zero_status zero_gather_params(const zero_layout *layout, int32_t unit_begin,
+                               int32_t unit_end, const uint16_t *const *shards,
+                               int32_t n, uint16_t *param_full, void *stream);
+
+/* ------------------------------------------------------- accumulation -- */
+
+/* Megatron-style fp32 main-gradient accumulation of one micro-batch:
+   main_grad[i] = main_grad[i] + float(micro_bf16[i]) for i < n. */
+zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro_bf16,
+                                 int64_t n, void *stream);
+
+/* ---------------------------------------------------------- errors -- */
+
+const char *zero_status_str(zero_status status);
+const char *zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

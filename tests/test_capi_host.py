@@ -1,0 +1,208 @@
+"""Host-side tests of libzeroshard (no GPU needed).
+
+  * The library loads and exports every function include/zero_shard.h
+    declares.
+  * zero_shard_init / zero_layout_query agree bit-exactly with the oracle's
+    own layout (a separate implementation) on many layouts, including the
+    five workload shapes.
+  * Argument validation returns an error code, with a message, before
+    anything is launched: missing replica (NULL rank buffer), bad N / rank,
+    bad unit range, misalignment, too many ranks per call, bad Adam config.
+    Every call here uses fake device addresses and the null stream, so a
+    validation miss would surface as a HIP error, never as a silent launch.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from fsdp_sharded_optimizer_shard_amd import zs
+from oracle.layout import plan
+from synthetic import WORKLOADS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "zero_shard.h")
+FAKE = 0x7f0000000000          # 16-byte aligned fake device address, never dereferenced
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(zero_[a-z_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_function():
+    declared = header_functions()
+    assert len(declared) >= 12
+    lib = zs.raw()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(zs.EXPORTS) == declared
+
+
+def _same_as_oracle(strategy, units, n, r):
+    L = zs.shard_init(strategy, n, r, units)
+    O = plan(units, n, r, sharded=strategy != "ddp")
+    info = L.info()
+    assert info["flat_len"] == O.flat_len and info["shard_len"] == O.shard_len
+    assert info["n_units"] == len(units) and info["world_n"] == n
+    for u, U in enumerate(O.units):
+        q = L.query(u)
+        assert q == {"numel": U.numel, "padded_len": U.padded, "flat_off": U.flat_off,
+                     "shard_len": U.shard, "shard_off": U.shard_off,
+                     "rank_flat_off": O.owned(u)[0]}, (units, n, r, u)
+    L.destroy()
+
+
+@pytest.mark.parametrize("cfg", sorted(WORKLOADS))
+def test_workload_layouts_match_oracle(cfg):
+    w = WORKLOADS[cfg]
+    for r in sorted({0, 1, w.n_ranks - 1}):
+        _same_as_oracle(w.strategy, list(w.units), w.n_ranks, r)
+
+
+@settings(max_examples=200, deadline=None)
+@given(units=st.lists(st.integers(0, 5000), min_size=1, max_size=40),
+       n=st.integers(1, 130), data=st.data(),
+       strategy=st.sampled_from(["ddp", "zero1", "zero2", "zero3", "fsdp", "megatron_do"]))
+def test_random_layouts_match_oracle(units, n, data, strategy):
+    r = data.draw(st.integers(0, n - 1))
+    _same_as_oracle(strategy, units, n, r)
+
+
+def test_huge_layout_offsets_are_int64():
+    units = [2 ** 40, 3, 2 ** 41 + 7]
+    _same_as_oracle("fsdp", units, 64, 63)
+
+
+# ---------------------------------------------------------------- errors --
+
+def _err(fn, *a, **kw):
+    with pytest.raises(zs.ZeroShardError) as e:
+        fn(*a, **kw)
+    return e.value
+
+
+@pytest.mark.parametrize("n,r,units", [(0, 0, [8]), (4, 4, [8]), (4, -1, [8]), (4, 0, []),
+                                       (4, 0, [8, -1])])
+def test_init_rejects_bad_arguments(n, r, units):
+    e = _err(zs.shard_init, "zero2", n, r, units)
+    assert e.status == zs.ERR_INVALID_ARG
+
+
+def test_init_rejects_overflow():
+    e = _err(zs.shard_init, "zero2", 8, 0, [2 ** 62, 2 ** 62])
+    assert e.status == zs.ERR_INVALID_ARG and "overflow" in str(e)
+
+
+def test_query_rejects_bad_unit():
+    L = zs.shard_init("zero2", 4, 1, [100, 200])
+    assert _err(L.query, 2).status == zs.ERR_INVALID_ARG
+    assert _err(L.query, -1).status == zs.ERR_INVALID_ARG
+
+
+def _layout(n=4, units=(4096, 100)):
+    return zs.shard_init("zero2", n, 1, list(units))
+
+
+def _adam(L, ub=0, ue=2, cfg=None, grads="ok", master=FAKE, pout=FAKE, **kw):
+    if grads == "ok":
+        grads = zs.Grads([FAKE] * L.info()["world_n"], zs.BF16, zs.INDEX_FULL)
+    cfg = cfg or zs.adam_cfg(step=1)
+    zs.adam_step(L, ub, ue, cfg, master, FAKE, FAKE, pout, grads=grads, stream=0, **kw)
+
+
+def test_missing_replica_is_rejected():
+    L = _layout()
+    g = zs.Grads([FAKE, FAKE, None, FAKE], zs.BF16, zs.INDEX_FULL)
+    e = _err(_adam, L, 0, 2, None, g)
+    assert e.status == zs.ERR_INVALID_ARG and "rank 2" in str(e) and "missing" in str(e)
+
+
+def test_rank_count_must_match_layout():
+    L = _layout()
+    g = zs.Grads([FAKE] * 3, zs.BF16, zs.INDEX_FULL)
+    assert _err(_adam, L, 0, 2, None, g).status == zs.ERR_INVALID_ARG
+
+
+def test_too_many_ranks_per_call_is_unsupported():
+    L = zs.shard_init("fsdp", 65, 0, [65 * 16])
+    g = zs.Grads([FAKE] * 65, zs.BF16, zs.INDEX_SHARD)
+    assert _err(_adam, L, 0, 1, None, g).status == zs.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("ub,ue", [(-1, 1), (0, 3), (2, 1)])
+def test_bad_unit_range(ub, ue):
+    assert _err(_adam, _layout(), ub, ue).status == zs.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("cfg", [zs.adam_cfg(step=0), zs.adam_cfg(beta1=1.0), zs.adam_cfg(beta2=-0.1),
+                                 zs.adam_cfg(eps=-1.0), zs.adam_cfg(weight_decay=-0.01),
+                                 zs.adam_cfg(lr=float("nan"))])
+def test_bad_adam_config(cfg):
+    assert _err(_adam, _layout(), 0, 2, cfg).status == zs.ERR_INVALID_ARG
+
+
+def test_exactly_one_gradient_source():
+    L = _layout()
+    assert _err(_adam, L, 0, 2, None, None).status == zs.ERR_INVALID_ARG
+    assert _err(_adam, L, 0, 2, None, "ok", grad_fp32=FAKE).status == zs.ERR_INVALID_ARG
+    # the fused path cannot take a clip coefficient
+    assert _err(_adam, L, 0, 2, None, "ok", clip_coef=FAKE).status == zs.ERR_INVALID_ARG
+
+
+def test_misaligned_buffers():
+    L = _layout()
+    assert _err(_adam, L, 0, 2, None, "ok", FAKE + 2).status == zs.ERR_ALIGNMENT
+    assert _err(_adam, L, 0, 2, None, "ok", FAKE, FAKE + 1).status == zs.ERR_ALIGNMENT
+    g = zs.Grads([FAKE, FAKE + 1, FAKE, FAKE], zs.BF16, zs.INDEX_FULL)
+    assert _err(_adam, L, 0, 2, None, g).status == zs.ERR_ALIGNMENT
+
+
+def test_bad_index_and_dtype():
+    L = _layout()
+    g = zs.Grads([FAKE] * 4, 7, zs.INDEX_FULL)
+    assert _err(_adam, L, 0, 2, None, g).status == zs.ERR_INVALID_ARG
+    g = zs.Grads([FAKE] * 4, zs.BF16, [0, 1, 2, 0])
+    assert _err(_adam, L, 0, 2, None, g).status == zs.ERR_INVALID_ARG
+
+
+def test_reduce_validation():
+    L = _layout()
+    g = zs.Grads([FAKE] * 4, zs.BF16, zs.INDEX_FULL)
+    need = zs.reduce_partials_count(L, 0, 2)
+    assert need >= 1
+    e = _err(zs.reduce_shard, L, 0, 2, g, FAKE, FAKE, need - 1, 0)
+    assert e.status == zs.ERR_INVALID_ARG
+    assert _err(zs.reduce_shard, L, 0, 2, g, None, None, 0, 0).status == zs.ERR_INVALID_ARG
+    assert zs.reduce_partials_count(L, 0, 3) == -1
+
+
+def test_partials_count_is_a_fixed_function_of_the_range():
+    L = zs.shard_init("zero2", 8, 0, [25_000_000] * 4 + [24_439_808])
+    per = [zs.reduce_partials_count(L, u, u + 1) for u in range(5)]
+    assert per == [min(2048, -(-3_125_000 // 2048))] * 4 + [min(2048, -(-3_054_976 // 2048))]
+    assert zs.reduce_partials_count(L, 0, 5) == 2048       # one launch of <= 32 units
+    L = zs.shard_init("fsdp", 64, 0, [64 * 4096] * 40)     # 40 units -> two launches
+    assert zs.reduce_partials_count(L, 0, 40) == 32 * 2 + 8 * 2
+
+
+def test_gather_and_accumulate_and_clip_validation():
+    L = _layout()
+    assert _err(zs.gather_params, L, 0, 2, [FAKE] * 3, FAKE, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.gather_params, L, 0, 2, [FAKE] * 4, FAKE + 1, 0).status == zs.ERR_ALIGNMENT
+    assert _err(zs.grad_accumulate, None, FAKE, 10, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.grad_accumulate, FAKE + 2, FAKE, 10, 0).status == zs.ERR_ALIGNMENT
+    assert _err(zs.clip_coef, FAKE, 0, 1.0, FAKE, None, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.clip_coef, FAKE, 4, 0.0, FAKE, None, 0).status == zs.ERR_INVALID_ARG
+
+
+def test_empty_work_launches_nothing():
+    # zero-sized units and n = 0 accumulation succeed without touching HIP
+    L = zs.shard_init("zero2", 4, 0, [0, 0])
+    _adam(L, 0, 2)
+    zs.grad_accumulate(FAKE, FAKE, 0, 0)
+    zs.gather_params(L, 0, 2, [FAKE] * 4, FAKE, 0)
