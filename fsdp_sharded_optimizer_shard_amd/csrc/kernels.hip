@@ -39,11 +39,13 @@ constexpr int kThreads = 256;
 constexpr int kVec = 8;                     // elements per thread per tile
 constexpr int kTile = kThreads * kVec;      // elements per tile
 constexpr int kMaxSegs = 32;                // units per launch (kernarg table)
-constexpr int kReduceGrid = 2048;           // fixed so the partial count is fixed
+constexpr int kWaves = kThreads / 64;       // waves per block = partials per tile
+constexpr int kWaveElems = kTile / kWaves;  // elements of a tile per wave
 constexpr int kMaxRanks = ZERO_MAX_RANKS_PER_CALL;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // One unit's slice inside a launch's tile space.
 struct Seg {
@@ -51,7 +53,7 @@ struct Seg {
     int64_t shard_off;  // R_u - R_begin: slice start in shard-indexed buffers
     int64_t full_off;   // (F_u - F_begin) + r*s_u: slice start in full buffers
     int64_t tile0;      // first tile of this slice
-    int64_t vec;        // 1 if both offsets are multiples of 8 (vector path)
+    int64_t vec;        // 1 if both offsets are multiples of 4 (vector path)
 };
 
 struct AdamScalars {
@@ -76,7 +78,7 @@ struct StepArgs {
     const float *gin;    // kApply: shard-indexed averaged gradient
     const float *clip;   // kApply: device clip coefficient or null
     float *gout;         // kReduce: shard-indexed averaged gradient
-    double *partials;    // kReduce: one fp64 sum of squares per block, or null
+    double *partials;    // kReduce: one fp64 sum of squares per wave and tile, or null
     uint16_t *pout;      // bf16 parameter output
     int32_t pout_full;   // 1: full-indexed, 0: shard-indexed
     int32_t _pad;
@@ -125,63 +127,69 @@ __device__ __forceinline__ float mean_of(const StepArgs &a, float sum)
     return a.pow2 ? sum * a.inv_n : sum / a.n_f;
 }
 
-// Sum of the N rank gradients for 8 consecutive elements (vector path).
-template <int NR, bool BF16>
-__device__ __forceinline__ void reduce8(const StepArgs &a, int64_t si, int64_t fi, float acc[8])
+// Sum of the N rank gradients for G groups of 4 consecutive elements, group
+// h at shard index si[h] / full index fi[h] (vector path).  Each rank is
+// added in ascending order, from +0.
+template <int NR, bool BF16, int G>
+__device__ __forceinline__ void reduce_groups(const StepArgs &a, const int64_t *si,
+                                              const int64_t *fi, float (*acc)[4])
 {
     const int n = NR > 0 ? NR : a.n_ranks;
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-        acc[k] = 0.0f;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            acc[h][e] = 0.0f;
     // one group of 8 rank loads in flight per thread; other waves hide the
     // latency between groups (unrolling further only raises register use)
 #pragma unroll 1
     for (int q0 = 0; q0 < n; q0 += 8) {
         if (BF16) {
-            u32x4 w[8];
+            u32x2 w[8][G];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int q = q0 + k;
                 if (q < n) {
-                    const int64_t i = ((a.full_mask >> q) & 1) ? fi : si;
-                    w[k] = ld_nt(reinterpret_cast<const u32x4 *>(
-                        static_cast<const uint16_t *>(a.grads[q]) + i));
+                    const bool full = (a.full_mask >> q) & 1;
+                    const uint16_t *base = static_cast<const uint16_t *>(a.grads[q]);
+#pragma unroll
+                    for (int h = 0; h < G; ++h)
+                        w[k][h] = ld_nt(reinterpret_cast<const u32x2 *>(base + (full ? fi[h] : si[h])));
                 }
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 if (q0 + k < n) {
-                    acc[0] = acc[0] + bf16lo(w[k].x);
-                    acc[1] = acc[1] + bf16hi(w[k].x);
-                    acc[2] = acc[2] + bf16lo(w[k].y);
-                    acc[3] = acc[3] + bf16hi(w[k].y);
-                    acc[4] = acc[4] + bf16lo(w[k].z);
-                    acc[5] = acc[5] + bf16hi(w[k].z);
-                    acc[6] = acc[6] + bf16lo(w[k].w);
-                    acc[7] = acc[7] + bf16hi(w[k].w);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        acc[h][0] = acc[h][0] + bf16lo(w[k][h].x);
+                        acc[h][1] = acc[h][1] + bf16hi(w[k][h].x);
+                        acc[h][2] = acc[h][2] + bf16lo(w[k][h].y);
+                        acc[h][3] = acc[h][3] + bf16hi(w[k][h].y);
+                    }
                 }
             }
         } else {
-            f32x4 w[8][2];
+            f32x4 w[8][G];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int q = q0 + k;
                 if (q < n) {
-                    const int64_t i = ((a.full_mask >> q) & 1) ? fi : si;
-                    const f32x4 *p = reinterpret_cast<const f32x4 *>(
-                        static_cast<const float *>(a.grads[q]) + i);
-                    w[k][0] = ld_nt(p);
-                    w[k][1] = ld_nt(p + 1);
+                    const bool full = (a.full_mask >> q) & 1;
+                    const float *base = static_cast<const float *>(a.grads[q]);
+#pragma unroll
+                    for (int h = 0; h < G; ++h)
+                        w[k][h] = ld_nt(reinterpret_cast<const f32x4 *>(base + (full ? fi[h] : si[h])));
                 }
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 if (q0 + k < n) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        acc[e] = acc[e] + w[k][0][e];
-                        acc[4 + e] = acc[4 + e] + w[k][1][e];
-                    }
+                    for (int h = 0; h < G; ++h)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[h][e] = acc[h][e] + w[k][h][e];
                 }
             }
         }
@@ -203,6 +211,15 @@ __device__ __forceinline__ float reduce1(const StepArgs &a, int64_t si, int64_t 
     return acc;
 }
 
+// Wave-wide fp64 sum in a fixed butterfly order; every lane gets the total.
+__device__ __forceinline__ double wave_sum(double x)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        x = x + __shfl_xor(x, off, 64);
+    return x;
+}
+
 // Block-wide fp64 sum in a fixed order (wave shuffles, then waves 0..3).
 __device__ double block_sum(double x)
 {
@@ -222,115 +239,150 @@ __device__ double block_sum(double x)
 }
 
 // -------------------------------------------------------- step kernel --
+//
+// Element ownership in a 2048-element tile: wave w covers [512w, 512w + 512)
+// and lane l owns the two 4-element groups at 512w + 4l and 512w + 256 + 4l.
+// Every load or store instruction of a wave therefore covers one contiguous
+// run -- 512 bytes of a bf16 stream, 1 KiB of an fp32 stream -- so caches
+// and HBM see whole lines written by a single instruction.  (With 8
+// contiguous elements per lane, each 16-byte fp32 store instruction fills
+// only every other 16 bytes of its span and lines are written back in
+// halves.)
+
+// The fused / reduce / apply work for G full groups of 4 elements.
+template <int MODE, int NR, bool BF16, int G>
+__device__ __forceinline__ void step_groups(const StepArgs &a, const Seg &sg, const int64_t *j,
+                                            float coef, double &sq)
+{
+    int64_t si[G], fi[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        si[h] = sg.shard_off + j[h];
+        fi[h] = sg.full_off + j[h];
+    }
+    float p[G][4], m[G][4], v[G][4], g[G][4];
+    if (MODE != kReduce) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const f32x4 pv = ld_nt(reinterpret_cast<const f32x4 *>(a.master + si[h]));
+            const f32x4 mv = ld_nt(reinterpret_cast<const f32x4 *>(a.m + si[h]));
+            const f32x4 vv = ld_nt(reinterpret_cast<const f32x4 *>(a.v + si[h]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[h][e] = pv[e];
+                m[h][e] = mv[e];
+                v[h][e] = vv[e];
+            }
+        }
+    }
+    if (MODE == kApply) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const f32x4 gv = ld_nt(reinterpret_cast<const f32x4 *>(a.gin + si[h]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                g[h][e] = gv[e] * coef;
+        }
+    } else {
+        float acc[G][4];
+        reduce_groups<NR, BF16, G>(a, si, fi, acc);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                g[h][e] = mean_of(a, acc[h][e]);
+    }
+    if (MODE == kReduce) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sq = sq + (double)g[h][e] * (double)g[h][e];
+            st_nt(reinterpret_cast<f32x4 *>(a.gout + si[h]),
+                  f32x4{g[h][0], g[h][1], g[h][2], g[h][3]});
+        }
+        return;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            adam1(a.sc, g[h][e], p[h][e], m[h][e], v[h][e]);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        st_nt(reinterpret_cast<f32x4 *>(a.master + si[h]), f32x4{p[h][0], p[h][1], p[h][2], p[h][3]});
+        st_nt(reinterpret_cast<f32x4 *>(a.m + si[h]), f32x4{m[h][0], m[h][1], m[h][2], m[h][3]});
+        st_nt(reinterpret_cast<f32x4 *>(a.v + si[h]), f32x4{v[h][0], v[h][1], v[h][2], v[h][3]});
+        u32x2 w;
+        w.x = to_bf16(p[h][0]) | (to_bf16(p[h][1]) << 16);
+        w.y = to_bf16(p[h][2]) | (to_bf16(p[h][3]) << 16);
+        st_nt(reinterpret_cast<u32x2 *>(a.pout + (a.pout_full ? fi[h] : si[h])), w);
+    }
+}
+
+// The same work one element at a time: ragged tails and unaligned slices.
+template <int MODE, int NR, bool BF16>
+__device__ __forceinline__ void step_scalar(const StepArgs &a, const Seg &sg, int64_t j,
+                                            int64_t cnt, float coef, double &sq)
+{
+    const int64_t si = sg.shard_off + j;
+    const int64_t fi = sg.full_off + j;
+    const int64_t oi = a.pout_full ? fi : si;
+    for (int64_t e = 0; e < cnt; ++e) {
+        float g;
+        if (MODE == kApply)
+            g = a.gin[si + e] * coef;
+        else
+            g = mean_of(a, reduce1<NR, BF16>(a, si + e, fi + e));
+        if (MODE == kReduce) {
+            a.gout[si + e] = g;
+            sq = sq + (double)g * (double)g;
+        } else {
+            float p = a.master[si + e], m = a.m[si + e], v = a.v[si + e];
+            adam1(a.sc, g, p, m, v);
+            a.master[si + e] = p;
+            a.m[si + e] = m;
+            a.v[si + e] = v;
+            a.pout[oi + e] = (uint16_t)to_bf16(p);
+        }
+    }
+}
 
 template <int MODE, int NR, bool BF16>
 __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a)
 {
-    double sq = 0.0;
     const float coef = (MODE == kApply && a.clip) ? *a.clip : 1.0f;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
     int s = 0;
     for (int64_t t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
         while (s + 1 < a.n_segs && t >= a.seg[s + 1].tile0)
             ++s;
         const Seg &sg = a.seg[s];
-        const int64_t j = (t - sg.tile0) * kTile + (int64_t)threadIdx.x * kVec;
-        if (j >= sg.len)
-            continue;
-        const int64_t si = sg.shard_off + j;
-        const int64_t fi = sg.full_off + j;
-        const int64_t oi = a.pout_full ? fi : si;
-
-        if (sg.vec && a.vec_ptrs && j + kVec <= sg.len) {
-            // ---------------- vector path: 8 elements, 128-bit accesses
-            float g[8];
-            f32x4 p0, p1, m0, m1, v0, v1;
-            if (MODE != kReduce) {
-                const f32x4 *pp = reinterpret_cast<const f32x4 *>(a.master + si);
-                const f32x4 *mp = reinterpret_cast<const f32x4 *>(a.m + si);
-                const f32x4 *vp = reinterpret_cast<const f32x4 *>(a.v + si);
-                p0 = ld_nt(pp); p1 = ld_nt(pp + 1);
-                m0 = ld_nt(mp); m1 = ld_nt(mp + 1);
-                v0 = ld_nt(vp); v1 = ld_nt(vp + 1);
-            }
-            if (MODE == kApply) {
-                const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gin + si);
-                const f32x4 g0 = ld_nt(gp), g1 = ld_nt(gp + 1);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    g[e] = g0[e] * coef;
-                    g[4 + e] = g1[e] * coef;
-                }
-            } else {
-                float acc[8];
-                reduce8<NR, BF16>(a, si, fi, acc);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    g[e] = mean_of(a, acc[e]);
-            }
-            if (MODE == kReduce) {
-                f32x4 g0, g1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    g0[e] = g[e];
-                    g1[e] = g[4 + e];
-                    sq = sq + (double)g[e] * (double)g[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sq = sq + (double)g[4 + e] * (double)g[4 + e];
-                f32x4 *gp = reinterpret_cast<f32x4 *>(a.gout + si);
-                st_nt(gp, g0);
-                st_nt(gp + 1, g1);
-            } else {
-                float p[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-                float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-                float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    adam1(a.sc, g[e], p[e], m[e], v[e]);
-                f32x4 *pp = reinterpret_cast<f32x4 *>(a.master + si);
-                f32x4 *mp = reinterpret_cast<f32x4 *>(a.m + si);
-                f32x4 *vp = reinterpret_cast<f32x4 *>(a.v + si);
-                st_nt(pp, f32x4{p[0], p[1], p[2], p[3]});
-                st_nt(pp + 1, f32x4{p[4], p[5], p[6], p[7]});
-                st_nt(mp, f32x4{m[0], m[1], m[2], m[3]});
-                st_nt(mp + 1, f32x4{m[4], m[5], m[6], m[7]});
-                st_nt(vp, f32x4{v[0], v[1], v[2], v[3]});
-                st_nt(vp + 1, f32x4{v[4], v[5], v[6], v[7]});
-                u32x4 w;
-                w.x = to_bf16(p[0]) | (to_bf16(p[1]) << 16);
-                w.y = to_bf16(p[2]) | (to_bf16(p[3]) << 16);
-                w.z = to_bf16(p[4]) | (to_bf16(p[5]) << 16);
-                w.w = to_bf16(p[6]) | (to_bf16(p[7]) << 16);
-                st_nt(reinterpret_cast<u32x4 *>(a.pout + oi), w);
-            }
+        const int64_t j0 = (t - sg.tile0) * kTile + wave * kWaveElems + lane * 4;
+        const int64_t j[2] = {j0, j0 + kWaveElems / 2};
+        const bool vec = sg.vec && a.vec_ptrs;
+        double sq = 0.0;  // kReduce: this thread's sum of squares in this tile
+        if (vec && j[1] + 4 <= sg.len) {
+            step_groups<MODE, NR, BF16, 2>(a, sg, j, coef, sq);
         } else {
-            // ---------------- scalar path: ragged tail or unaligned slice
-            const int64_t cnt = (sg.len - j) < kVec ? (sg.len - j) : kVec;
-            for (int64_t e = 0; e < cnt; ++e) {
-                float g;
-                if (MODE == kApply)
-                    g = a.gin[si + e] * coef;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (j[h] >= sg.len)
+                    continue;
+                if (vec && j[h] + 4 <= sg.len)
+                    step_groups<MODE, NR, BF16, 1>(a, sg, &j[h], coef, sq);
                 else
-                    g = mean_of(a, reduce1<NR, BF16>(a, si + e, fi + e));
-                if (MODE == kReduce) {
-                    a.gout[si + e] = g;
-                    sq = sq + (double)g * (double)g;
-                } else {
-                    float p = a.master[si + e], m = a.m[si + e], v = a.v[si + e];
-                    adam1(a.sc, g, p, m, v);
-                    a.master[si + e] = p;
-                    a.m[si + e] = m;
-                    a.v[si + e] = v;
-                    a.pout[oi + e] = (uint16_t)to_bf16(p);
-                }
+                    step_scalar<MODE, NR, BF16>(a, sg, j[h],
+                                                sg.len - j[h] < 4 ? sg.len - j[h] : 4, coef, sq);
             }
         }
-    }
-    if (MODE == kReduce && a.partials) {
-        const double total = block_sum(sq);
-        if (threadIdx.x == 0)
-            a.partials[blockIdx.x] = total;
+        if (MODE == kReduce && a.partials) {
+            // every lane takes part; lanes past the slice end add 0
+            const double w = wave_sum(sq);
+            if (lane == 0)
+                a.partials[t * kWaves + wave] = w;
+        }
     }
 }
 
@@ -385,28 +437,33 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a)
 
 // ------------------------------------------------- accumulate kernel --
 
+// Same ownership as the step kernel: lane l of wave w owns the 4-element
+// groups at 512w + 4l and 512w + 256 + 4l of each 2048-element tile.
 __global__ __launch_bounds__(kThreads) void accumulate_kernel(float *acc, const uint16_t *micro,
                                                               int64_t n, int32_t vec)
 {
+    const int64_t lane_off = (threadIdx.x >> 6) * kWaveElems + (threadIdx.x & 63) * 4;
     const int64_t stride = (int64_t)gridDim.x * kTile;
     for (int64_t b = (int64_t)blockIdx.x * kTile; b < n; b += stride) {
-        const int64_t i = b + (int64_t)threadIdx.x * kVec;
-        if (i >= n)
-            continue;
-        if (vec && i + kVec <= n) {
-            f32x4 *ap = reinterpret_cast<f32x4 *>(acc + i);
-            f32x4 a0 = ld_nt(ap), a1 = ld_nt(ap + 1);
-            const u32x4 w = ld_nt(reinterpret_cast<const u32x4 *>(micro + i));
-            a0.x = a0.x + bf16lo(w.x); a0.y = a0.y + bf16hi(w.x);
-            a0.z = a0.z + bf16lo(w.y); a0.w = a0.w + bf16hi(w.y);
-            a1.x = a1.x + bf16lo(w.z); a1.y = a1.y + bf16hi(w.z);
-            a1.z = a1.z + bf16lo(w.w); a1.w = a1.w + bf16hi(w.w);
-            st_nt(ap, a0);
-            st_nt(ap + 1, a1);
-        } else {
-            const int64_t cnt = (n - i) < kVec ? (n - i) : kVec;
-            for (int64_t e = 0; e < cnt; ++e)
-                acc[i + e] = acc[i + e] + bf16f(micro[i + e]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t i = b + lane_off + h * (kWaveElems / 2);
+            if (i >= n)
+                continue;
+            if (vec && i + 4 <= n) {
+                f32x4 *ap = reinterpret_cast<f32x4 *>(acc + i);
+                f32x4 x = ld_nt(ap);
+                const u32x2 w = ld_nt(reinterpret_cast<const u32x2 *>(micro + i));
+                x.x = x.x + bf16lo(w.x);
+                x.y = x.y + bf16hi(w.x);
+                x.z = x.z + bf16lo(w.y);
+                x.w = x.w + bf16hi(w.y);
+                st_nt(ap, x);
+            } else {
+                const int64_t cnt = (n - i) < 4 ? (n - i) : 4;
+                for (int64_t e = 0; e < cnt; ++e)
+                    acc[i + e] = acc[i + e] + bf16f(micro[i + e]);
+            }
         }
     }
 }
@@ -449,19 +506,39 @@ int device_cus()
     return cached[dev];
 }
 
-int blocks_per_cu()
+// Launch width of the persistent kernels: every CU gets as many blocks as
+// can be resident at once (from the occupancy of that kernel), so the whole
+// grid is in flight from the start and no late second batch of blocks runs
+// at low occupancy.  ZERO_SHARD_BLOCKS_PER_CU overrides it (1..64 blocks per
+// CU; 0 means one block per tile, no grid stride).  Read once per process.
+int blocks_per_cu_override()
 {
     static int v = [] {
         const char *e = std::getenv("ZERO_SHARD_BLOCKS_PER_CU");
-        const int x = e ? std::atoi(e) : 0;
-        return (x >= 1 && x <= 64) ? x : 8;
+        if (!e || !*e)
+            return -1;
+        const int x = std::atoi(e);
+        return (x >= 0 && x <= 64) ? x : -1;
     }();
     return v;
 }
 
-int64_t stream_grid(int64_t n_tiles)
+template <typename Kernel>
+int resident_blocks(Kernel kernel)
 {
-    const int64_t g = (int64_t)device_cus() * blocks_per_cu();
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, 0) != hipSuccess ||
+        nb < 1)
+        nb = 4;
+    return nb;
+}
+
+int64_t stream_grid(int64_t n_tiles, int resident)
+{
+    const int o = blocks_per_cu_override();
+    if (o == 0)
+        return n_tiles;
+    const int64_t g = (int64_t)device_cus() * (o > 0 ? o : resident);
     return n_tiles < g ? n_tiles : g;
 }
 
@@ -499,7 +576,7 @@ int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg 
         s.shard_off = L->shard_off[u] - L->shard_off[ub];
         s.full_off = L->flat_off[u] - L->flat_off[ub] + (int64_t)L->rank * len;
         s.tile0 = tiles;
-        s.vec = (s.shard_off % kVec == 0 && s.full_off % kVec == 0) ? 1 : 0;
+        s.vec = (s.shard_off % 4 == 0 && s.full_off % 4 == 0) ? 1 : 0;
         tiles += tiles_of(len);
     }
     *n_segs = k;
@@ -569,22 +646,30 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
     return s;
 }
 
+// grid > 0: that many blocks; grid == 0: the persistent width of the kernel.
+template <int MODE, int NR, bool BF16>
+void launch_one(const StepArgs &a, int64_t grid, hipStream_t st)
+{
+    static const int resident = resident_blocks(step_kernel<MODE, NR, BF16>);
+    const int64_t blocks = grid > 0 ? grid : stream_grid(a.n_tiles, resident);
+    hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0,
+                       st, a);
+}
+
 template <int MODE, bool BF16>
 void launch_step(const StepArgs &a, int64_t grid, hipStream_t st)
 {
-    const dim3 g((unsigned)grid), b(kThreads);
     if constexpr (MODE == kApply) {
-        hipLaunchKernelGGL((step_kernel<kApply, 1, true>), g, b, 0, st, a);
-        return;
+        launch_one<kApply, 1, true>(a, grid, st);
     } else {
-    switch (a.n_ranks) {
-    case 1: hipLaunchKernelGGL((step_kernel<MODE, 1, BF16>), g, b, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((step_kernel<MODE, 2, BF16>), g, b, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((step_kernel<MODE, 4, BF16>), g, b, 0, st, a); break;
-    case 8: hipLaunchKernelGGL((step_kernel<MODE, 8, BF16>), g, b, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((step_kernel<MODE, 64, BF16>), g, b, 0, st, a); break;
-    default: hipLaunchKernelGGL((step_kernel<MODE, 0, BF16>), g, b, 0, st, a); break;
-    }
+        switch (a.n_ranks) {
+        case 1: launch_one<MODE, 1, BF16>(a, grid, st); break;
+        case 2: launch_one<MODE, 2, BF16>(a, grid, st); break;
+        case 4: launch_one<MODE, 4, BF16>(a, grid, st); break;
+        case 8: launch_one<MODE, 8, BF16>(a, grid, st); break;
+        case 64: launch_one<MODE, 64, BF16>(a, grid, st); break;
+        default: launch_one<MODE, 0, BF16>(a, grid, st); break;
+        }
     }
 }
 
@@ -617,8 +702,7 @@ int64_t zero_reduce_partials_count(const zero_layout *L, int32_t ub, int32_t ue)
     for_each_chunk(ub, ue, [&](int32_t u0, int32_t u1) {
         Seg seg[kMaxSegs];
         int32_t ns = 0;
-        const int64_t tiles = fill_segs(L, ub, u0, u1, seg, &ns);
-        total += tiles < kReduceGrid ? tiles : kReduceGrid;
+        total += kWaves * fill_segs(L, ub, u0, u1, seg, &ns);
         return ZERO_OK;
     });
     return total;
@@ -656,10 +740,9 @@ zero_status zero_reduce_shard(const zero_layout *L, int32_t ub, int32_t ue,
         if (a.n_tiles == 0)
             return ZERO_OK;
         a.gout = out;
-        const int64_t grid = a.n_tiles < kReduceGrid ? a.n_tiles : kReduceGrid;
         a.partials = partials ? partials + poff : nullptr;
-        poff += grid;
-        return launch_mode<kReduce>(a, grads->dtype == ZERO_BF16, grid,
+        poff += kWaves * a.n_tiles;
+        return launch_mode<kReduce>(a, grads->dtype == ZERO_BF16, 0,
                                     static_cast<hipStream_t>(stream));
     });
 }
@@ -736,11 +819,10 @@ zero_status zero_adam_step(const zero_layout *L, int32_t ub, int32_t ue,
         a.pout = param_out;
         a.pout_full = param_index == ZERO_INDEX_FULL;
         a.sc = sc;
-        const int64_t grid = stream_grid(a.n_tiles);
         const hipStream_t s = static_cast<hipStream_t>(stream);
         if (grads)
-            return launch_mode<kFused>(a, grads->dtype == ZERO_BF16, grid, s);
-        return launch_mode<kApply>(a, true, grid, s);
+            return launch_mode<kFused>(a, grads->dtype == ZERO_BF16, 0, s);
+        return launch_mode<kApply>(a, true, 0, s);
     });
 }
 
@@ -798,7 +880,8 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
             a.vec_ptrs = al;
             if (tiles == 0)
                 return ZERO_OK;
-            int64_t gx = stream_grid(tiles) / a.n_src;
+            static const int resident = resident_blocks(gather_kernel);
+            int64_t gx = stream_grid(tiles, resident) / a.n_src;
             gx = gx < 1 ? 1 : gx;
             (void)hipGetLastError();
             hipLaunchKernelGGL(gather_kernel, dim3((unsigned)gx, (unsigned)a.n_src), dim3(kThreads),
@@ -823,7 +906,8 @@ zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro, int64_
     if (n == 0)
         return ZERO_OK;
     const int64_t tiles = tiles_of(n);
-    const int64_t grid = stream_grid(tiles);
+    static const int resident = resident_blocks(accumulate_kernel);
+    const int64_t grid = stream_grid(tiles, resident);
     const int32_t vec = aligned16(main_grad) && aligned16(micro);
     (void)hipGetLastError();
     hipLaunchKernelGGL(accumulate_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
