@@ -28,6 +28,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "fused_step_7b_n8_counters.md")
+KERNELS_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_shard_amd", "csrc", "kernels.hip")
 BYTES_FUSED = 42          # per shard element, bf16 grads, N = 8
 BYTES_GATHER_PER_PEER = 4  # read 2 + write 2 per element per peer slice
 
@@ -177,11 +179,30 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": fused_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": counter_traffic(),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated)",
+            "algorithmic_bytes": BYTES_FUSED * S,
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def counter_traffic():
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy calibration),
+    or None if that summary was taken on a different kernels.hip."""
+    import hashlib
+    try:
+        kv = dict(line.split(": ", 1) for line in open(COUNTERS).read().splitlines()
+                  if line.startswith(("kernels_hip_sha256: ", "fused_traffic_bytes_per_launch: ")))
+        sha = hashlib.sha256(open(KERNELS_SRC, "rb").read()).hexdigest()
+        if kv.get("kernels_hip_sha256") != sha:
+            return None
+        return float(kv["fused_traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, grads, master, S, r, budget_s):

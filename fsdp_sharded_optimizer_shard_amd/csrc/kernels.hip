@@ -5,17 +5,20 @@
 // (12 bytes), and writes master, m, v (12) and the bf16 parameter (2), for
 // about N + 20 flops -- far below the machine balance, so there is no
 // contraction and no MFMA.  The design rules that matter are the memory ones:
-//   * 256-thread blocks, each thread owns 8 consecutive elements of a
-//     2048-element tile, so every stream moves in 128-bit loads/stores
-//     (one per bf16 stream, two per fp32 stream) and a wave covers whole
-//     128-byte lines;
+//   * 256-thread blocks over 2048-element tiles; each lane owns two groups
+//     of 4 consecutive elements so that every load / store instruction of a
+//     wave covers one contiguous run (fp32 streams in 128-bit accesses, bf16
+//     streams in 64-bit ones) and whole lines are written by one
+//     instruction -- rocprof FETCH_SIZE / WRITE_SIZE equal the algorithmic
+//     bytes;
 //   * one pass: the reduce over ranks, the Adam update and the bf16 cast are
 //     fused so each byte crosses HBM once;
-//   * persistent grid-stride launch over a tile space that concatenates the
-//     slices of many units (FSDP layers, gradient buckets), so small units do
-//     not pay one launch and one ramp-down each;
+//   * one launch covers a tile space that concatenates the slices of many
+//     units (FSDP layers, gradient buckets), so small units do not pay one
+//     launch and one ramp-down each; by default one block per tile (see
+//     blocks_per_cu_override for the measurement behind that choice);
 //   * the N rank streams are loaded in groups of 8 before they are summed,
-//     keeping 8 x 16 bytes per thread in flight without holding all N.
+//     keeping 8 loads per thread in flight without holding all N.
 //
 // Arithmetic (identical on every launch shape): fp32, one rounding per
 // operation, no contraction into FMA (pragma below plus -ffp-contract=off),
@@ -87,6 +90,19 @@ struct StepArgs {
 };
 
 // ------------------------------------------------------------ helpers --
+
+// Tiles a block walks: a grid-stride over the launch's tile space.  The
+// default launch has one block per tile (a single iteration); the
+// persistent width (ZERO_SHARD_BLOCKS_PER_CU) walks several.  Every tile is
+// visited exactly once, in increasing order per block.
+struct TileWalk {
+    int64_t t, end, stride;
+};
+
+__device__ __forceinline__ TileWalk tile_walk(int64_t n_tiles)
+{
+    return {(int64_t)blockIdx.x, n_tiles, (int64_t)gridDim.x};
+}
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -355,7 +371,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a)
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     int s = 0;
-    for (int64_t t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
+    const TileWalk tw = tile_walk(a.n_tiles);
+    for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         while (s + 1 < a.n_segs && t >= a.seg[s + 1].tile0)
             ++s;
         const Seg &sg = a.seg[s];
@@ -415,7 +432,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a)
     const uint16_t *src = a.src[y];
     const int64_t q = a.rank_of[y];
     int s = 0;
-    for (int64_t t = blockIdx.x; t < a.n_tiles; t += gridDim.x) {
+    const TileWalk tw = tile_walk(a.n_tiles);
+    for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         while (s + 1 < a.n_segs && t >= a.seg[s + 1].tile0)
             ++s;
         const GSeg &sg = a.seg[s];
@@ -443,8 +461,9 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(float *acc, const 
                                                               int64_t n, int32_t vec)
 {
     const int64_t lane_off = (threadIdx.x >> 6) * kWaveElems + (threadIdx.x & 63) * 4;
-    const int64_t stride = (int64_t)gridDim.x * kTile;
-    for (int64_t b = (int64_t)blockIdx.x * kTile; b < n; b += stride) {
+    const TileWalk tw = tile_walk((n + kTile - 1) / kTile);
+    for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
+        const int64_t b = t * kTile;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int64_t i = b + lane_off + h * (kWaveElems / 2);
@@ -506,19 +525,21 @@ int device_cus()
     return cached[dev];
 }
 
-// Launch width of the persistent kernels: every CU gets as many blocks as
-// can be resident at once (from the occupancy of that kernel), so the whole
-// grid is in flight from the start and no late second batch of blocks runs
-// at low occupancy.  ZERO_SHARD_BLOCKS_PER_CU overrides it (1..64 blocks per
-// CU; 0 means one block per tile, no grid stride).  Read once per process.
+// Launch width.  Default: one block per 2048-element tile.  Measured on
+// MI355X (7B / N = 8 step, paired runs over six buffer placements) this beat
+// a persistent grid sized to the resident occupancy by 6 % on the fused
+// kernel and 12 % on the gather: the dispatcher hands out blocks in tile
+// order, which keeps the active window of every stream compact, and it
+// balances the tail by itself.  ZERO_SHARD_BLOCKS_PER_CU=K (1..64) selects a
+// persistent grid of K blocks per CU instead (0 = the default).  Read once.
 int blocks_per_cu_override()
 {
     static int v = [] {
         const char *e = std::getenv("ZERO_SHARD_BLOCKS_PER_CU");
         if (!e || !*e)
-            return -1;
+            return 0;
         const int x = std::atoi(e);
-        return (x >= 0 && x <= 64) ? x : -1;
+        return (x >= 0 && x <= 64) ? x : 0;
     }();
     return v;
 }
@@ -533,12 +554,14 @@ int resident_blocks(Kernel kernel)
     return nb;
 }
 
+// `resident` (blocks of the kernel that fit on one CU) caps the persistent
+// width so a persistent grid is fully resident from the start.
 int64_t stream_grid(int64_t n_tiles, int resident)
 {
     const int o = blocks_per_cu_override();
     if (o == 0)
         return n_tiles;
-    const int64_t g = (int64_t)device_cus() * (o > 0 ? o : resident);
+    const int64_t g = (int64_t)device_cus() * (o < resident ? o : resident);
     return n_tiles < g ? n_tiles : g;
 }
 
@@ -646,7 +669,7 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
     return s;
 }
 
-// grid > 0: that many blocks; grid == 0: the persistent width of the kernel.
+// grid > 0: that many blocks; grid == 0: the default launch width.
 template <int MODE, int NR, bool BF16>
 void launch_one(const StepArgs &a, int64_t grid, hipStream_t st)
 {
@@ -878,7 +901,7 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
             a.n_tiles = tiles;
             a.dst = param_full;
             a.vec_ptrs = al;
-            if (tiles == 0)
+                if (tiles == 0)
                 return ZERO_OK;
             static const int resident = resident_blocks(gather_kernel);
             int64_t gx = stream_grid(tiles, resident) / a.n_src;
