@@ -1,10 +1,10 @@
 """Benchmark: one data-parallel rank's sharded optimizer step on one MI355X.
 
-Workload (default): the Mistral-7B-sized ZeRO-3 rank shard -- Psi =
-7.24e9, N = 8 simulated ranks, this GPU is rank 7 and owns 905,000,000
-elements.  Inputs are synthetic and resident in HBM before timing: 8 bf16
-rank-gradient shards ~N(0, 1e-3), fp32 master ~N(0, 0.02), m = v = 0,
-7 peer bf16 parameter shards.  One step is the whole hot path:
+Default workload (the headline): the Mistral-7B-sized ZeRO-3 rank shard --
+Psi = 7.24e9, N = 8 simulated ranks, this GPU is rank 7 and owns
+905,000,000 elements.  Inputs are synthetic and resident in HBM before
+timing: 8 bf16 rank-gradient shards ~N(0, 1e-3), fp32 master ~N(0, 0.02),
+m = v = 0, 7 peer bf16 parameter shards.  One step is the whole hot path:
   1. zero_adam_step, fused: reduce the 8 rank gradients in fp32, divide by
      8, Adam (lr 1e-3, betas 0.9 / 0.999, eps 1e-8), round to bf16 and store
      this rank's slice into the 7.24e9-element flat parameter buffer;
@@ -17,6 +17,12 @@ roofline: the fused kernel's algorithmic bytes (42 B per shard element:
 duration from HIP events on the launch stream, against 8 TB/s.
 cpu_baseline: the CPU oracle (single thread) timed on a bounded sample of
 the same shard (the first elements, streamed in chunks from the GPU).
+
+--config 0 | 1 | 3 | 4 measures the other workloads instead (same JSON
+shape, their own metric): the tiny ZeRO-2 step, the GPT-2-small buffer with
+the global-norm clip, the Megatron distributed optimizer (fp32 main-gradient
+accumulation of 4 micro-batches + fp32 reduce + Adam + gather), and the
+Llama-70B FSDP full shard at N = 64 swept unit by unit.
 """
 import argparse
 import json
@@ -30,8 +36,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "fused_step_7b_n8_counters.md")
 KERNELS_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_shard_amd", "csrc", "kernels.hip")
-BYTES_FUSED = 42          # per shard element, bf16 grads, N = 8
-BYTES_GATHER_PER_PEER = 4  # read 2 + write 2 per element per peer slice
+HEADLINE_METRIC = "shard optimizer-step params/sec at 7B N=8; achieved HBM GB/s vs peak"
 
 
 def parse():
@@ -39,58 +44,97 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
-                    help="oracle time budget for the CPU baseline; 0 skips it")
+                    help="oracle time budget for the CPU baseline (headline only); 0 skips it")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
-                    help="instead of the step, run a plain bf16 copy of BYTES through "
+                    help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build simulates the N data-parallel ranks "
-              "inside one GPU's memory and has no multi-GPU path; run with --gpus 1.",
-              file=sys.stderr)
-        sys.exit(2)
+class Phases:
+    """HIP-event timing of named phases on one stream; several launches of
+    one phase in a step are summed, and each launch is also kept."""
 
-    import numpy as np
-    import torch
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.marks = []        # (name, start_event, end_event) in launch order
 
-    from fsdp_sharded_optimizer_shard_amd import zs
-    from synthetic import WORKLOADS, grad_bits, master_init
+    def run(self, name, fn):
+        E = self.torch.cuda.Event
+        a, b = E(enable_timing=True), E(enable_timing=True)
+        a.record(self.stream)
+        fn()
+        b.record(self.stream)
+        self.marks.append((name, a, b))
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
+    def summary(self, steps):
+        per = {}
+        for name, a, b in self.marks:
+            per.setdefault(name, []).append(a.elapsed_time(b))
+        return {k: {"ms_per_step": sum(v) / steps, "launches_per_step": len(v) // steps,
+                    "ms_per_launch_mean": sum(v) / len(v), "ms_per_launch_min": min(v)}
+                for k, v in per.items()}
+
+
+def timed(args, torch, step):
+    """warmup, then exactly `steps` steps between synchronisations; returns
+    (wall ms per step, phase summary)."""
     stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    ph = Phases(torch, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(ph)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return 1e3 * wall / args.steps, ph.summary(args.steps)
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy // 2
-        L = zs.shard_init("zero2", 1, 0, [n])
-        src = torch.ones(n, dtype=torch.int16, device=dev)
-        dst = torch.empty(n, dtype=torch.int16, device=dev)
-        for _ in range(3):
-            zs.gather_params(L, 0, 1, [src], dst)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            zs.gather_params(L, 0, 1, [src], dst)
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
-        print(json.dumps({"calibrate_copy_bytes": 2 * n, "ms": ms, "GBps": 4 * n / ms / 1e6}),
-              flush=True)
-        return
 
+def phase(ph, name, fn):
+    if ph is None:
+        fn()
+    else:
+        ph.run(name, fn)
+
+
+def roofline(name, bytes_per_launch, ms_per_launch, traffic=None):
+    gbps = bytes_per_launch / (ms_per_launch * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": name, "achieved": gbps, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                            "copy-calibrated)",
+            "algorithmic_bytes": bytes_per_launch}
+
+
+def base_line(args, metric, value, unit, ms, workload, **config):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded N(0,1e-3) bf16 rank grads, N(0,0.02) fp32 master)",
+            "config": {"workload": workload, **config}}
+
+
+def add_rates(kernels, name, bytes_per_launch):
+    k = kernels[name]
+    k["bytes_per_launch"] = bytes_per_launch
+    k["gbps"] = bytes_per_launch / (k["ms_per_launch_mean"] * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------ workloads --
+
+def run_headline(args, torch, zs, np):
+    from synthetic import WORKLOADS, grad_bits, master_init
+    dev = torch.device("cuda:0")
     w = WORKLOADS[2]
     N, r = w.n_ranks, w.n_ranks - 1
     L = zs.shard_init("zero3", N, r, list(w.units))
     S = L.shard_len
-    q0 = L.query(0)
     print(f"# setup: {w.name}, rank {r}, shard {S} elements", file=sys.stderr, flush=True)
-
     grads = [grad_bits(w, 0, q, S, device=dev) for q in range(N)]
     master = master_init(w, S, device=dev, rank=r)
     m = torch.zeros(S, device=dev)
@@ -100,93 +144,259 @@ def main():
     shard_ptrs = peers + [None]                      # own slice is written by the step
     G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
     torch.cuda.synchronize()
+    t = [0]
 
-    t_state = [0]
+    def step(ph):
+        t[0] += 1
+        cfg = zs.adam_cfg(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=t[0])
+        phase(ph, "fused_reduce_adam_cast",
+              lambda: zs.adam_step(L, 0, 1, cfg, master, m, v, full, zs.INDEX_FULL, grads=G))
+        phase(ph, "gather_7_peers", lambda: zs.gather_params(L, 0, 1, shard_ptrs, full))
 
-    def step(ev=None):
-        t_state[0] += 1
-        cfg = zs.adam_cfg(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=t_state[0])
-        if ev:
-            ev[0].record(stream)
-        zs.adam_step(L, 0, 1, cfg, master, m, v, full, zs.INDEX_FULL, grads=G, stream=stream)
-        if ev:
-            ev[1].record(stream)
-        zs.gather_params(L, 0, 1, shard_ptrs, full, stream=stream)
-        if ev:
-            ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    fused_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    gather_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    ms_per_step = 1e3 * wall / args.steps
-    fused_avg = float(np.mean(fused_ms))
-    gather_avg = float(np.mean(gather_ms))
-    fused_gbps = BYTES_FUSED * S / (fused_avg * 1e-3) / 1e9
-    gather_gbps = BYTES_GATHER_PER_PEER * (N - 1) * S / (gather_avg * 1e-3) / 1e9
-    step_bytes = (BYTES_FUSED + BYTES_GATHER_PER_PEER * (N - 1)) * S
-
+    ms, kern = timed(args, torch, step)
+    fused_b, gather_b = 42 * S, 4 * (N - 1) * S
+    add_rates(kern, "fused_reduce_adam_cast", fused_b)
+    add_rates(kern, "gather_7_peers", gather_b)
     cpu = None
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_baseline(w, grads, master, S, r, args.cpu_baseline_seconds)
+    out = base_line(args, HEADLINE_METRIC, S / (ms * 1e-3), "params/s", ms,
+                    "Mistral-7B ZeRO-3 rank shard step: reduce 8 bf16 rank grads + Adam + "
+                    "bf16 cast into the flat buffer + gather of 7 peer shards",
+                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S,
+                    rank_flat_offset=L.query(0)["rank_flat_off"],
+                    algorithmic_bytes_per_step=fused_b + gather_b)
+    out["step_gbps"] = (fused_b + gather_b) / (ms * 1e-3) / 1e9
+    out["state_gbps_16psi_over_n"] = 16 * S / (ms * 1e-3) / 1e9
+    out["kernels"] = kern
+    out["roofline"] = roofline("fused_reduce_adam_cast (step_kernel<fused, N=8, bf16>)", fused_b,
+                               kern["fused_reduce_adam_cast"]["ms_per_launch_mean"],
+                               counter_traffic())
+    out["cpu_baseline"] = cpu
+    return out
 
-    out = {
-        "metric": "shard optimizer-step params/sec at 7B N=8; achieved HBM GB/s vs peak",
-        "value": S / (ms_per_step * 1e-3),
-        "unit": "params/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded N(0,1e-3) bf16 rank grads, N(0,0.02) fp32 master)",
-        "config": {
-            "workload": "Mistral-7B ZeRO-3 rank shard step: reduce 8 bf16 rank grads + Adam + "
-                        "bf16 cast into the flat buffer + gather of 7 peer shards",
-            "psi": w.psi, "n_ranks": N, "rank": r, "shard_elems": S,
-            "rank_flat_offset": q0["rank_flat_off"],
-            "algorithmic_bytes_per_step": step_bytes,
-        },
-        "step_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "state_gbps_16psi_over_n": 16 * S / (ms_per_step * 1e-3) / 1e9,
-        "kernels": {
-            "fused_reduce_adam_cast": {"ms_mean": fused_avg, "ms_min": float(np.min(fused_ms)),
-                                       "ms_max": float(np.max(fused_ms)), "gbps": fused_gbps,
-                                       "bytes_per_elem": BYTES_FUSED},
-            "gather_7_peers": {"ms_mean": gather_avg, "ms_min": float(np.min(gather_ms)),
-                               "gbps": gather_gbps,
-                               "bytes_per_elem": BYTES_GATHER_PER_PEER * (N - 1)},
-            "step_events_ms_mean": float(np.mean(step_ms)),
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "fused_reduce_adam_cast (step_kernel<fused, N=8, bf16>)",
-            "achieved": fused_gbps,
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": fused_gbps / HBM_PEAK_GBPS,
-            "traffic": counter_traffic(),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                            "copy-calibrated)",
-            "algorithmic_bytes": BYTES_FUSED * S,
-        },
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+
+def run_tiny(args, torch, zs, np):
+    """Config 0: Psi = 2^20, N = 4, all four ranks' fused steps into one
+    shared flat buffer (cache-resident, launch-bound: not a roofline point)."""
+    from synthetic import WORKLOADS, grad_bits, master_init
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[0]
+    N = w.n_ranks
+    lays = [zs.shard_init("zero2", N, r, list(w.units)) for r in range(N)]
+    S, P = lays[0].shard_len, lays[0].flat_len
+    grads = [grad_bits(w, 0, q, P, device=dev) for q in range(N)]
+    G = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
+    full = torch.empty(P, dtype=torch.int16, device=dev)
+    st = [[master_init(w, S, device=dev, rank=r), torch.zeros(S, device=dev),
+           torch.zeros(S, device=dev)] for r in range(N)]
+    t = [0]
+
+    def step(ph):
+        t[0] += 1
+        cfg = zs.adam_cfg(step=t[0])
+        for r in range(N):
+            phase(ph, "fused_reduce_adam_cast",
+                  lambda r=r: zs.adam_step(lays[r], 0, 1, cfg, *st[r], full, zs.INDEX_FULL,
+                                           grads=G))
+
+    ms, kern = timed(args, torch, step)
+    b = (2 * N + 26) * S
+    add_rates(kern, "fused_reduce_adam_cast", b)
+    out = base_line(args, "tiny ZeRO-2 step params/sec (Psi=2^20, N=4, all ranks)",
+                    P / (ms * 1e-3), "params/s", ms,
+                    "tiny ZeRO-2 step: 4 ranks x fused reduce + Adam + bf16 into one buffer",
+                    psi=w.psi, n_ranks=N, shard_elems=S)
+    out["kernels"] = kern
+    out["roofline"] = roofline("step_kernel<fused, N=4, bf16> (cache-resident; not a roofline "
+                               "point)", b, kern["fused_reduce_adam_cast"]["ms_per_launch_mean"])
+    out["cpu_baseline"] = None
+    return out
+
+
+def run_gpt2_clip(args, torch, zs, np):
+    """Config 1: Psi = 124,439,808, N = 8, five 25M buckets, all 8 ranks:
+    reduce (with sum-of-squares partials) -> clip coefficient -> AdamW from
+    the fp32 gradient."""
+    from synthetic import WORKLOADS, grad_bits, master_init
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[1]
+    N, U = w.n_ranks, len(w.units)
+    lays = [zs.shard_init("zero2", N, r, list(w.units)) for r in range(N)]
+    S, P = lays[0].shard_len, lays[0].flat_len
+    grads = [grad_bits(w, 0, q, P, device=dev) for q in range(N)]
+    G = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
+    full = torch.empty(P, dtype=torch.int16, device=dev)
+    st = [[master_init(w, lays[r].shard_len, device=dev, rank=r),
+           torch.zeros(lays[r].shard_len, device=dev), torch.zeros(lays[r].shard_len, device=dev)]
+          for r in range(N)]
+    gsh = [torch.empty(L.shard_len, device=dev) for L in lays]
+    counts = [zs.reduce_partials_count(L, 0, U) for L in lays]
+    offs = [sum(counts[:r]) for r in range(N)]
+    partials = torch.empty(sum(counts), dtype=torch.float64, device=dev)
+    coef = torch.empty(1, device=dev)
+    t = [0]
+
+    def step(ph):
+        t[0] += 1
+        cfg = zs.adam_cfg(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                          weight_decay=w.weight_decay, decoupled=w.decoupled, step=t[0])
+        for r in range(N):
+            phase(ph, "reduce_with_sumsq",
+                  lambda r=r: zs.reduce_shard(lays[r], 0, U, G, gsh[r], partials[offs[r]:],
+                                              counts[r]))
+        phase(ph, "clip_coef", lambda: zs.clip_coef(partials, partials.numel(),
+                                                    w.max_grad_norm, coef))
+        for r in range(N):
+            phase(ph, "adamw_apply_cast",
+                  lambda r=r: zs.adam_step(lays[r], 0, U, cfg, *st[r], full, zs.INDEX_FULL,
+                                           grad_fp32=gsh[r], clip_coef=coef))
+
+    ms, kern = timed(args, torch, step)
+    rb, ab = (2 * N + 4) * S, 30 * S
+    add_rates(kern, "reduce_with_sumsq", rb)
+    add_rates(kern, "adamw_apply_cast", ab)
+    kern["clip_coef"]["bytes_per_launch"] = 8 * partials.numel() + 4
+    dom = max(("reduce_with_sumsq", rb), ("adamw_apply_cast", ab),
+              key=lambda x: kern[x[0]]["ms_per_step"])
+    out = base_line(args, "GPT-2-small clipped AdamW step params/sec (N=8, all ranks)",
+                    P / (ms * 1e-3), "params/s", ms,
+                    "GPT-2-small flat buffer, 5 x 25M buckets, N=8: reduce + global-norm clip "
+                    "+ AdamW + bf16 for all 8 ranks",
+                    psi=w.psi, n_ranks=N, shard_elems=S, buckets=list(w.units))
+    out["step_gbps"] = N * (rb + ab) / (ms * 1e-3) / 1e9
+    out["kernels"] = kern
+    out["roofline"] = roofline(dom[0], dom[1], kern[dom[0]]["ms_per_launch_mean"])
+    out["cpu_baseline"] = None
+    return out
+
+
+def run_megatron(args, torch, zs, np):
+    """Config 3: Psi = 7.24e9, N = 8, rank 7: four bf16 micro-batch
+    gradients accumulated into the fp32 main gradient over the whole buffer,
+    then the fused fp32 reduce (7 peer fp32 shards + own main gradient) +
+    Adam + bf16 into the replicated buffer, then the gather of 7 peers."""
+    from synthetic import KIND_MICRO, WORKLOADS, grad_bits, master_init
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[3]
+    N, r = w.n_ranks, w.n_ranks - 1
+    L = zs.shard_init("megatron_do", N, r, list(w.units))
+    S, P = L.shard_len, L.flat_len
+    main = torch.zeros(P, device=dev)
+    micro = grad_bits(w, 0, r, P, device=dev, kind=KIND_MICRO)
+    peers32 = [torch.empty(S, device=dev).normal_(0, 1e-3) for _ in range(N - 1)]
+    G = zs.Grads(peers32 + [main], zs.FP32, [zs.INDEX_SHARD] * (N - 1) + [zs.INDEX_FULL])
+    master = master_init(w, S, device=dev, rank=r)
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    replica = torch.empty(P, dtype=torch.int16, device=dev)
+    peers16 = [torch.full((S,), q + 1, dtype=torch.int16, device=dev) for q in range(N - 1)]
+    torch.cuda.synchronize()
+    t = [0]
+
+    def step(ph):
+        t[0] += 1
+        cfg = zs.adam_cfg(step=t[0])
+        main.zero_()
+        for _ in range(w.micro_batches):
+            phase(ph, "accumulate_fp32", lambda: zs.grad_accumulate(main, micro, P))
+        phase(ph, "fused_fp32_reduce_adam_cast",
+              lambda: zs.adam_step(L, 0, 1, cfg, master, m, v, replica, zs.INDEX_FULL, grads=G))
+        phase(ph, "gather_7_peers", lambda: zs.gather_params(L, 0, 1, peers16 + [None], replica))
+
+    ms, kern = timed(args, torch, step)
+    acc_b, fb, gb = 10 * P, (4 * N + 26) * S, 4 * (N - 1) * S
+    add_rates(kern, "accumulate_fp32", acc_b)
+    add_rates(kern, "fused_fp32_reduce_adam_cast", fb)
+    add_rates(kern, "gather_7_peers", gb)
+    opt_ms = (kern["fused_fp32_reduce_adam_cast"]["ms_per_step"]
+              + kern["gather_7_peers"]["ms_per_step"])
+    out = base_line(args, "Megatron distributed-optimizer step shard params/sec (7B, N=8)",
+                    S / (ms * 1e-3), "params/s", ms,
+                    "Megatron DO, Psi=7.24e9, N=8, rank 7: 4 micro-batch fp32 accumulations "
+                    "over the whole buffer + fp32 reduce + Adam + bf16 + gather of 7 peers "
+                    "(the step also zeroes main_grad with torch, untimed per phase)",
+                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S, micro_batches=w.micro_batches)
+    out["optimizer_only_shard_params_per_s"] = S / (opt_ms * 1e-3)
+    out["kernels"] = kern
+    dom = max(("accumulate_fp32", acc_b), ("fused_fp32_reduce_adam_cast", fb),
+              key=lambda x: kern[x[0]]["ms_per_launch_mean"])
+    out["roofline"] = roofline(dom[0], dom[1], kern[dom[0]]["ms_per_launch_mean"])
+    out["cpu_baseline"] = None
+    return out
+
+
+def run_fsdp70b(args, torch, zs, np):
+    """Config 4: Llama-70B FSDP full shard, N = 64, rank 63: for each of the
+    81 units, fused reduce of 64 rank gradients + Adam + bf16 into the
+    unit's full buffer, then the gather of the unit's 63 peer shards.  The
+    per-unit working buffers are allocated once at the largest unit."""
+    from synthetic import WORKLOADS, grad_bits
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[4]
+    N, r = w.n_ranks, w.n_ranks - 1
+    units = list(w.units)
+    L = zs.shard_init("fsdp", N, r, units)
+    S = L.shard_len
+    q = [L.query(u) for u in range(len(units))]
+    smax = max(x["shard_len"] for x in q)
+    grads = [grad_bits(w, 0, k, smax, device=dev) for k in range(N)]
+    G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+    master = torch.empty(S, device=dev).normal_(0, 0.02)
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    full_unit = torch.empty(N * smax, dtype=torch.int16, device=dev)
+    peers = [torch.full((smax,), k + 1, dtype=torch.int16, device=dev) for k in range(N - 1)]
+    torch.cuda.synchronize()
+    t = [0]
+
+    def step(ph):
+        t[0] += 1
+        cfg = zs.adam_cfg(step=t[0])
+        for u, x in enumerate(q):
+            so = x["shard_off"]
+            phase(ph, "fused_reduce64_adam_cast",
+                  lambda u=u, so=so: zs.adam_step(L, u, u + 1, cfg, master[so:], m[so:], v[so:],
+                                                  full_unit, zs.INDEX_FULL, grads=G))
+            phase(ph, "gather_63_peers",
+                  lambda u=u: zs.gather_params(L, u, u + 1, peers + [None], full_unit))
+
+    ms, kern = timed(args, torch, step)
+    fb, gb = (2 * N + 26) * S, 4 * (N - 1) * S
+    for name, b in (("fused_reduce64_adam_cast", fb), ("gather_63_peers", gb)):
+        k = kern[name]
+        k["bytes_per_step"] = b
+        k["gbps"] = b / (k["ms_per_step"] * 1e-3) / 1e9
+    out = base_line(args, "Llama-70B FSDP per-unit sweep shard params/sec (N=64)",
+                    S / (ms * 1e-3), "params/s", ms,
+                    "Llama-70B FSDP full shard, N=64, rank 63: 81 units x (fused reduce of 64 "
+                    "rank grads + Adam + bf16 into the unit buffer, gather of 63 peers)",
+                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S, units=len(units))
+    out["kernels"] = kern
+    fk = kern["fused_reduce64_adam_cast"]
+    out["roofline"] = roofline("step_kernel<fused, N=64, bf16> (81 launches, summed)", fb,
+                               fk["ms_per_step"])
+    out["cpu_baseline"] = None
+    return out
+
+
+def calibrate_copy(args, torch, zs, np):
+    dev = torch.device("cuda:0")
+    n = args.calibrate_copy // 2
+    L = zs.shard_init("zero2", 1, 0, [n])
+    src = torch.ones(n, dtype=torch.int16, device=dev)
+    dst = torch.empty(n, dtype=torch.int16, device=dev)
+    for _ in range(3):
+        zs.gather_params(L, 0, 1, [src], dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        zs.gather_params(L, 0, 1, [src], dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"calibrate_copy_bytes": 2 * n, "ms": ms, "GBps": 4 * n / ms / 1e6}
 
 
 def counter_traffic():
@@ -210,7 +420,6 @@ def cpu_baseline(w, grads, master, S, r, budget_s):
     16M-element chunks are copied from the GPU and stepped (step 1) until the
     oracle has run for `budget_s` seconds; only oracle time is counted."""
     import numpy as np
-    import torch
 
     from oracle import _c
 
@@ -233,6 +442,29 @@ def cpu_baseline(w, grads, master, S, r, budget_s):
             "sample": f"first {done} of {S} elements of the rank-{r} shard, step 1, "
                       f"{chunk}-element chunks, {spent:.1f} s of oracle time "
                       f"(reduce 8 bf16 ranks + Adam + bf16 cast)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build simulates the N data-parallel ranks "
+              "inside one GPU's memory and has no multi-GPU path; run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fsdp_sharded_optimizer_shard_amd import zs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        out = calibrate_copy(args, torch, zs, np)
+    else:
+        run = {0: run_tiny, 1: run_gpt2_clip, 2: run_headline, 3: run_megatron,
+               4: run_fsdp70b}[args.config]
+        out = run(args, torch, zs, np)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -164,15 +164,15 @@ zero_status zero_layout_query(const zero_layout *layout, int32_t unit,
    with G_q indexed as grads->index says.  `out` is shard-indexed fp32.
    If `sumsq_partials` is non-NULL it receives exactly
    zero_reduce_partials_count(...) fp64 partial sums of out[i]^2 (each square
-   exact in fp64; one partial per 512 consecutive elements of a unit slice,
-   summed in a fixed order), for the global-norm clip; `n_partials` is the
-   capacity of that buffer. */
+   exact in fp64; one partial per 2048-element tile of a unit slice, summed
+   in a fixed order), for the global-norm clip; `n_partials` is the capacity
+   of that buffer. */
 zero_status zero_reduce_shard(const zero_layout *layout, int32_t unit_begin,
                               int32_t unit_end, const zero_grads *grads,
                               float *out, double *sumsq_partials,
                               int64_t n_partials, void *stream);
 
-/* Number of fp64 partials zero_reduce_shard writes for a range: 4 per
+/* Number of fp64 partials zero_reduce_shard writes for a range: one per
    2048-element tile of every unit slice in the range (a fixed function of
    the range, independent of the device and of the launch width). */
 int64_t zero_reduce_partials_count(const zero_layout *layout,
@@ -180,7 +180,7 @@ int64_t zero_reduce_partials_count(const zero_layout *layout,
 
 /* Global gradient-norm clip coefficient (not defined on the pages; PyTorch
    clip_grad_norm_ semantics): norm = sqrt(sum of the n partials in fp64, in
-   a fixed order: per-thread strided sums, then a fixed tree),
+   a fixed order for a given n: strided per-thread sums, then a fixed tree),
    *coef_out = min(1, fp32(max_norm / (norm + 1e-6))).
    `partials`, `coef_out` (one float) and `norm_out` (one double, may be
    NULL) are device pointers.  n >= 1, max_norm > 0. */

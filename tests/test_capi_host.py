@@ -183,12 +183,12 @@ def test_reduce_validation():
 
 def test_partials_count_is_a_fixed_function_of_the_range():
     L = zs.shard_init("zero2", 8, 0, [25_000_000] * 4 + [24_439_808])
-    # one partial per wave (512 elements) of every 2048-element tile
+    # one partial per 2048-element tile
     per = [zs.reduce_partials_count(L, u, u + 1) for u in range(5)]
-    assert per == [4 * -(-3_125_000 // 2048)] * 4 + [4 * -(-3_054_976 // 2048)]
+    assert per == [-(-3_125_000 // 2048)] * 4 + [-(-3_054_976 // 2048)]
     assert zs.reduce_partials_count(L, 0, 5) == sum(per)
     L = zs.shard_init("fsdp", 64, 0, [64 * 4096] * 40)     # 40 units -> two launches
-    assert zs.reduce_partials_count(L, 0, 40) == 4 * 2 * 40
+    assert zs.reduce_partials_count(L, 0, 40) == 2 * 40
 
 
 def test_gather_and_accumulate_and_clip_validation():
