@@ -76,6 +76,14 @@ _lib.zero_adam_step.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _P, _P,
 _lib.zero_adam_step.restype = _I32
 _lib.zero_gather_params.argtypes = [_P, _I32, _I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P]
 _lib.zero_gather_params.restype = _I32
+class _UnitIO(ctypes.Structure):
+    _fields_ = [("rank_grads", ctypes.POINTER(ctypes.c_void_p)),
+                ("peer_shards", ctypes.POINTER(ctypes.c_void_p)), ("unit_full", _P)]
+
+
+_lib.zero_fsdp_sweep.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _I32,
+                                 ctypes.POINTER(_UnitIO), _P, _P, _P, _I32, _P, _P]
+_lib.zero_fsdp_sweep.restype = _I32
 _lib.zero_grad_accumulate.argtypes = [_P, _P, _I64, _P]
 _lib.zero_grad_accumulate.restype = _I32
 _lib.zero_status_str.argtypes = [_I32]
@@ -85,7 +93,8 @@ _lib.zero_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("zero_shard_init", "zero_shard_destroy", "zero_layout_info", "zero_layout_query",
            "zero_reduce_shard", "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
-           "zero_gather_params", "zero_grad_accumulate", "zero_status_str", "zero_last_error")
+           "zero_gather_params", "zero_grad_accumulate", "zero_fsdp_sweep", "zero_status_str",
+           "zero_last_error")
 
 
 class ZeroShardError(RuntimeError):
@@ -220,6 +229,26 @@ def gather_params(layout: Layout, unit_begin: int, unit_end: int, shards, param_
     arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
     _check(_lib.zero_gather_params(layout.handle, unit_begin, unit_end, arr, len(ptrs),
                                    _addr(param_full), _stream(stream)), "zero_gather_params")
+
+
+def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, grad_dtype: int,
+               units, master, m, v, max_inflight: int = 2, step_stream=None,
+               gather_stream=None) -> None:
+    """units: one (rank_grads, peer_shards, unit_full) per unit of the range;
+    rank_grads / peer_shards are lists of world_n buffers (None allowed in
+    peer_shards).  gather_stream defaults to step_stream (sequential)."""
+    keep = []
+    arr = (_UnitIO * max(1, len(units)))()
+    for i, (grads, peers, full) in enumerate(units):
+        g = (ctypes.c_void_p * max(1, len(grads)))(*[_addr(x) for x in grads])
+        p = (ctypes.c_void_p * max(1, len(peers)))(*[_addr(x) for x in peers])
+        keep += [g, p]
+        arr[i] = _UnitIO(g, p, _addr(full))
+    ss = _stream(step_stream)
+    gs = ss if gather_stream is None else _stream(gather_stream)
+    _check(_lib.zero_fsdp_sweep(layout.handle, unit_begin, unit_end, ctypes.byref(cfg), grad_dtype,
+                                arr, _addr(master), _addr(m), _addr(v), max_inflight, ss, gs),
+           "zero_fsdp_sweep")
 
 
 def grad_accumulate(main_grad, micro_bf16, n: int, stream=None) -> None:

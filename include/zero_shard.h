@@ -222,6 +222,52 @@ zero_status zero_gather_params(const zero_layout *layout, int32_t unit_begin,
                                int32_t unit_end, const uint16_t *const *shards,
                                int32_t n, uint16_t *param_full, void *stream);
 
+/* ------------------------------------------------------ FSDP sweep -- */
+
+/* One unit's buffers for zero_fsdp_sweep. */
+typedef struct zero_unit_io {
+    const void *const *rank_grads;      /* host array of world_n device pointers:
+                                           this unit's rank gradients, each
+                                           indexed over this rank's slice of the
+                                           unit (s_u elements, unit-local)     */
+    const uint16_t *const *peer_shards; /* host array of world_n device pointers
+                                           (s_u bf16 each) gathered into the
+                                           unit buffer; NULL entries skipped,
+                                           this rank's own entry must be NULL  */
+    uint16_t *unit_full;                /* device, L_u bf16: the unit's full
+                                           flat parameters                     */
+} zero_unit_io;
+
+/* The FSDP per-unit sweep as a two-stream pipeline ("DP, ZeRO-1/2/3, FSDP"
+   notes, follow-up on how FSDP hides communication: the all-gather runs on
+   its own stream, the next unit's gather is prefetched, and
+   limit_all_gathers bounds how many gathered units exist at once).
+   For every unit u in [unit_begin, unit_end), in order:
+     on step_stream:   the fused reduce of io[u].rank_grads (grad_dtype) +
+                       Adam + bf16 of this rank's slice into io[u].unit_full
+                       (zero_adam_step on the single unit; master, m and v
+                       are shard-indexed from unit_begin, as everywhere);
+     on gather_stream: after that step, zero_gather_params of
+                       io[u].peer_shards into io[u].unit_full (an all-gather
+                       carries every rank's updated shard, so it follows the
+                       step of its unit).
+   max_inflight caps the pipeline: the step of unit u waits until the
+   gather of unit u - max_inflight has finished.  1 makes the sweep
+   sequential, 2 double-buffers (the step of unit u+1 overlaps the gather of
+   unit u), 0 means no cap.  When the call's work completes on step_stream,
+   every gather has completed too (step_stream waits for the last one).
+   gather_stream may equal step_stream (sequential).  Results are identical
+   to per-unit zero_adam_step + zero_gather_params calls.  Host-side errors
+   launch nothing; a HIP error part-way returns ZERO_ERR_HIP with the units
+   before it enqueued.  `io` is a host array of (unit_end - unit_begin)
+   entries. */
+zero_status zero_fsdp_sweep(const zero_layout *layout, int32_t unit_begin,
+                            int32_t unit_end, const zero_adam_cfg *cfg,
+                            int32_t grad_dtype, const zero_unit_io *io,
+                            float *master, float *m, float *v,
+                            int32_t max_inflight, void *step_stream,
+                            void *gather_stream);
+
 /* ------------------------------------------------------- accumulation -- */
 
 /* Megatron-style fp32 main-gradient accumulation of one micro-batch:

@@ -207,3 +207,25 @@ def test_empty_work_launches_nothing():
     _adam(L, 0, 2)
     zs.grad_accumulate(FAKE, FAKE, 0, 0)
     zs.gather_params(L, 0, 2, [FAKE] * 4, FAKE, 0)
+
+
+def test_fsdp_sweep_validation_launches_nothing():
+    L = zs.shard_init("fsdp", 4, 3, [4096, 100])
+    cfg = zs.adam_cfg(step=1)
+    good = ([FAKE] * 4, [FAKE, FAKE, FAKE, None], FAKE)
+    # a missing replica in the second unit is caught before the first launches
+    bad = ([FAKE, None, FAKE, FAKE], [FAKE, FAKE, FAKE, None], FAKE)
+    e = _err(zs.fsdp_sweep, L, 0, 2, cfg, zs.BF16, [good, bad], FAKE, FAKE, FAKE, 2, 0, 0)
+    assert e.status == zs.ERR_INVALID_ARG and "unit 1" in str(e) and "missing" in str(e)
+    own = ([FAKE] * 4, [FAKE] * 4, FAKE)
+    e = _err(zs.fsdp_sweep, L, 0, 2, cfg, zs.BF16, [good, own], FAKE, FAKE, FAKE, 2, 0, 0)
+    assert e.status == zs.ERR_INVALID_ARG and "own" in str(e)
+    mis = ([FAKE] * 4, [FAKE, FAKE, FAKE, None], FAKE + 1)
+    assert _err(zs.fsdp_sweep, L, 0, 2, cfg, zs.BF16, [good, mis], FAKE, FAKE, FAKE, 2, 0,
+                0).status == zs.ERR_ALIGNMENT
+    assert _err(zs.fsdp_sweep, L, 0, 2, cfg, zs.BF16, [good, good], FAKE, FAKE, FAKE, -1, 0,
+                0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.fsdp_sweep, L, 0, 2, cfg, 9, [good, good], FAKE, FAKE, FAKE, 2, 0,
+                0).status == zs.ERR_INVALID_ARG
+    # an empty range is fine and launches nothing
+    zs.fsdp_sweep(L, 1, 1, cfg, zs.BF16, [], FAKE, FAKE, FAKE, 2, 0, 0)
