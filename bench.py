@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--fsdp2", action="store_true",
+                    help="config 2 only: the exact Mistral-7B per-parameter dim-0 layout "
+                         "(291 parameters) instead of one flat unit")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
                     help="oracle time budget for the CPU baseline (headline only); 0 skips it")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -132,9 +135,15 @@ def run_headline(args, torch, zs, np):
     dev = torch.device("cuda:0")
     w = WORKLOADS[2]
     N, r = w.n_ranks, w.n_ranks - 1
-    L = zs.shard_init("zero3", N, r, list(w.units))
+    if args.fsdp2:
+        from synthetic import mistral7b_shapes
+        L = zs.shard_init_rows("fsdp2", N, r, mistral7b_shapes())
+    else:
+        L = zs.shard_init("zero3", N, r, list(w.units))
     S = L.shard_len
-    print(f"# setup: {w.name}, rank {r}, shard {S} elements", file=sys.stderr, flush=True)
+    U = L.info()["n_units"]
+    print(f"# setup: {w.name}, rank {r}, shard {S} elements, {U} units", file=sys.stderr,
+          flush=True)
     grads = [grad_bits(w, 0, q, S, device=dev) for q in range(N)]
     master = master_init(w, S, device=dev, rank=r)
     m = torch.zeros(S, device=dev)
@@ -150,8 +159,8 @@ def run_headline(args, torch, zs, np):
         t[0] += 1
         cfg = zs.adam_cfg(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=t[0])
         phase(ph, "fused_reduce_adam_cast",
-              lambda: zs.adam_step(L, 0, 1, cfg, master, m, v, full, zs.INDEX_FULL, grads=G))
-        phase(ph, "gather_7_peers", lambda: zs.gather_params(L, 0, 1, shard_ptrs, full))
+              lambda: zs.adam_step(L, 0, U, cfg, master, m, v, full, zs.INDEX_FULL, grads=G))
+        phase(ph, "gather_7_peers", lambda: zs.gather_params(L, 0, U, shard_ptrs, full))
 
     ms, kern = timed(args, torch, step)
     fused_b, gather_b = 42 * S, 4 * (N - 1) * S
@@ -161,10 +170,11 @@ def run_headline(args, torch, zs, np):
     if args.cpu_baseline_seconds > 0:
         cpu = cpu_baseline(w, grads, master, S, r, args.cpu_baseline_seconds)
     out = base_line(args, HEADLINE_METRIC, S / (ms * 1e-3), "params/s", ms,
-                    "Mistral-7B ZeRO-3 rank shard step: reduce 8 bf16 rank grads + Adam + "
+                    ("Mistral-7B FSDP2 per-parameter (291 params, dim-0 rows) " if args.fsdp2
+                     else "Mistral-7B ZeRO-3 ") +
+                    "rank shard step: reduce 8 bf16 rank grads + Adam + "
                     "bf16 cast into the flat buffer + gather of 7 peer shards",
-                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S,
-                    rank_flat_offset=L.query(0)["rank_flat_off"],
+                    psi=L.flat_len, n_ranks=N, rank=r, shard_elems=S, units=U,
                     algorithmic_bytes_per_step=fused_b + gather_b)
     out["step_gbps"] = (fused_b + gather_b) / (ms * 1e-3) / 1e9
     out["state_gbps_16psi_over_n"] = 16 * S / (ms * 1e-3) / 1e9

@@ -34,7 +34,7 @@ INDEX_FULL, INDEX_SHARD = 0, 1
 MAX_RANKS_PER_CALL = 64
 
 STRATEGY = {"ddp": DDP, "zero1": STAGE1, "zero1_allreduce": STAGE1, "zero2": STAGE2,
-            "zero3": STAGE3, "fsdp": FSDP, "megatron_do": MEGATRON_DO}
+            "zero3": STAGE3, "fsdp": FSDP, "fsdp2": FSDP, "megatron_do": MEGATRON_DO}
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
@@ -59,6 +59,11 @@ def adam_cfg(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, decoup
 
 _lib.zero_shard_init.argtypes = [ctypes.POINTER(_P), _I32, _I32, _I32, _I32, ctypes.POINTER(_I64)]
 _lib.zero_shard_init.restype = _I32
+_lib.zero_shard_init_rows.argtypes = [ctypes.POINTER(_P), _I32, _I32, _I32, _I32,
+                                      ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+_lib.zero_shard_init_rows.restype = _I32
+_lib.zero_layout_rows.argtypes = [_P, _I32] + [ctypes.POINTER(_I64)] * 3
+_lib.zero_layout_rows.restype = _I32
 _lib.zero_shard_destroy.argtypes = [_P]
 _lib.zero_shard_destroy.restype = None
 _lib.zero_layout_info.argtypes = [_P] + [ctypes.POINTER(_I64)] * 2 + [ctypes.POINTER(_I32)] * 4
@@ -91,7 +96,7 @@ _lib.zero_status_str.restype = ctypes.c_char_p
 _lib.zero_last_error.argtypes = []
 _lib.zero_last_error.restype = ctypes.c_char_p
 
-EXPORTS = ("zero_shard_init", "zero_shard_destroy", "zero_layout_info", "zero_layout_query",
+EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy", "zero_layout_info", "zero_layout_query",
            "zero_reduce_shard", "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
            "zero_gather_params", "zero_grad_accumulate", "zero_fsdp_sweep", "zero_status_str",
            "zero_last_error")
@@ -162,6 +167,12 @@ class Layout:
         keys = ("numel", "padded_len", "flat_off", "shard_len", "shard_off", "rank_flat_off")
         return dict(zip(keys, (x.value for x in v)))
 
+    def rows(self, unit: int) -> dict:
+        v = [_I64() for _ in range(3)]
+        _check(_lib.zero_layout_rows(self.handle, unit, *[ctypes.byref(x) for x in v]),
+               "zero_layout_rows")
+        return dict(zip(("cols", "first_row", "row_count"), (x.value for x in v)))
+
     @property
     def flat_len(self) -> int:
         return self.info()["flat_len"]
@@ -178,6 +189,18 @@ def shard_init(strategy, world_n: int, rank: int, unit_numel: Sequence[int]) -> 
     _check(_lib.zero_shard_init(ctypes.byref(h), s, world_n, rank, len(unit_numel), arr),
            "zero_shard_init")
     return Layout(h.value, unit_numel)
+
+
+def shard_init_rows(strategy, world_n: int, rank: int, shapes) -> Layout:
+    """FSDP2-style layout: one unit per (rows, cols) parameter."""
+    s = STRATEGY[strategy] if isinstance(strategy, str) else int(strategy)
+    n = len(shapes)
+    rows = (_I64 * max(1, n))(*[int(r) for r, _ in shapes])
+    cols = (_I64 * max(1, n))(*[int(c) for _, c in shapes])
+    h = _P()
+    _check(_lib.zero_shard_init_rows(ctypes.byref(h), s, world_n, rank, n, rows, cols),
+           "zero_shard_init_rows")
+    return Layout(h.value, [int(r) * int(c) for r, c in shapes])
 
 
 class Grads:

@@ -16,6 +16,7 @@ struct zero_layout {
     int32_t n_units;
     // Per unit u (size n_units), and the prefix tables F and R (size n_units + 1).
     std::vector<int64_t> numel;      // n_u
+    std::vector<int64_t> cols;       // elements per padding row (1: per element)
     std::vector<int64_t> padded;     // L_u
     std::vector<int64_t> slice;      // s_u
     std::vector<int64_t> flat_off;   // F_u, F_{U} = flat length

@@ -105,6 +105,25 @@ __device__ __forceinline__ TileWalk tile_walk(int64_t n_tiles)
     return {(int64_t)blockIdx.x, n_tiles, (int64_t)gridDim.x};
 }
 
+// The segment holding tile t: the last s with seg[s].tile0 <= t (seg[0].tile0
+// is 0).  A binary search -- at most 5 dependent scalar loads for 32
+// segments -- because with one block per tile every block looks its segment
+// up from scratch, and for a light kernel (the gather moves 16 bytes per
+// thread) a linear scan over the table costs more than the copy.
+template <typename SegT>
+__device__ __forceinline__ int find_seg(const SegT *seg, int n_segs, int64_t t)
+{
+    int lo = 0, hi = n_segs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (seg[mid].tile0 <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -373,12 +392,9 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a)
     const float coef = (MODE == kApply && a.clip) ? *a.clip : 1.0f;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    int s = 0;
     const TileWalk tw = tile_walk(a.n_tiles);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
-        while (s + 1 < a.n_segs && t >= a.seg[s + 1].tile0)
-            ++s;
-        const Seg &sg = a.seg[s];
+        const Seg &sg = a.seg[find_seg(a.seg, a.n_segs, t)];
         const int64_t j0 = (t - sg.tile0) * kTile + wave * kWaveElems + lane * 4;
         const int64_t j[2] = {j0, j0 + kWaveElems / 2};
         const bool vec = sg.vec && a.vec_ptrs;
@@ -434,12 +450,9 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a)
     const int y = blockIdx.y;
     const uint16_t *src = a.src[y];
     const int64_t q = a.rank_of[y];
-    int s = 0;
     const TileWalk tw = tile_walk(a.n_tiles);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
-        while (s + 1 < a.n_segs && t >= a.seg[s + 1].tile0)
-            ++s;
-        const GSeg &sg = a.seg[s];
+        const GSeg &sg = a.seg[find_seg(a.seg, a.n_segs, t)];
         const int64_t j = (t - sg.tile0) * kTile + (int64_t)threadIdx.x * kVec;
         if (j >= sg.len)
             continue;

@@ -6,6 +6,9 @@
 // rank keeps and updates only its own 1/N (same notes, concepts "ZeRO-1 / 2
 // / 3").  Each unit is zero-padded at its tail to a multiple of N.  Under
 // DDP nothing is sharded ("Data Parallel, ZeRO and FSDP", plain DDP).
+// zero_shard_init_rows pads and slices in whole dim-0 rows instead: FSDP2
+// shards each parameter on its own along dim 0 (same notes, "FSDP2 vs
+// FSDP1"), with torch.chunk row counts.
 #include <cstdarg>
 #include <cstdio>
 #include <new>
@@ -43,8 +46,11 @@ zero_status check_range(const zero_layout *L, int32_t unit_begin, int32_t unit_e
 
 extern "C" {
 
-zero_status zero_shard_init(zero_layout **out, zero_strategy strategy, int32_t world_n,
-                            int32_t rank, int32_t n_units, const int64_t *unit_numel)
+// Shared planner: unit u has rows[u] rows of cols[u] elements; padding and
+// slicing are in whole rows (cols = 1 gives the element-granular layout).
+static zero_status plan_layout(zero_layout **out, zero_strategy strategy, int32_t world_n,
+                               int32_t rank, int32_t n_units, const int64_t *rows,
+                               const int64_t *cols)
 {
     using zs::fail;
     if (!out)
@@ -56,7 +62,7 @@ zero_status zero_shard_init(zero_layout **out, zero_strategy strategy, int32_t w
         return fail(ZERO_ERR_INVALID_ARG, "world_n must be >= 1 (got %d)", world_n);
     if (rank < 0 || rank >= world_n)
         return fail(ZERO_ERR_INVALID_ARG, "rank %d outside [0, %d)", rank, world_n);
-    if (n_units < 1 || !unit_numel)
+    if (n_units < 1 || !rows)
         return fail(ZERO_ERR_INVALID_ARG, "need at least one unit and a size array");
 
     zero_layout *L = new (std::nothrow) zero_layout;
@@ -70,6 +76,7 @@ zero_status zero_shard_init(zero_layout **out, zero_strategy strategy, int32_t w
         L->parts = sharded ? world_n : 1;
         L->n_units = n_units;
         L->numel.resize(n_units);
+        L->cols.resize(n_units);
         L->padded.resize(n_units);
         L->slice.resize(n_units);
         L->flat_off.resize(n_units + 1);
@@ -78,23 +85,25 @@ zero_status zero_shard_init(zero_layout **out, zero_strategy strategy, int32_t w
         const int64_t kMax = INT64_MAX / 4;  // keeps every byte offset representable
         int64_t F = 0, R = 0;
         for (int32_t u = 0; u < n_units; ++u) {
-            const int64_t n = unit_numel[u];
-            if (n < 0) {
+            const int64_t nr = rows[u];
+            const int64_t c = cols ? cols[u] : 1;
+            if (nr < 0 || c < 1) {
                 delete L;
-                return fail(ZERO_ERR_INVALID_ARG, "unit %d has negative size", u);
+                return fail(ZERO_ERR_INVALID_ARG, "unit %d has negative size or cols < 1", u);
             }
-            if (n > kMax - P || F > kMax - (n + P)) {
+            if (nr > kMax - P || c > kMax / (nr + P) || F > kMax - (nr + P) * c) {
                 delete L;
                 return fail(ZERO_ERR_INVALID_ARG, "layout size overflows at unit %d", u);
             }
-            const int64_t padded = (n + P - 1) / P * P;
-            L->numel[u] = n;
-            L->padded[u] = padded;
-            L->slice[u] = padded / P;
+            const int64_t chunk_rows = (nr + P - 1) / P;
+            L->numel[u] = nr * c;
+            L->cols[u] = c;
+            L->slice[u] = chunk_rows * c;
+            L->padded[u] = chunk_rows * c * P;
             L->flat_off[u] = F;
             L->shard_off[u] = R;
-            F += padded;
-            R += padded / P;
+            F += L->padded[u];
+            R += L->slice[u];
         }
         L->flat_off[n_units] = F;
         L->shard_off[n_units] = R;
@@ -105,6 +114,21 @@ zero_status zero_shard_init(zero_layout **out, zero_strategy strategy, int32_t w
     *out = L;
     zs::clear_error();
     return ZERO_OK;
+}
+
+zero_status zero_shard_init(zero_layout **out, zero_strategy strategy, int32_t world_n,
+                            int32_t rank, int32_t n_units, const int64_t *unit_numel)
+{
+    return plan_layout(out, strategy, world_n, rank, n_units, unit_numel, nullptr);
+}
+
+zero_status zero_shard_init_rows(zero_layout **out, zero_strategy strategy, int32_t world_n,
+                                 int32_t rank, int32_t n_units, const int64_t *unit_rows,
+                                 const int64_t *unit_cols)
+{
+    if (!unit_cols)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "unit_cols is NULL");
+    return plan_layout(out, strategy, world_n, rank, n_units, unit_rows, unit_cols);
 }
 
 void zero_shard_destroy(zero_layout *layout) { delete layout; }
@@ -138,6 +162,25 @@ zero_status zero_layout_query(const zero_layout *L, int32_t unit, int64_t *numel
     if (shard_len) *shard_len = L->slice[unit];
     if (shard_off) *shard_off = L->shard_off[unit];
     if (rank_flat_off) *rank_flat_off = L->flat_off[unit] + (int64_t)L->rank * L->slice[unit];
+    return ZERO_OK;
+}
+
+zero_status zero_layout_rows(const zero_layout *L, int32_t unit, int64_t *cols,
+                             int64_t *first_row, int64_t *row_count)
+{
+    if (!L)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    if (unit < 0 || unit >= L->n_units)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "unit %d outside [0, %d)", unit, L->n_units);
+    const int64_t c = L->cols[unit];
+    const int64_t rows = L->numel[unit] / c;
+    const int64_t chunk = L->slice[unit] / c;
+    int64_t first = (int64_t)L->rank * chunk;
+    first = first < rows ? first : rows;
+    const int64_t left = rows - first;
+    if (cols) *cols = c;
+    if (first_row) *first_row = first;
+    if (row_count) *row_count = left < chunk ? left : chunk;
     return ZERO_OK;
 }
 

@@ -140,6 +140,20 @@ zero_status zero_shard_init(zero_layout **out, zero_strategy strategy,
                             int32_t world_n, int32_t rank, int32_t n_units,
                             const int64_t *unit_numel);
 
+/* FSDP2-style per-parameter dim-0 sharding ("DP, ZeRO-1/2/3, FSDP" notes,
+   follow-up "FSDP2 vs FSDP1": every parameter sharded on its own along dim
+   0, so a rank holds whole rows and its sharded state dict needs no
+   gather).  Unit u is a parameter of unit_rows[u] x unit_cols[u] elements
+   (row-major; unit_cols >= 1, unit_rows >= 0).  It is cut into chunks of
+   c_u = ceil(rows / N) rows (the torch.chunk rule): rank r holds rows
+   [r c_u, min((r+1) c_u, rows)), padded with zero rows to c_u rows, so
+   s_u = c_u * cols and L_u = N * s_u.  Offsets F_u, R_u and every other
+   call work exactly as for zero_shard_init. */
+zero_status zero_shard_init_rows(zero_layout **out, zero_strategy strategy,
+                                 int32_t world_n, int32_t rank,
+                                 int32_t n_units, const int64_t *unit_rows,
+                                 const int64_t *unit_cols);
+
 void zero_shard_destroy(zero_layout *layout);
 
 /* Whole-layout sizes: padded flat length sum L_u, this rank's shard length
@@ -155,6 +169,14 @@ zero_status zero_layout_query(const zero_layout *layout, int32_t unit,
                               int64_t *numel, int64_t *padded_len,
                               int64_t *flat_off, int64_t *shard_len,
                               int64_t *shard_off, int64_t *rank_flat_off);
+
+/* The rows of unit u this rank really holds (the rest of its slice is
+   padding): *cols (1 for element-granular layouts), *first_row and
+   *row_count (0 when this rank's chunk lies past the end).  For an
+   element-granular layout rows are elements.  Any output may be NULL. */
+zero_status zero_layout_rows(const zero_layout *layout, int32_t unit,
+                             int64_t *cols, int64_t *first_row,
+                             int64_t *row_count);
 
 /* ------------------------------------------------------------ reduce -- */
 

@@ -29,6 +29,7 @@ MODEL_STATE_BYTES = {
     "zero2": lambda psi, n: 2 * psi + Fr(14 * psi, n),
     "zero3": lambda psi, n: Fr(16 * psi, n),
     "fsdp": lambda psi, n: Fr(16 * psi, n),
+    "fsdp2": lambda psi, n: Fr(16 * psi, n),
     "megatron_do": lambda psi, n: 6 * psi + Fr(12 * psi, n),
 }
 
@@ -39,6 +40,7 @@ COMM_ELEMENTS = {
     "zero2": lambda psi: 2 * psi,
     "zero3": lambda psi: 3 * psi,
     "fsdp": lambda psi: 3 * psi,
+    "fsdp2": lambda psi: 3 * psi,
     "megatron_do": lambda psi: 2 * psi,
 }
 

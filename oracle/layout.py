@@ -14,12 +14,20 @@ What the pages fix:
     "reduce-scatter and all-gather"; "Behind the scenes...", section "ZeRO:
     The Dial Between DDP and FSDP").
 
+  * FSDP2 instead shards every parameter on its own along dim 0 (DTensor),
+    so each rank holds whole rows and a sharded state dict needs no gather
+    ("dp-zero-fsdp", follow-up "FSDP2 vs FSDP1").
+
 Readings taken (where the pages are silent):
   * Each unit of n elements is padded with zeros at its tail to the next
     multiple of N, L = ceil(n / N) * N, and rank r owns the contiguous slice
     [r * L/N, (r + 1) * L/N) of that unit.  Units are laid out one after the
     other in the flat buffer.  A gradient bucket is such a unit.
   * DDP has no sharding: the single "shard" is the whole buffer.
+  * FSDP2 (plan_rows): a parameter of `rows` x `cols` is cut into chunks of
+    c = ceil(rows / N) rows (the torch.chunk rule); rank r holds rows
+    [r c, min((r + 1) c, rows)) and is padded with zero rows to c rows, so
+    the unit is padded to c N rows and every slice is c * cols elements.
 """
 from dataclasses import dataclass
 from typing import List, Optional, Sequence, Tuple
@@ -28,10 +36,11 @@ from typing import List, Optional, Sequence, Tuple
 @dataclass(frozen=True)
 class Unit:
     numel: int      # n_u, unpadded
-    padded: int     # L_u = ceil(n_u / N) * N
+    padded: int     # L_u = ceil(n_u / N) * N (FSDP2: ceil(rows / N) * N * cols)
     shard: int      # s_u = L_u / N
     flat_off: int   # F_u = sum of L_j for j < u
     shard_off: int  # R_u = sum of s_j for j < u
+    cols: int = 1   # elements per dim-0 row (1: element-granular padding)
 
 
 @dataclass(frozen=True)
@@ -77,6 +86,35 @@ def plan(unit_numel: Sequence[int], n_ranks: int, rank: int, sharded: bool = Tru
         flat += padded
         shard += s
     return Layout(n_ranks, rank if sharded else 0, sharded, tuple(units))
+
+
+def plan_rows(shapes: Sequence[Tuple[int, int]], n_ranks: int, rank: int) -> Layout:
+    """FSDP2 per-parameter dim-0 sharding: one unit per (rows, cols) parameter."""
+    if n_ranks < 1 or not (0 <= rank < n_ranks):
+        raise ValueError("need N >= 1 and 0 <= rank < N")
+    if len(shapes) < 1 or any(int(r) < 0 or int(c) < 1 for r, c in shapes):
+        raise ValueError("need at least one parameter, rows >= 0 and cols >= 1")
+    units = []
+    flat = 0
+    shard = 0
+    for rows, cols in shapes:
+        rows, cols = int(rows), int(cols)
+        chunk = -(-rows // n_ranks)                 # rows per rank
+        s = chunk * cols
+        units.append(Unit(rows * cols, s * n_ranks, s, flat, shard, cols))
+        flat += s * n_ranks
+        shard += s
+    return Layout(n_ranks, rank, True, tuple(units))
+
+
+def valid_rows(layout: Layout, u: int) -> Tuple[int, int]:
+    """(first row, row count) of parameter u that this rank really holds;
+    the rest of its slice is padding."""
+    U = layout.units[u]
+    rows = U.numel // U.cols
+    chunk = U.shard // U.cols
+    first = min(layout.rank * chunk, rows)
+    return first, max(0, min(chunk, rows - first))
 
 
 def owner_of(layout: Layout, flat_index: int) -> Optional[Tuple[int, int, int]]:

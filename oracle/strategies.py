@@ -31,9 +31,10 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 from . import _c
-from .layout import Layout, plan
+from .layout import Layout, plan, plan_rows
 
-STRATEGIES = ("ddp", "zero1", "zero1_allreduce", "zero2", "zero3", "fsdp", "megatron_do")
+STRATEGIES = ("ddp", "zero1", "zero1_allreduce", "zero2", "zero3", "fsdp", "fsdp2", "megatron_do")
+SHARDED_PARAMS = ("zero3", "fsdp", "fsdp2")
 
 
 @dataclass
@@ -110,17 +111,21 @@ def all_gather(layouts: Sequence[Layout], shards: Sequence[np.ndarray]) -> np.nd
     return full
 
 
-def make_cluster(strategy: str, unit_numel: Sequence[int], n_ranks: int,
+def make_cluster(strategy: str, unit_numel: Sequence, n_ranks: int,
                  master0: np.ndarray) -> Cluster:
     """N ranks holding the initial state.  master0 is the fp32 master in
     model order (sum of the unit sizes, no padding); bf16 params start as its
-    rounding; m = v = 0; padding positions are zero."""
+    rounding; m = v = 0; padding positions are zero.  For "fsdp2" the units
+    are (rows, cols) parameter shapes."""
     if strategy not in STRATEGIES:
         raise ValueError(strategy)
     sharded = strategy != "ddp"
-    layouts = [plan(unit_numel, n_ranks, r, sharded) for r in range(n_ranks)]
+    if strategy == "fsdp2":
+        layouts = [plan_rows(unit_numel, n_ranks, r) for r in range(n_ranks)]
+    else:
+        layouts = [plan(unit_numel, n_ranks, r, sharded) for r in range(n_ranks)]
     P = layouts[0].flat_len
-    assert master0.dtype == np.float32 and master0.size == sum(unit_numel)
+    assert master0.dtype == np.float32 and master0.size == sum(U.numel for U in layouts[0].units)
     master0 = pad(layouts[0], master0)
     params_full = _c.f32_to_bf16(master0)
     ranks = []
@@ -138,7 +143,7 @@ def make_cluster(strategy: str, unit_numel: Sequence[int], n_ranks: int,
             else:
                 grads = np.zeros(lay.shard_len, np.uint16)
             params = (_shard_of(params_full, lay).copy()
-                      if strategy in ("zero3", "fsdp") else params_full.copy())
+                      if strategy in SHARDED_PARAMS else params_full.copy())
         ranks.append(RankState(params, grads, master,
                                np.zeros_like(master), np.zeros_like(master)))
     return Cluster(strategy, layouts, ranks)
@@ -193,7 +198,7 @@ def step(cl: Cluster, cfg: AdamConfig, t: int, grads: Sequence, micro: int = 1) 
         cl.comm_log.append(("all_reduce", 2 * P))
     else:
         cl.comm_log.append(("reduce_scatter", P))
-    if s in ("zero3", "fsdp"):
+    if s in SHARDED_PARAMS:
         # forward and backward each all-gather the parameters once
         cl.comm_log.append(("all_gather_forward", P))
         cl.comm_log.append(("all_gather_backward", P))
@@ -212,7 +217,7 @@ def step(cl: Cluster, cfg: AdamConfig, t: int, grads: Sequence, micro: int = 1) 
             R.grads[:] = _shard_of(full_grads[q], lay)
         _c.adam(hp, g, R.master, R.m, R.v)
         new_param_shards.append(_c.f32_to_bf16(R.master))
-    if s in ("zero3", "fsdp"):
+    if s in SHARDED_PARAMS:
         for q in range(N):
             cl.ranks[q].params[:] = new_param_shards[q]
     else:
@@ -225,7 +230,7 @@ def step(cl: Cluster, cfg: AdamConfig, t: int, grads: Sequence, micro: int = 1) 
 def full_params(cl: Cluster, q: int = 0, padded: bool = False) -> np.ndarray:
     """Rank q's view of the full bf16 parameter buffer (gathered, not logged,
     for ZeRO-3 / FSDP), in model order unless `padded`."""
-    if cl.strategy in ("zero3", "fsdp"):
+    if cl.strategy in SHARDED_PARAMS:
         full = all_gather(cl.layouts, [R.params for R in cl.ranks])
     else:
         full = cl.ranks[q].params.copy()

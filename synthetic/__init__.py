@@ -45,6 +45,20 @@ def llama70b_units() -> List[int]:
     return [layer] * LLAMA70B_LAYERS + [root]
 
 
+MISTRAL7B_HIDDEN, MISTRAL7B_FFN, MISTRAL7B_KV, MISTRAL7B_VOCAB, MISTRAL7B_LAYERS = (
+    4096, 14336, 1024, 32000, 32)
+
+
+def mistral7b_shapes() -> List[Tuple[int, int]]:
+    """(rows, cols) of every Mistral-7B parameter in module order (dim 0 =
+    output features; 1-D norm weights are (H, 1)): embedding, 32 x (input
+    norm, q, k, v, o, post-attention norm, gate, up, down), final norm,
+    untied lm_head.  7,241,732,096 elements."""
+    h, f, kv, V = MISTRAL7B_HIDDEN, MISTRAL7B_FFN, MISTRAL7B_KV, MISTRAL7B_VOCAB
+    layer = [(h, 1), (h, h), (kv, h), (kv, h), (h, h), (h, 1), (f, h), (f, h), (h, f)]
+    return [(V, h)] + layer * MISTRAL7B_LAYERS + [(h, 1), (V, h)]
+
+
 @dataclass(frozen=True)
 class Workload:
     cfg: int

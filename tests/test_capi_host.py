@@ -229,3 +229,31 @@ def test_fsdp_sweep_validation_launches_nothing():
                 0).status == zs.ERR_INVALID_ARG
     # an empty range is fine and launches nothing
     zs.fsdp_sweep(L, 1, 1, cfg, zs.BF16, [], FAKE, FAKE, FAKE, 2, 0, 0)
+
+
+@settings(max_examples=150, deadline=None)
+@given(shapes=st.lists(st.tuples(st.integers(0, 300), st.integers(1, 40)), min_size=1,
+                       max_size=30),
+       n=st.integers(1, 70), data=st.data())
+def test_rows_layout_matches_oracle(shapes, n, data):
+    from oracle.layout import plan_rows, valid_rows
+    r = data.draw(st.integers(0, n - 1))
+    L = zs.shard_init_rows("fsdp2", n, r, shapes)
+    O = plan_rows(shapes, n, r)
+    assert L.flat_len == O.flat_len and L.shard_len == O.shard_len
+    for u, U in enumerate(O.units):
+        assert L.query(u) == {"numel": U.numel, "padded_len": U.padded, "flat_off": U.flat_off,
+                              "shard_len": U.shard, "shard_off": U.shard_off,
+                              "rank_flat_off": O.owned(u)[0]}
+        first, cnt = valid_rows(O, u)
+        assert L.rows(u) == {"cols": U.cols, "first_row": first, "row_count": cnt}
+
+
+def test_rows_layout_rejects_bad_shapes():
+    assert _err(zs.shard_init_rows, "fsdp2", 4, 0, [(5, 0)]).status == zs.ERR_INVALID_ARG
+    assert _err(zs.shard_init_rows, "fsdp2", 4, 0, [(-1, 3)]).status == zs.ERR_INVALID_ARG
+    assert _err(zs.shard_init_rows, "fsdp2", 4, 0, [(2 ** 40, 2 ** 30)]).status == \
+        zs.ERR_INVALID_ARG
+    # element-granular layouts report rows = elements
+    L = zs.shard_init("zero2", 4, 3, [10])
+    assert L.rows(0) == {"cols": 1, "first_row": 9, "row_count": 1}

@@ -1,0 +1,120 @@
+"""GPU parity of FSDP2 per-parameter dim-0 layouts (zero_shard_init_rows):
+the same kernels, driven by row-granular slices, against the oracle.
+
+  * uneven row splits (rows not divisible by N, ranks past the last chunk,
+    1-D weights) for every rank of N = 8, fused into one full buffer;
+  * the exact Mistral-7B per-parameter layout (291 parameters,
+    7,241,732,096 elements) at N = 8, rank 7, one call over all parameters
+    (10 launches of up to 32), 2 steps, sampled.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import _c, strategies
+from oracle.layout import valid_rows
+from synthetic import grad_bits, master_init, mistral7b_shapes, small_workload
+
+pytestmark = pytest.mark.gpu
+zs = None
+DEV = "cuda:0"
+
+
+def setup_module(module):
+    global zs
+    from fsdp_sharded_optimizer_shard_amd import zs as _zs
+    zs = _zs
+
+
+def test_fsdp2_uneven_rows_all_ranks():
+    shapes = [(250, 64), (9, 512), (64, 1), (1, 4096), (17, 8), (2048, 3)]
+    n = 8
+    psi = sum(r * c for r, c in shapes)
+    w = small_workload([psi], n, "fsdp2", steps=3, cfg=9, weight_decay=0.01, decoupled=True)
+    master0 = master_init(w, psi).numpy()
+    oc = strategies.make_cluster("fsdp2", shapes, n, master0)
+    lays = [zs.shard_init_rows("fsdp2", n, r, shapes) for r in range(n)]
+    U = len(shapes)
+    lay0 = oc.layouts[0]
+    full = torch.zeros(lay0.flat_len, dtype=torch.int16, device=DEV)
+    mfull = strategies.pad(lay0, master0)
+    st = []
+    idxs = []
+    for r in range(n):
+        idx = np.concatenate([np.arange(b, b + k) for b, _, k in oc.layouts[r].owned_runs()])
+        idxs.append(idx)
+        st.append([torch.from_numpy(mfull[idx].copy()).to(DEV),
+                   torch.zeros(idx.size, device=DEV), torch.zeros(idx.size, device=DEV)])
+    cfg = strategies.AdamConfig(weight_decay=0.01, decoupled=True)
+    for t in range(w.steps):
+        grads = [grad_bits(w, t, q, psi).numpy().view(np.uint16) for q in range(n)]
+        strategies.step(oc, cfg, t + 1, grads)
+        gd = [torch.from_numpy(strategies.pad(lay0, g).view(np.int16)).to(DEV) for g in grads]
+        G = zs.Grads(gd, zs.BF16, zs.INDEX_FULL)
+        for r in range(n):
+            zs.adam_step(lays[r], 0, U, zs.adam_cfg(weight_decay=0.01, decoupled=True, step=t + 1),
+                         *st[r], full, zs.INDEX_FULL, grads=G)
+        torch.cuda.synchronize()
+        assert np.array_equal(full.cpu().numpy().view(np.uint16),
+                              strategies.full_params(oc, padded=True)), t
+    S = strategies.full_state(oc, padded=True)
+    for r in range(n):
+        for k, name in enumerate(("master", "m", "v")):
+            assert np.array_equal(st[r][k].cpu().numpy().view(np.uint32),
+                                  S[name][idxs[r]].view(np.uint32)), (r, name)
+        # the library's valid rows agree with the oracle's (state dict export)
+        for u in range(U):
+            first, cnt = valid_rows(oc.layouts[r], u)
+            assert lays[r].rows(u) == {"cols": shapes[u][1], "first_row": first,
+                                       "row_count": cnt}
+
+
+def test_fsdp2_mistral7b_full_size_sampled():
+    shapes = mistral7b_shapes()
+    n, r = 8, 7
+    L = zs.shard_init_rows("fsdp2", n, r, shapes)
+    S = L.shard_len
+    assert L.flat_len == 7_241_732_096 and S == 905_216_512
+    w = small_workload([L.flat_len], n, "fsdp2", steps=2, cfg=8)
+    rng = np.random.default_rng(8)
+    idx = np.unique(np.concatenate([rng.integers(0, S, 1 << 20),
+                                    [L.query(u)["shard_off"] for u in range(len(shapes))],
+                                    [S - 1]])).astype(np.int64)
+    tidx = torch.from_numpy(idx).to(DEV)
+    master = master_init(w, S, device=DEV, rank=r)
+    m = torch.zeros(S, device=DEV)
+    v = torch.zeros(S, device=DEV)
+    own = torch.empty(S, dtype=torch.int16, device=DEV)
+    p_h = master[tidx].cpu().numpy().copy()
+    m_h = np.zeros(idx.size, np.float32)
+    v_h = np.zeros(idx.size, np.float32)
+    par_h = np.empty(idx.size, np.uint16)
+    for t in range(w.steps):
+        grads = [grad_bits(w, t, q, S, device=DEV) for q in range(n)]
+        samp = [g[tidx].cpu().numpy().view(np.uint16) for g in grads]
+        zs.adam_step(L, 0, len(shapes), zs.adam_cfg(step=t + 1), master, m, v, own, zs.INDEX_SHARD,
+                     grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
+        del grads
+        _c.rank_step(_c.hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, t + 1, False), samp, 1.0,
+                     p_h, m_h, v_h, par_h)
+    torch.cuda.synchronize()
+    assert np.array_equal(master[tidx].cpu().numpy().view(np.uint32), p_h.view(np.uint32))
+    assert np.array_equal(m[tidx].cpu().numpy().view(np.uint32), m_h.view(np.uint32))
+    assert np.array_equal(v[tidx].cpu().numpy().view(np.uint32), v_h.view(np.uint32))
+    assert np.array_equal(own[tidx].cpu().numpy().view(np.uint16), par_h)
+    # gather the 7 peer shards into the full per-parameter buffer
+    full = torch.empty(L.flat_len, dtype=torch.int16, device=DEV)
+    peers = [torch.full((S,), q + 1, dtype=torch.int16, device=DEV) for q in range(n - 1)]
+    zs.gather_params(L, 0, len(shapes), peers + [own], full)
+    torch.cuda.synchronize()
+    # spot-check every parameter's rank slots
+    for u in range(0, len(shapes), 7):
+        x = L.query(u)
+        s, F = x["shard_len"], x["flat_off"]
+        for q in (0, 3, n - 1):
+            got = full[F + q * s: F + q * s + min(s, 64)].cpu().numpy().view(np.uint16)
+            if q < n - 1:
+                assert np.all(got == q + 1), (u, q)
+            else:
+                want = own[x["shard_off"]: x["shard_off"] + min(s, 64)].cpu().numpy().view(np.uint16)
+                assert np.array_equal(got, want), u
