@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--ddp-buckets", action="store_true",
+                    help="config 1 only: one DDP replica, each bucket's reduce launched as "
+                         "backward would produce it (last bucket first), then clip + AdamW")
     ap.add_argument("--fsdp2", action="store_true",
                     help="config 2 only: the exact Mistral-7B per-parameter dim-0 layout "
                          "(291 parameters) instead of one flat unit")
@@ -281,6 +284,61 @@ def run_gpt2_clip(args, torch, zs, np):
     return out
 
 
+def run_gpt2_ddp_buckets(args, torch, zs, np):
+    """Config 1 as DDP with bucket-as-ready reduction: one replica; the 5
+    gradient buckets are reduced (all-reduce arithmetic over the 8 ranks)
+    one launch each, last bucket first, then the global clip coefficient and
+    one AdamW call over the whole replica."""
+    from synthetic import WORKLOADS, grad_bits, master_init
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[1]
+    N, U = w.n_ranks, len(w.units)
+    L = zs.shard_init("ddp", N, 0, list(w.units))
+    P = L.flat_len
+    grads = [grad_bits(w, 0, q, P, device=dev) for q in range(N)]
+    fo = [L.query(u)["flat_off"] for u in range(U)]
+    Gu = [zs.Grads([g[fo[u]:] for g in grads], zs.BF16, zs.INDEX_FULL) for u in range(U)]
+    tiles = [zs.reduce_partials_count(L, u, u + 1) for u in range(U)]
+    offs = [sum(tiles[:u]) for u in range(U)]
+    partials = torch.empty(sum(tiles), dtype=torch.float64, device=dev)
+    g = torch.empty(P, device=dev)
+    coef = torch.empty(1, device=dev)
+    p = master_init(w, P, device=dev)
+    m = torch.zeros(P, device=dev)
+    v = torch.zeros(P, device=dev)
+    out = torch.empty(P, dtype=torch.int16, device=dev)
+    t = [0]
+
+    def step(ph):
+        t[0] += 1
+        cfg = zs.adam_cfg(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
+                          weight_decay=w.weight_decay, decoupled=w.decoupled, step=t[0])
+        for u in reversed(range(U)):
+            phase(ph, f"reduce_bucket_{u}",
+                  lambda u=u: zs.reduce_shard(L, u, u + 1, Gu[u], g[fo[u]:], partials[offs[u]:],
+                                              tiles[u]))
+        phase(ph, "clip_coef", lambda: zs.clip_coef(partials, partials.numel(),
+                                                    w.max_grad_norm, coef))
+        phase(ph, "adamw_apply_cast",
+              lambda: zs.adam_step(L, 0, U, cfg, p, m, v, out, zs.INDEX_FULL, grad_fp32=g,
+                                   clip_coef=coef))
+
+    ms, kern = timed(args, torch, step)
+    for u in range(U):
+        add_rates(kern, f"reduce_bucket_{u}", (2 * N + 4) * w.units[u])
+    add_rates(kern, "adamw_apply_cast", 30 * P)
+    out_line = base_line(args, "GPT-2-small DDP bucket-as-ready step params/sec (one replica)",
+                         P / (ms * 1e-3), "params/s", ms,
+                         "GPT-2-small DDP replica, N=8: per-bucket reduce launches (last bucket "
+                         "first) + global clip + one AdamW",
+                         psi=w.psi, n_ranks=N, buckets=list(w.units))
+    out_line["kernels"] = kern
+    out_line["roofline"] = roofline("adamw_apply_cast", 30 * P,
+                                    kern["adamw_apply_cast"]["ms_per_launch_mean"])
+    out_line["cpu_baseline"] = None
+    return out_line
+
+
 def run_megatron(args, torch, zs, np):
     """Config 3: Psi = 7.24e9, N = 8, rank 7: four bf16 micro-batch
     gradients accumulated into the fp32 main gradient over the whole buffer,
@@ -495,8 +553,8 @@ def main():
     if args.calibrate_copy:
         out = calibrate_copy(args, torch, zs, np)
     else:
-        run = {0: run_tiny, 1: run_gpt2_clip, 2: run_headline, 3: run_megatron,
-               4: run_fsdp70b}[args.config]
+        run = {0: run_tiny, 1: run_gpt2_ddp_buckets if args.ddp_buckets else run_gpt2_clip,
+               2: run_headline, 3: run_megatron, 4: run_fsdp70b}[args.config]
         out = run(args, torch, zs, np)
     print(json.dumps(out), flush=True)
 

@@ -70,13 +70,14 @@ _lib.zero_layout_info.argtypes = [_P] + [ctypes.POINTER(_I64)] * 2 + [ctypes.POI
 _lib.zero_layout_info.restype = _I32
 _lib.zero_layout_query.argtypes = [_P, _I32] + [ctypes.POINTER(_I64)] * 6
 _lib.zero_layout_query.restype = _I32
-_lib.zero_reduce_shard.argtypes = [_P, _I32, _I32, ctypes.POINTER(_Grads), _P, _P, _I64, _P]
+_lib.zero_reduce_shard.argtypes = [_P, _I32, _I32, ctypes.POINTER(_Grads), _P, _I32, _P, _I64,
+                                   _P]
 _lib.zero_reduce_shard.restype = _I32
 _lib.zero_reduce_partials_count.argtypes = [_P, _I32, _I32]
 _lib.zero_reduce_partials_count.restype = _I64
 _lib.zero_clip_coef.argtypes = [_P, _I64, ctypes.c_float, _P, _P, _P]
 _lib.zero_clip_coef.restype = _I32
-_lib.zero_adam_step.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _P, _P,
+_lib.zero_adam_step.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _P, _I32, _P,
                                 ctypes.POINTER(_Grads), _P, _P, _P, _P, _I32, _P]
 _lib.zero_adam_step.restype = _I32
 _lib.zero_gather_params.argtypes = [_P, _I32, _I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P]
@@ -207,6 +208,7 @@ class Grads:
     """Marshalled zero_grads; keeps its ctypes arrays alive."""
 
     def __init__(self, bufs, dtype: int = BF16, index=INDEX_FULL):
+        self._keep = list(bufs)              # keeps tensors alive; sliceable by callers
         ptrs = [_addr(b) for b in bufs]
         self._ptrs = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
         self._index = None
@@ -226,9 +228,11 @@ def reduce_partials_count(layout: Layout, unit_begin: int, unit_end: int) -> int
 
 
 def reduce_shard(layout: Layout, unit_begin: int, unit_end: int, grads: Grads, out,
-                 sumsq_partials=None, n_partials: int = 0, stream=None) -> None:
+                 sumsq_partials=None, n_partials: int = 0, stream=None,
+                 out_index: int = INDEX_SHARD) -> None:
     _check(_lib.zero_reduce_shard(layout.handle, unit_begin, unit_end, grads.ref() if grads else None,
-                                  _addr(out), _addr(sumsq_partials), n_partials, _stream(stream)),
+                                  _addr(out), out_index, _addr(sumsq_partials), n_partials,
+                                  _stream(stream)),
            "zero_reduce_shard")
 
 
@@ -239,9 +243,10 @@ def clip_coef(partials, n: int, max_norm: float, coef_out, norm_out=None, stream
 
 def adam_step(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, master, m, v,
               param_out, param_index: int = INDEX_FULL, grad_fp32=None, clip_coef=None,
-              grads: Optional[Grads] = None, stream=None) -> None:
+              grads: Optional[Grads] = None, stream=None, grad_index: int = INDEX_SHARD) -> None:
     _check(_lib.zero_adam_step(layout.handle, unit_begin, unit_end, ctypes.byref(cfg),
-                               _addr(grad_fp32), _addr(clip_coef), grads.ref() if grads else None,
+                               _addr(grad_fp32), grad_index, _addr(clip_coef),
+                               grads.ref() if grads else None,
                                _addr(master), _addr(m), _addr(v), _addr(param_out), param_index,
                                _stream(stream)), "zero_adam_step")
 

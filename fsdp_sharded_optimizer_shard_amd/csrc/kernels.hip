@@ -79,9 +79,13 @@ struct StepArgs {
     int32_t pow2;
     int32_t vec_ptrs;    // every base pointer is 16-byte aligned
     float *master, *m, *v;
-    const float *gin;    // kApply: shard-indexed averaged gradient
+    const float *gin;    // kApply: averaged gradient
+    int32_t gin_full;    // kApply: 1 if gin is full-indexed, 0 if shard-indexed
+    int32_t _pad2;
     const float *clip;   // kApply: device clip coefficient or null
-    float *gout;         // kReduce: shard-indexed averaged gradient
+    float *gout;         // kReduce: averaged gradient
+    int32_t gout_full;   // kReduce: 1 if gout is full-indexed, 0 if shard-indexed
+    int32_t _pad3;
     double *partials;    // kReduce: one fp64 sum of squares per tile, or null
     uint16_t *pout;      // bf16 parameter output
     int32_t pout_full;   // 1: full-indexed, 0: shard-indexed
@@ -316,7 +320,8 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const Seg &sg, co
     if (MODE == kApply) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const f32x4 gv = ld_nt(reinterpret_cast<const f32x4 *>(a.gin + si[h]));
+            const f32x4 gv =
+                ld_nt(reinterpret_cast<const f32x4 *>(a.gin + (a.gin_full ? fi[h] : si[h])));
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 g[h][e] = gv[e] * coef;
@@ -336,7 +341,7 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const Seg &sg, co
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 sq = sq + (double)g[h][e] * (double)g[h][e];
-            st_nt(reinterpret_cast<f32x4 *>(a.gout + si[h]),
+            st_nt(reinterpret_cast<f32x4 *>(a.gout + (a.gout_full ? fi[h] : si[h])),
                   f32x4{g[h][0], g[h][1], g[h][2], g[h][3]});
         }
         return;
@@ -369,11 +374,11 @@ __device__ __forceinline__ void step_scalar(const StepArgs &a, const Seg &sg, in
     for (int64_t e = 0; e < cnt; ++e) {
         float g;
         if (MODE == kApply)
-            g = a.gin[si + e] * coef;
+            g = a.gin[(a.gin_full ? fi : si) + e] * coef;
         else
             g = mean_of(a, reduce1<NR, BF16>(a, si + e, fi + e));
         if (MODE == kReduce) {
-            a.gout[si + e] = g;
+            a.gout[(a.gout_full ? fi : si) + e] = g;
             sq = sq + (double)g * (double)g;
         } else {
             float p = a.master[si + e], m = a.m[si + e], v = a.v[si + e];
@@ -757,8 +762,8 @@ int64_t zero_reduce_partials_count(const zero_layout *L, int32_t ub, int32_t ue)
 }
 
 zero_status zero_reduce_shard(const zero_layout *L, int32_t ub, int32_t ue,
-                              const zero_grads *grads, float *out, double *partials,
-                              int64_t n_partials, void *stream)
+                              const zero_grads *grads, float *out, int32_t out_index,
+                              double *partials, int64_t n_partials, void *stream)
 {
     zero_status st = check_range(L, ub, ue);
     if (st != ZERO_OK)
@@ -769,6 +774,8 @@ zero_status zero_reduce_shard(const zero_layout *L, int32_t ub, int32_t ue,
         return st;
     if (reinterpret_cast<uintptr_t>(out) % 4)
         return fail(ZERO_ERR_ALIGNMENT, "out is misaligned");
+    if (out_index != ZERO_INDEX_FULL && out_index != ZERO_INDEX_SHARD)
+        return fail(ZERO_ERR_INVALID_ARG, "unknown out_index %d", out_index);
     if (partials) {
         if (reinterpret_cast<uintptr_t>(partials) % 8)
             return fail(ZERO_ERR_ALIGNMENT, "sumsq_partials is misaligned");
@@ -788,6 +795,7 @@ zero_status zero_reduce_shard(const zero_layout *L, int32_t ub, int32_t ue,
         if (a.n_tiles == 0)
             return ZERO_OK;
         a.gout = out;
+        a.gout_full = out_index == ZERO_INDEX_FULL;
         a.partials = partials ? partials + poff : nullptr;
         poff += a.n_tiles;
         return launch_mode<kReduce>(a, grads->dtype == ZERO_BF16, 0,
@@ -815,7 +823,7 @@ zero_status zero_clip_coef(const double *partials, int64_t n, float max_norm, fl
 }
 
 zero_status zero_adam_step(const zero_layout *L, int32_t ub, int32_t ue,
-                           const zero_adam_cfg *cfg, const float *grad_fp32,
+                           const zero_adam_cfg *cfg, const float *grad_fp32, int32_t grad_index,
                            const float *clip_coef, const zero_grads *grads, float *master,
                            float *m, float *v, uint16_t *param_out, int32_t param_index,
                            void *stream)
@@ -840,6 +848,8 @@ zero_status zero_adam_step(const zero_layout *L, int32_t ub, int32_t ue,
         return fail(ZERO_ERR_INVALID_ARG, "master, m, v and param_out are required");
     if (param_index != ZERO_INDEX_FULL && param_index != ZERO_INDEX_SHARD)
         return fail(ZERO_ERR_INVALID_ARG, "unknown param_index %d", param_index);
+    if (grad_index != ZERO_INDEX_FULL && grad_index != ZERO_INDEX_SHARD)
+        return fail(ZERO_ERR_INVALID_ARG, "unknown grad_index %d", grad_index);
     if (reinterpret_cast<uintptr_t>(master) % 4 || reinterpret_cast<uintptr_t>(m) % 4 ||
         reinterpret_cast<uintptr_t>(v) % 4 || reinterpret_cast<uintptr_t>(param_out) % 2 ||
         reinterpret_cast<uintptr_t>(grad_fp32) % 4 || reinterpret_cast<uintptr_t>(clip_coef) % 4)
@@ -863,6 +873,7 @@ zero_status zero_adam_step(const zero_layout *L, int32_t ub, int32_t ue,
         a.m = m;
         a.v = v;
         a.gin = grad_fp32;
+        a.gin_full = grad_index == ZERO_INDEX_FULL;
         a.clip = clip_coef;
         a.pout = param_out;
         a.pout_full = param_index == ZERO_INDEX_FULL;

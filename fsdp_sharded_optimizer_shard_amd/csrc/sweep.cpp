@@ -112,8 +112,8 @@ extern "C" zero_status zero_fsdp_sweep(const zero_layout *L, int32_t ub, int32_t
             return st;
         const zero_grads g{x.rank_grads, nullptr, n, grad_dtype, ZERO_INDEX_SHARD, 0};
         const int64_t so = L->shard_off[u] - L->shard_off[ub];
-        st = zero_adam_step(L, u, u + 1, cfg, nullptr, nullptr, &g, master + so, m + so, v + so,
-                            x.unit_full, ZERO_INDEX_FULL, step_stream);
+        st = zero_adam_step(L, u, u + 1, cfg, nullptr, ZERO_INDEX_SHARD, nullptr, &g, master + so,
+                            m + so, v + so, x.unit_full, ZERO_INDEX_FULL, step_stream);
         if (st != ZERO_OK)
             return st;
         if (two) {

@@ -183,7 +183,10 @@ zero_status zero_layout_rows(const zero_layout *layout, int32_t unit,
 /* Reduce-scatter arithmetic: for every element of this rank's slices of
    units [unit_begin, unit_end),
        out[i] = (G_0[i] + G_1[i] + ... + G_{N-1}[i]) / N      (fp32)
-   with G_q indexed as grads->index says.  `out` is shard-indexed fp32.
+   with G_q indexed as grads->index says.  `out` is fp32, indexed as
+   `out_index` says: ZERO_INDEX_SHARD for this rank's reduce-scatter result,
+   ZERO_INDEX_FULL to write this rank's slices into a full flat buffer (the
+   N ranks' calls together then form the all-reduce).
    If `sumsq_partials` is non-NULL it receives exactly
    zero_reduce_partials_count(...) fp64 partial sums of out[i]^2 (each square
    exact in fp64; one partial per 2048-element tile of a unit slice, summed
@@ -191,7 +194,8 @@ zero_status zero_layout_rows(const zero_layout *layout, int32_t unit,
    of that buffer. */
 zero_status zero_reduce_shard(const zero_layout *layout, int32_t unit_begin,
                               int32_t unit_end, const zero_grads *grads,
-                              float *out, double *sumsq_partials,
+                              float *out, int32_t out_index,
+                              double *sumsq_partials,
                               int64_t n_partials, void *stream);
 
 /* Number of fp64 partials zero_reduce_shard writes for a range: one per
@@ -214,8 +218,15 @@ zero_status zero_clip_coef(const double *partials, int64_t n, float max_norm,
 /* Adam / AdamW on this rank's slices of units [unit_begin, unit_end), then
    bf16 rounding of the new master into `param_out`.
    Gradient source, exactly one of:
-     grad_fp32 != NULL: shard-indexed fp32 averaged gradient (from
-                        zero_reduce_shard), multiplied by *clip_coef (a
+     grad_fp32 != NULL: fp32 averaged gradient, indexed as `grad_index`
+                        says: ZERO_INDEX_SHARD for a reduce-scatter result
+                        (zero_reduce_shard on this layout), ZERO_INDEX_FULL
+                        for an all-reduce result over this layout's whole
+                        flat buffer (zero_reduce_shard of every rank's
+                        layout with out_index = ZERO_INDEX_FULL -- ZeRO-1
+                        implemented with all-reduce, "DP, ZeRO-1/2/3, FSDP"
+                        notes, follow-up on the ZeRO-1 / ZeRO-2
+                        communication gap); multiplied by *clip_coef (a
                         device float; NULL means 1);
      grads != NULL:     fused path -- the N ranks' buffers are reduced
                         (as zero_reduce_shard) in the same pass, so each
@@ -227,7 +238,8 @@ zero_status zero_clip_coef(const double *partials, int64_t n, float max_norm,
    (ZERO_INDEX_SHARD, ZeRO-3 / FSDP). */
 zero_status zero_adam_step(const zero_layout *layout, int32_t unit_begin,
                            int32_t unit_end, const zero_adam_cfg *cfg,
-                           const float *grad_fp32, const float *clip_coef,
+                           const float *grad_fp32, int32_t grad_index,
+                           const float *clip_coef,
                            const zero_grads *grads, float *master, float *m,
                            float *v, uint16_t *param_out, int32_t param_index,
                            void *stream);

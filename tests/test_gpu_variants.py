@@ -1,0 +1,132 @@
+"""GPU parity of two variants of the step.
+
+  * ZeRO-1 implemented with all-reduce ("dp-zero-fsdp", follow-up on the
+    ZeRO-1 / ZeRO-2 communication gap): every rank's slice of the average is
+    written into one full fp32 buffer (the all-reduce arithmetic, N
+    reduce-scatters), then each rank takes Adam on its slice of that full
+    gradient (grad_index = FULL).  Identical to the oracle's
+    zero1_allreduce strategy, clip included.
+  * DDP with bucket-as-ready reduction ("Data Parallel, ZeRO and FSDP",
+    plain DDP: each bucket's all-reduce starts as soon as backward produced
+    it): per-bucket reduce launches in reverse bucket order, then the clip
+    and one Adam call.  The partials land where the whole-range call puts
+    them, so the clip coefficient and every result are identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import _c, strategies
+from synthetic import grad_bits, master_init, small_workload
+
+pytestmark = pytest.mark.gpu
+zs = None
+DEV = "cuda:0"
+
+
+def setup_module(module):
+    global zs
+    from fsdp_sharded_optimizer_shard_amd import zs as _zs
+    zs = _zs
+
+
+def h16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def test_zero1_over_allreduce_matches_oracle():
+    units, n = [5000, 333, 20000, 7], 4
+    w = small_workload(units, n, "zero1_allreduce", steps=3, cfg=7, weight_decay=0.01,
+                       decoupled=True, max_grad_norm=1e-3, outlier_frac=0.01)
+    psi = sum(units)
+    master0 = master_init(w, psi).numpy()
+    oc = strategies.make_cluster("zero1_allreduce", units, n, master0)
+    lay0 = oc.layouts[0]
+    lays = [zs.shard_init("zero1", n, r, units) for r in range(n)]
+    U = len(units)
+    P = lays[0].flat_len
+    mfull = strategies.pad(lay0, master0)
+    st = []
+    for r in range(n):
+        idx = np.concatenate([np.arange(b, b + k) for b, _, k in oc.layouts[r].owned_runs()])
+        st.append([torch.from_numpy(mfull[idx].copy()).to(DEV),
+                   torch.zeros(idx.size, device=DEV), torch.zeros(idx.size, device=DEV)])
+    full = torch.zeros(P, dtype=torch.int16, device=DEV)
+    gavg = torch.empty(P, device=DEV)
+    counts = [zs.reduce_partials_count(L, 0, U) for L in lays]
+    partials = torch.empty(sum(counts), dtype=torch.float64, device=DEV)
+    coef = torch.empty(1, device=DEV)
+    cfg = strategies.AdamConfig(weight_decay=0.01, decoupled=True, max_grad_norm=1e-3)
+    for t in range(w.steps):
+        grads = [grad_bits(w, t, q, psi).numpy().view(np.uint16) for q in range(n)]
+        strategies.step(oc, cfg, t + 1, grads)
+        G = zs.Grads([torch.from_numpy(strategies.pad(lay0, g).view(np.int16)).to(DEV)
+                      for g in grads], zs.BF16, zs.INDEX_FULL)
+        off = 0
+        for q, L in enumerate(lays):          # the all-reduce: N slices of one buffer
+            zs.reduce_shard(L, 0, U, G, gavg, partials[off:], counts[q], out_index=zs.INDEX_FULL)
+            off += counts[q]
+        zs.clip_coef(partials, partials.numel(), 1e-3, coef)
+        for r, L in enumerate(lays):
+            zs.adam_step(L, 0, U, zs.adam_cfg(weight_decay=0.01, decoupled=True, step=t + 1),
+                         *st[r], full, zs.INDEX_FULL, grad_fp32=gavg, grad_index=zs.INDEX_FULL,
+                         clip_coef=coef)
+        torch.cuda.synchronize()
+        want_avg = _c.average([strategies.pad(lay0, g) for g in grads])
+        assert np.array_equal(gavg.cpu().numpy().view(np.uint32), want_avg.view(np.uint32))
+        assert np.array_equal(h16(full), strategies.full_params(oc, padded=True)), t
+    S = strategies.full_state(oc, padded=True)
+    for r in range(n):
+        idx = np.concatenate([np.arange(b, b + k) for b, _, k in oc.layouts[r].owned_runs()])
+        for k, name in enumerate(("master", "m", "v")):
+            assert np.array_equal(st[r][k].cpu().numpy().view(np.uint32),
+                                  S[name][idx].view(np.uint32)), (r, name)
+
+
+def test_ddp_bucket_as_ready_equals_whole_range():
+    buckets, n = [25000, 25000, 24439, 4096, 1], 8
+    w = small_workload(buckets, n, "ddp", steps=2, cfg=6, weight_decay=0.01, decoupled=True,
+                       max_grad_norm=1.0, outlier_frac=0.01)
+    psi = sum(buckets)
+    master0 = master_init(w, psi).numpy()
+    oc = strategies.make_cluster("ddp", buckets, n, master0)
+    L = zs.shard_init("ddp", n, 0, buckets)
+    U = len(buckets)
+    assert L.flat_len == psi
+    tiles = [zs.reduce_partials_count(L, u, u + 1) for u in range(U)]
+    offs = [sum(tiles[:u]) for u in range(U)]
+    assert sum(tiles) == zs.reduce_partials_count(L, 0, U)
+    runs = {}
+    for mode in ("buckets", "whole"):
+        p = torch.from_numpy(master0.copy()).to(DEV)
+        m = torch.zeros(psi, device=DEV)
+        v = torch.zeros(psi, device=DEV)
+        out = torch.zeros(psi, dtype=torch.int16, device=DEV)
+        g = torch.empty(psi, device=DEV)
+        partials = torch.empty(sum(tiles), dtype=torch.float64, device=DEV)
+        coef = torch.empty(1, device=DEV)
+        coefs = []
+        for t in range(w.steps):
+            grads = [grad_bits(w, t, q, psi).numpy().view(np.uint16) for q in range(n)]
+            G = zs.Grads([torch.from_numpy(x.view(np.int16)).to(DEV) for x in grads], zs.BF16,
+                         zs.INDEX_FULL)
+            if mode == "buckets":
+                for u in reversed(range(U)):      # backward produces the last bucket first
+                    fo = L.query(u)["flat_off"]
+                    Gu = zs.Grads([x[fo:] for x in G._keep], zs.BF16, zs.INDEX_FULL)
+                    zs.reduce_shard(L, u, u + 1, Gu, g[fo:], partials[offs[u]:], tiles[u])
+            else:
+                zs.reduce_shard(L, 0, U, G, g, partials, sum(tiles))
+            zs.clip_coef(partials, partials.numel(), 1.0, coef)
+            zs.adam_step(L, 0, U, zs.adam_cfg(weight_decay=0.01, decoupled=True, step=t + 1),
+                         p, m, v, out, zs.INDEX_FULL, grad_fp32=g, clip_coef=coef)
+            torch.cuda.synchronize()
+            coefs.append(coef.item())
+            if mode == "buckets":
+                strategies.step(oc, strategies.AdamConfig(weight_decay=0.01, decoupled=True,
+                                                          max_grad_norm=1.0), t + 1, grads)
+        runs[mode] = (h16(out), p.cpu().numpy(), coefs)
+    assert runs["buckets"][2] == runs["whole"][2]
+    assert np.array_equal(runs["buckets"][0], runs["whole"][0])
+    assert np.array_equal(runs["buckets"][1].view(np.uint32), runs["whole"][1].view(np.uint32))
+    assert np.array_equal(runs["buckets"][0], strategies.full_params(oc))
