@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--ddp-buckets", action="store_true",
                     help="config 1 only: one DDP replica, each bucket's reduce launched as "
                          "backward would produce it (last bucket first), then clip + AdamW")
+    ap.add_argument("--fsdp-linear", action="store_true",
+                    help="the hand-written FSDP linear layer (Mistral-7B MLP up projection, "
+                         "in 4096, out 14336, 4096 tokens per rank, N=8, rank 7) instead of a "
+                         "config")
     ap.add_argument("--fsdp2", action="store_true",
                     help="config 2 only: the exact Mistral-7B per-parameter dim-0 layout "
                          "(291 parameters) instead of one flat unit")
@@ -472,6 +476,87 @@ def run_fsdp70b(args, torch, zs, np):
     return out
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def run_fsdp_linear(args, torch, zs, np):
+    """One rank's FSDP linear-layer training step, N = 8 simulated ranks:
+    forward (all-gather W, transpose, Y = X W), backward for this rank
+    (re-gather, dX = dY W^T, transposes, dW = X^T dY) and the other 7 ranks'
+    local dW (simulated), the reduce-scatter of the 8 dW into this rank's
+    rows, and Adam on the W shard."""
+    from synthetic import small_workload, grad_bits
+    dev = torch.device("cuda:0")
+    N, r, inf, outf, batch = 8, 7, 4096, 14336, 4096
+    L = zs.shard_init_rows("fsdp2", N, r, [(inf, outf)])
+    S, Lu = L.shard_len, L.query(0)["padded_len"]
+    w = small_workload([inf * outf], N, "fsdp2", cfg=5)
+    shards = [grad_bits(w, 0, q, S, device=dev) for q in range(N)]
+    xs = [torch.randn(batch, inf, device=dev).to(torch.bfloat16).view(torch.int16) for _ in range(N)]
+    dys = [(torch.randn(batch, outf, device=dev) * 1e-2).to(torch.bfloat16).view(torch.int16)
+           for _ in range(N)]
+    w_full = torch.empty(Lu, dtype=torch.int16, device=dev)
+    w_t = torch.empty(outf * inf, dtype=torch.int16, device=dev)
+    x_t = torch.empty(inf * batch, dtype=torch.int16, device=dev)
+    dy_t = torch.empty(outf * batch, dtype=torch.int16, device=dev)
+    y = torch.empty((batch, outf), dtype=torch.int16, device=dev)
+    dx = torch.empty((batch, inf), dtype=torch.int16, device=dev)
+    dws = [torch.empty(Lu, device=dev) for _ in range(N)]
+    gshard = torch.empty(S, device=dev)
+    master = torch.randn(S, device=dev) * 0.02
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    own = torch.empty(S, dtype=torch.int16, device=dev)
+    G = zs.Grads(dws, zs.FP32, zs.INDEX_FULL)
+    t = [0]
+
+    def step(ph):
+        t[0] += 1
+        phase(ph, "gather_w", lambda: zs.gather_params(L, 0, 1, shards, w_full))
+        phase(ph, "transpose_w", lambda: zs.transpose_bf16(inf, outf, w_full, outf, w_t, inf))
+        phase(ph, "gemm_forward", lambda: zs.gemm_bf16_nt(batch, outf, inf, xs[r], inf, w_t, inf,
+                                                          y, outf, zs.BF16))
+        phase(ph, "gather_w", lambda: zs.gather_params(L, 0, 1, shards, w_full))
+        phase(ph, "gemm_dx", lambda: zs.gemm_bf16_nt(batch, inf, outf, dys[r], outf, w_full, outf,
+                                                     dx, inf, zs.BF16))
+        for q in range(N):
+            phase(ph, "transpose_x_dy", lambda q=q: (
+                zs.transpose_bf16(batch, inf, xs[q], inf, x_t, batch),
+                zs.transpose_bf16(batch, outf, dys[q], outf, dy_t, batch)))
+            phase(ph, "gemm_dw", lambda q=q: zs.gemm_bf16_nt(inf, outf, batch, x_t, batch, dy_t,
+                                                             batch, dws[q], outf, zs.FP32))
+        phase(ph, "reduce_scatter_dw", lambda: zs.reduce_shard(L, 0, 1, G, gshard))
+        phase(ph, "adam_shard", lambda: zs.adam_step(L, 0, 1, zs.adam_cfg(step=t[0]), master, m, v,
+                                                     own, zs.INDEX_SHARD, grad_fp32=gshard))
+
+    ms, kern = timed(args, torch, step)
+    flops = 2.0 * batch * inf * outf
+    for name, count in (("gemm_forward", 1), ("gemm_dx", 1), ("gemm_dw", N)):
+        k = kern[name]
+        k["flops_per_launch"] = flops
+        k["tflops"] = flops * count / (k["ms_per_step"] * 1e-3) / 1e12
+    kern["reduce_scatter_dw"]["gbps"] = (4 * N + 4) * S / (
+        kern["reduce_scatter_dw"]["ms_per_step"] * 1e-3) / 1e9
+    out = base_line(args, "FSDP linear-layer training step tokens/sec per rank "
+                          "(Mistral-7B MLP up projection, N=8)",
+                    batch / (ms * 1e-3), "tokens/s", ms,
+                    "hand-written FSDP linear layer, W 4096 x 14336 row-sharded over 8 ranks, "
+                    "4096 tokens per rank: gather + Y = X W, gather + dX, the 8 ranks' dW, "
+                    "reduce-scatter of dW, Adam on the shard",
+                    in_features=inf, out_features=outf, tokens_per_rank=batch, n_ranks=N, rank=r)
+    out["dtype"] = "bf16 (fp32 accumulate)"
+    out["kernels"] = kern
+    gemm_ms = sum(kern[k]["ms_per_step"] for k in ("gemm_forward", "gemm_dx", "gemm_dw"))
+    out["gemm_tflops"] = flops * (N + 2) / (gemm_ms * 1e-3) / 1e12
+    out["roofline"] = {"bound": "mfma", "kernel": "gemm_nt_kernel (bf16, fp32 accumulate), "
+                                                   "all 10 launches of the step",
+                       "achieved": out["gemm_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": out["gemm_tflops"] / MFMA_BF16_PEAK_TFLOPS,
+                       "traffic": None}
+    out["cpu_baseline"] = None
+    return out
+
+
 def calibrate_copy(args, torch, zs, np):
     dev = torch.device("cuda:0")
     n = args.calibrate_copy // 2
@@ -552,6 +637,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.calibrate_copy:
         out = calibrate_copy(args, torch, zs, np)
+    elif args.fsdp_linear:
+        out = run_fsdp_linear(args, torch, zs, np)
     else:
         run = {0: run_tiny, 1: run_gpt2_ddp_buckets if args.ddp_buckets else run_gpt2_clip,
                2: run_headline, 3: run_megatron, 4: run_fsdp70b}[args.config]

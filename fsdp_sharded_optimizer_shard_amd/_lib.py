@@ -90,6 +90,16 @@ class _UnitIO(ctypes.Structure):
 _lib.zero_fsdp_sweep.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _I32,
                                  ctypes.POINTER(_UnitIO), _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_sweep.restype = _I32
+_lib.zero_gemm_bf16_nt.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I32, _P]
+_lib.zero_gemm_bf16_nt.restype = _I32
+_lib.zero_transpose_bf16.argtypes = [_I64, _I64, _P, _I64, _P, _I64, _P]
+_lib.zero_transpose_bf16.restype = _I32
+_lib.zero_fsdp_linear_forward.argtypes = [_P, _I32, ctypes.POINTER(ctypes.c_void_p), _I64, _P, _P,
+                                          _P, _P, _I32, _P]
+_lib.zero_fsdp_linear_forward.restype = _I32
+_lib.zero_fsdp_linear_backward.argtypes = [_P, _I32, ctypes.POINTER(ctypes.c_void_p), _I64, _P,
+                                           _P, _P, _P, _P, _P, _I32, _P, _P]
+_lib.zero_fsdp_linear_backward.restype = _I32
 _lib.zero_grad_accumulate.argtypes = [_P, _P, _I64, _P]
 _lib.zero_grad_accumulate.restype = _I32
 _lib.zero_status_str.argtypes = [_I32]
@@ -99,8 +109,9 @@ _lib.zero_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy", "zero_layout_info", "zero_layout_query",
            "zero_reduce_shard", "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
-           "zero_gather_params", "zero_grad_accumulate", "zero_fsdp_sweep", "zero_status_str",
-           "zero_last_error")
+           "zero_gather_params", "zero_grad_accumulate", "zero_fsdp_sweep", "zero_gemm_bf16_nt",
+           "zero_transpose_bf16", "zero_fsdp_linear_forward", "zero_fsdp_linear_backward",
+           "zero_status_str", "zero_last_error")
 
 
 class ZeroShardError(RuntimeError):
@@ -277,6 +288,36 @@ def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, gra
     _check(_lib.zero_fsdp_sweep(layout.handle, unit_begin, unit_end, ctypes.byref(cfg), grad_dtype,
                                 arr, _addr(master), _addr(m), _addr(v), max_inflight, ss, gs),
            "zero_fsdp_sweep")
+
+
+def gemm_bf16_nt(M: int, N: int, K: int, A, lda: int, B, ldb: int, C, ldc: int,
+                 c_dtype: int = FP32, stream=None) -> None:
+    _check(_lib.zero_gemm_bf16_nt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, c_dtype,
+                                  _stream(stream)), "zero_gemm_bf16_nt")
+
+
+def transpose_bf16(rows: int, cols: int, src, lds: int, dst, ldd: int, stream=None) -> None:
+    _check(_lib.zero_transpose_bf16(rows, cols, _addr(src), lds, _addr(dst), ldd, _stream(stream)),
+           "zero_transpose_bf16")
+
+
+def _ptrs(bufs):
+    return (ctypes.c_void_p * max(1, len(bufs)))(*[_addr(b) for b in bufs])
+
+
+def fsdp_linear_forward(layout: Layout, unit: int, w_shards, batch: int, x, w_full, w_t, y,
+                        y_dtype: int = BF16, stream=None) -> None:
+    _check(_lib.zero_fsdp_linear_forward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
+                                         _addr(w_full), _addr(w_t), _addr(y), y_dtype,
+                                         _stream(stream)), "zero_fsdp_linear_forward")
+
+
+def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy, w_full, x_t,
+                         dy_t, dx, dw_full, dx_dtype: int = BF16, stream=None) -> None:
+    _check(_lib.zero_fsdp_linear_backward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
+                                          _addr(dy), _addr(w_full), _addr(x_t), _addr(dy_t),
+                                          _addr(dx), dx_dtype, _addr(dw_full), _stream(stream)),
+           "zero_fsdp_linear_backward")
 
 
 def grad_accumulate(main_grad, micro_bf16, n: int, stream=None) -> None:

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libzeroshard.so")
 SOURCES = [os.path.join(CSRC, "layout.cpp"), os.path.join(CSRC, "kernels.hip"),
-           os.path.join(CSRC, "sweep.cpp")]
+           os.path.join(CSRC, "sweep.cpp"), os.path.join(CSRC, "gemm.hip"),
+           os.path.join(CSRC, "linear.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,0 +1,103 @@
+// A hand-written FSDP linear layer for one rank ("DP, ZeRO-1/2/3, FSDP"
+// notes, follow-up on writing one FSDP linear layer by hand): every rank
+// stores 1/N of the rows of W; forward all-gathers the full W and computes
+// X W for the local batch; backward all-gathers W again, computes dX and the
+// full-shape dW locally; the reduce-scatter of dW over the ranks is
+// zero_reduce_shard on the N ranks' dW buffers.
+//
+// W is unit `unit` of a row layout (zero_shard_init_rows) with rows =
+// in_features and cols = out_features, so Y = X W takes (batch x in) to
+// (batch x out).  The contractions run on the MFMA GEMM in its natural
+// form C = A B^T (both operands contiguous along K); the other operand
+// orders come from the bf16 transpose.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace zs {
+zero_status zero_rows_fill(float *p, int64_t ld, int64_t r0, int64_t r1, int64_t cols,
+                           hipStream_t s);
+}
+
+namespace {
+
+struct Dims {
+    int64_t in, out, in_pad;
+};
+
+zero_status layer_dims(const zero_layout *L, int32_t unit, Dims *d)
+{
+    if (!L)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    if (unit < 0 || unit >= L->n_units)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "unit %d outside [0, %d)", unit, L->n_units);
+    d->out = L->cols[unit];
+    d->in = L->numel[unit] / d->out;
+    d->in_pad = L->padded[unit] / d->out;
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zero_status zero_fsdp_linear_forward(const zero_layout *L, int32_t unit,
+                                     const uint16_t *const *w_shards, int64_t batch,
+                                     const uint16_t *x, uint16_t *w_full, uint16_t *w_t, void *y,
+                                     int32_t y_dtype, void *stream)
+{
+    Dims d;
+    zero_status st = layer_dims(L, unit, &d);
+    if (st != ZERO_OK)
+        return st;
+    if (!w_shards || !x || !w_full || !w_t || !y || batch < 0)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "w_shards, x, w_full, w_t, y and batch >= 0 "
+                        "are required");
+    for (int32_t q = 0; q < L->parts; ++q)
+        if (!w_shards[q])
+            return zs::fail(ZERO_ERR_INVALID_ARG, "W shard of rank %d is NULL", q);
+    if (d.in % 8)
+        return zs::fail(ZERO_ERR_UNSUPPORTED, "in_features must be a multiple of 8");
+    if ((st = zero_gather_params(L, unit, unit + 1, w_shards, L->parts, w_full, stream)) != ZERO_OK)
+        return st;
+    if ((st = zero_transpose_bf16(d.in, d.out, w_full, d.out, w_t, d.in, stream)) != ZERO_OK)
+        return st;
+    return zero_gemm_bf16_nt(batch, d.out, d.in, x, d.in, w_t, d.in, y, d.out, y_dtype, stream);
+}
+
+zero_status zero_fsdp_linear_backward(const zero_layout *L, int32_t unit,
+                                      const uint16_t *const *w_shards, int64_t batch,
+                                      const uint16_t *x, const uint16_t *dy, uint16_t *w_full,
+                                      uint16_t *x_t, uint16_t *dy_t, void *dx, int32_t dx_dtype,
+                                      float *dw_full, void *stream)
+{
+    Dims d;
+    zero_status st = layer_dims(L, unit, &d);
+    if (st != ZERO_OK)
+        return st;
+    if (!w_shards || !x || !dy || !w_full || !x_t || !dy_t || !dx || !dw_full || batch < 0)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "every buffer and batch >= 0 are required");
+    for (int32_t q = 0; q < L->parts; ++q)
+        if (!w_shards[q])
+            return zs::fail(ZERO_ERR_INVALID_ARG, "W shard of rank %d is NULL", q);
+    if (d.out % 8 || batch % 8)
+        return zs::fail(ZERO_ERR_UNSUPPORTED, "out_features and batch must be multiples of 8");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // re-gather W (FSDP frees it after forward)
+    if ((st = zero_gather_params(L, unit, unit + 1, w_shards, L->parts, w_full, stream)) != ZERO_OK)
+        return st;
+    // dX = dY W^T: (batch x out) times (in x out)^T
+    if ((st = zero_gemm_bf16_nt(batch, d.in, d.out, dy, d.out, w_full, d.out, dx, d.in, dx_dtype,
+                                stream)) != ZERO_OK)
+        return st;
+    // dW = X^T dY: (in x batch) times (out x batch)^T, fp32, full shape
+    if ((st = zero_transpose_bf16(batch, d.in, x, d.in, x_t, batch, stream)) != ZERO_OK ||
+        (st = zero_transpose_bf16(batch, d.out, dy, d.out, dy_t, batch, stream)) != ZERO_OK ||
+        (st = zero_gemm_bf16_nt(d.in, d.out, batch, x_t, batch, dy_t, batch, dw_full, d.out,
+                                ZERO_FP32, stream)) != ZERO_OK)
+        return st;
+    // padding rows of the row-sharded layout hold zero gradient
+    return zs::zero_rows_fill(dw_full, d.out, d.in, d.in_pad, d.out, s);
+}
+
+}  // extern "C"

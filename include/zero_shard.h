@@ -309,6 +309,59 @@ zero_status zero_fsdp_sweep(const zero_layout *layout, int32_t unit_begin,
 zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro_bf16,
                                  int64_t n, void *stream);
 
+/* ----------------------------------------------- FSDP linear layer -- */
+
+/* C[M x N] = A[M x K] * B[N x K]^T on the MFMA units: A and B bf16
+   row-major with leading dimensions lda, ldb (both operands contiguous
+   along K), fp32 accumulation, C row-major with leading dimension ldc, fp32
+   (c_dtype ZERO_FP32) or bf16 rounded to nearest even (ZERO_BF16).  Needs K,
+   lda, ldb multiples of 8, lda, ldb >= K, ldc >= N, and 16-byte aligned A
+   and B.  Accumulation order is the kernel's own (error within the usual
+   gamma_K bound of fp32 dot products). */
+zero_status zero_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                              int64_t lda, const uint16_t *B, int64_t ldb,
+                              void *C, int64_t ldc, int32_t c_dtype,
+                              void *stream);
+
+/* dst[c * ldd + r] = src[r * lds + c] for r < rows, c < cols (bf16 bits). */
+zero_status zero_transpose_bf16(int64_t rows, int64_t cols, const uint16_t *src,
+                                int64_t lds, uint16_t *dst, int64_t ldd,
+                                void *stream);
+
+/* A hand-written FSDP linear layer ("DP, ZeRO-1/2/3, FSDP" notes, follow-up
+   on writing one FSDP linear layer: each rank stores 1/N of the rows of W;
+   forward all-gathers W and computes X W; backward all-gathers W again,
+   computes dX and the full-shape dW locally, and reduce-scatters dW into
+   each rank's rows).  W is unit `unit` of a row layout
+   (zero_shard_init_rows): rows = in_features (in), cols = out_features
+   (out), so rank r's W shard is its c_u x out rows.
+   forward:  w_full = all-gather(w_shards) (device, L_u bf16 workspace);
+             w_t = W^T (device, out x in bf16 workspace);
+             y = x W (x: batch x in bf16; y: batch x out, y_dtype).
+   backward: w_full = all-gather(w_shards) again; dx = dy W^T (dy: batch x
+             out bf16; dx: batch x in, dx_dtype); x_t, dy_t (in x batch and
+             out x batch bf16 workspaces) = transposes; dw_full = x^T dy
+             (fp32, the padded unit: in rows then zeroed padding rows, L_u
+             elements).  The reduce-scatter of the N ranks' dw_full is
+             zero_reduce_shard (fp32 grads, ZERO_INDEX_FULL) on this unit,
+             and zero_adam_step(grad_fp32 = its output) steps the shard.
+   `w_shards` is a host array of world_n device pointers (s_u bf16 each, this
+   rank's own included).  in must be a multiple of 8 (forward), out and
+   batch multiples of 8 (backward). */
+zero_status zero_fsdp_linear_forward(const zero_layout *layout, int32_t unit,
+                                     const uint16_t *const *w_shards,
+                                     int64_t batch, const uint16_t *x,
+                                     uint16_t *w_full, uint16_t *w_t, void *y,
+                                     int32_t y_dtype, void *stream);
+
+zero_status zero_fsdp_linear_backward(const zero_layout *layout, int32_t unit,
+                                      const uint16_t *const *w_shards,
+                                      int64_t batch, const uint16_t *x,
+                                      const uint16_t *dy, uint16_t *w_full,
+                                      uint16_t *x_t, uint16_t *dy_t, void *dx,
+                                      int32_t dx_dtype, float *dw_full,
+                                      void *stream);
+
 /* ---------------------------------------------------------- errors -- */
 
 const char *zero_status_str(zero_status status);

@@ -31,7 +31,7 @@ FAKE = 0x7f0000000000          # 16-byte aligned fake device address, never dere
 def header_functions():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(zero_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(zero_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_exports_every_declared_function():
