@@ -5,9 +5,9 @@
 // (12 bytes), and writes master, m, v (12) and the bf16 parameter (2), for
 // about N + 20 flops -- far below the machine balance, so there is no
 // contraction and no MFMA.  The design rules that matter are the memory ones:
-//   * 256-thread blocks over 2048-element tiles; each lane owns two groups
-//     of 4 consecutive elements so that every load / store instruction of a
-//     wave covers one contiguous run (fp32 streams in 128-bit accesses, bf16
+//   * 2048-element tiles; in the step kernel each lane owns one group of 4
+//     consecutive elements so that every load / store instruction of a wave
+//     covers one contiguous run (fp32 streams in 128-bit accesses, bf16
 //     streams in 64-bit ones) and whole lines are written by one
 //     instruction -- rocprof FETCH_SIZE / WRITE_SIZE equal the algorithmic
 //     bytes;
@@ -42,8 +42,10 @@ constexpr int kThreads = 256;
 constexpr int kVec = 8;                     // elements per thread per tile
 constexpr int kTile = kThreads * kVec;      // elements per tile
 constexpr int kMaxSegs = 32;                // units per launch (kernarg table)
-constexpr int kWaves = kThreads / 64;       // waves per block
-constexpr int kWaveElems = kTile / kWaves;  // elements of a tile per wave
+constexpr int kWaves = kThreads / 64;       // waves per 256-thread block
+constexpr int kWaveElems = kTile / kWaves;  // elements of a tile per wave (256-thread blocks)
+constexpr int kStepThreads = 512;           // step kernel: one 4-element group per lane
+constexpr int kStepWaveElems = kTile / (kStepThreads / 64);  // 256
 constexpr int kClipThreads = 1024;          // one block sums the clip partials
 constexpr int kMaxRanks = ZERO_MAX_RANKS_PER_CALL;
 
@@ -282,14 +284,16 @@ __device__ double block_sum(double x)
 
 // -------------------------------------------------------- step kernel --
 //
-// Element ownership in a 2048-element tile: wave w covers [512w, 512w + 512)
-// and lane l owns the two 4-element groups at 512w + 4l and 512w + 256 + 4l.
-// Every load or store instruction of a wave therefore covers one contiguous
-// run -- 512 bytes of a bf16 stream, 1 KiB of an fp32 stream -- so caches
-// and HBM see whole lines written by a single instruction.  (With 8
-// contiguous elements per lane, each 16-byte fp32 store instruction fills
-// only every other 16 bytes of its span and lines are written back in
-// halves.)
+// Element ownership in a 2048-element tile: the step kernel runs 512-thread
+// blocks; wave w covers [256w, 256w + 256) and lane l owns the 4-element
+// group at 256w + 4l.  Every load or store instruction of a wave therefore
+// covers one contiguous run -- 512 bytes of a bf16 stream, 1 KiB of an fp32
+// stream -- so caches and HBM see whole lines written by one instruction.
+// (With 8 contiguous elements per lane, each 16-byte fp32 store instruction
+// filled only every other 16 bytes of its span and lines were written back
+// in halves.)  One group per lane keeps the kernel at 55 VGPRs, 8 waves per
+// SIMD; paired runs on the 7B / N = 8 step measured 2-3 % over 256-thread
+// blocks with two groups per lane (91 VGPRs, 5 waves).
 
 // The fused / reduce / apply work for G full groups of 4 elements.
 template <int MODE, int NR, bool BF16, int G>
@@ -392,7 +396,7 @@ __device__ __forceinline__ void step_scalar(const StepArgs &a, const Seg &sg, in
 }
 
 template <int MODE, int NR, bool BF16>
-__global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a)
+__global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs a)
 {
     const float coef = (MODE == kApply && a.clip) ? *a.clip : 1.0f;
     const int lane = threadIdx.x & 63;
@@ -400,27 +404,19 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a)
     const TileWalk tw = tile_walk(a.n_tiles);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         const Seg &sg = a.seg[find_seg(a.seg, a.n_segs, t)];
-        const int64_t j0 = (t - sg.tile0) * kTile + wave * kWaveElems + lane * 4;
-        const int64_t j[2] = {j0, j0 + kWaveElems / 2};
+        const int64_t j[1] = {(t - sg.tile0) * kTile + wave * kStepWaveElems + lane * 4};
         const bool vec = sg.vec && a.vec_ptrs;
         double sq = 0.0;  // kReduce: this thread's sum of squares in this tile
-        if (vec && j[1] + 4 <= sg.len) {
-            step_groups<MODE, NR, BF16, 2>(a, sg, j, coef, sq);
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                if (j[h] >= sg.len)
-                    continue;
-                if (vec && j[h] + 4 <= sg.len)
-                    step_groups<MODE, NR, BF16, 1>(a, sg, &j[h], coef, sq);
-                else
-                    step_scalar<MODE, NR, BF16>(a, sg, j[h],
-                                                sg.len - j[h] < 4 ? sg.len - j[h] : 4, coef, sq);
-            }
+        if (j[0] < sg.len) {
+            if (vec && j[0] + 4 <= sg.len)
+                step_groups<MODE, NR, BF16, 1>(a, sg, j, coef, sq);
+            else
+                step_scalar<MODE, NR, BF16>(a, sg, j[0], sg.len - j[0] < 4 ? sg.len - j[0] : 4,
+                                            coef, sq);
         }
         if (MODE == kReduce && a.partials) {
             // every thread takes part; threads past the slice end add 0
-            const double b = block_sum<kThreads>(sq);
+            const double b = block_sum<kStepThreads>(sq);
             if (threadIdx.x == 0)
                 a.partials[t] = b;
         }
@@ -575,10 +571,10 @@ int blocks_per_cu_override()
 }
 
 template <typename Kernel>
-int resident_blocks(Kernel kernel)
+int resident_blocks(Kernel kernel, int threads = kThreads)
 {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess ||
         nb < 1)
         nb = 4;
     return nb;
@@ -703,10 +699,10 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
 template <int MODE, int NR, bool BF16>
 void launch_one(const StepArgs &a, int64_t grid, hipStream_t st)
 {
-    static const int resident = resident_blocks(step_kernel<MODE, NR, BF16>);
+    static const int resident = resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads);
     const int64_t blocks = grid > 0 ? grid : stream_grid(a.n_tiles, resident);
-    hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       st, a);
+    hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kStepThreads),
+                       0, st, a);
 }
 
 template <int MODE, bool BF16>
