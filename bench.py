@@ -481,10 +481,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 def run_fsdp_linear(args, torch, zs, np):
     """One rank's FSDP linear-layer training step, N = 8 simulated ranks:
-    forward (all-gather W, transpose, Y = X W), backward for this rank
-    (re-gather, dX = dY W^T, transposes, dW = X^T dY) and the other 7 ranks'
-    local dW (simulated), the reduce-scatter of the 8 dW into this rank's
-    rows, and Adam on the W shard."""
+    forward (all-gather W, Y = X W), backward for this rank (re-gather,
+    dX = dY W^T, dW = X^T dY) and the other 7 ranks' local dW (simulated),
+    the reduce-scatter of the 8 dW into this rank's rows, and Adam on the W
+    shard.  The GEMMs read X, W and dY in place."""
     from synthetic import small_workload, grad_bits
     dev = torch.device("cuda:0")
     N, r, inf, outf, batch = 8, 7, 4096, 14336, 4096
@@ -496,9 +496,6 @@ def run_fsdp_linear(args, torch, zs, np):
     dys = [(torch.randn(batch, outf, device=dev) * 1e-2).to(torch.bfloat16).view(torch.int16)
            for _ in range(N)]
     w_full = torch.empty(Lu, dtype=torch.int16, device=dev)
-    w_t = torch.empty(outf * inf, dtype=torch.int16, device=dev)
-    x_t = torch.empty(inf * batch, dtype=torch.int16, device=dev)
-    dy_t = torch.empty(outf * batch, dtype=torch.int16, device=dev)
     y = torch.empty((batch, outf), dtype=torch.int16, device=dev)
     dx = torch.empty((batch, inf), dtype=torch.int16, device=dev)
     dws = [torch.empty(Lu, device=dev) for _ in range(N)]
@@ -508,23 +505,23 @@ def run_fsdp_linear(args, torch, zs, np):
     v = torch.zeros(S, device=dev)
     own = torch.empty(S, dtype=torch.int16, device=dev)
     G = zs.Grads(dws, zs.FP32, zs.INDEX_FULL)
+    KI, KO = zs.K_INNER, zs.K_OUTER
     t = [0]
 
     def step(ph):
         t[0] += 1
         phase(ph, "gather_w", lambda: zs.gather_params(L, 0, 1, shards, w_full))
-        phase(ph, "transpose_w", lambda: zs.transpose_bf16(inf, outf, w_full, outf, w_t, inf))
-        phase(ph, "gemm_forward", lambda: zs.gemm_bf16_nt(batch, outf, inf, xs[r], inf, w_t, inf,
-                                                          y, outf, zs.BF16))
+        # Y = X W (W read in place as a K-outer operand)
+        phase(ph, "gemm_forward", lambda: zs.gemm_bf16(batch, outf, inf, xs[r], inf, KI, w_full,
+                                                       outf, KO, y, outf, zs.BF16))
         phase(ph, "gather_w", lambda: zs.gather_params(L, 0, 1, shards, w_full))
-        phase(ph, "gemm_dx", lambda: zs.gemm_bf16_nt(batch, inf, outf, dys[r], outf, w_full, outf,
-                                                     dx, inf, zs.BF16))
+        # dX = dY W^T
+        phase(ph, "gemm_dx", lambda: zs.gemm_bf16(batch, inf, outf, dys[r], outf, KI, w_full, outf,
+                                                  KI, dx, inf, zs.BF16))
+        # every rank's dW = X^T dY (fp32), both operands K-outer
         for q in range(N):
-            phase(ph, "transpose_x_dy", lambda q=q: (
-                zs.transpose_bf16(batch, inf, xs[q], inf, x_t, batch),
-                zs.transpose_bf16(batch, outf, dys[q], outf, dy_t, batch)))
-            phase(ph, "gemm_dw", lambda q=q: zs.gemm_bf16_nt(inf, outf, batch, x_t, batch, dy_t,
-                                                             batch, dws[q], outf, zs.FP32))
+            phase(ph, "gemm_dw", lambda q=q: zs.gemm_bf16(inf, outf, batch, xs[q], inf, KO, dys[q],
+                                                          outf, KO, dws[q], outf, zs.FP32))
         phase(ph, "reduce_scatter_dw", lambda: zs.reduce_shard(L, 0, 1, G, gshard))
         phase(ph, "adam_shard", lambda: zs.adam_step(L, 0, 1, zs.adam_cfg(step=t[0]), master, m, v,
                                                      own, zs.INDEX_SHARD, grad_fp32=gshard))
@@ -548,7 +545,7 @@ def run_fsdp_linear(args, torch, zs, np):
     out["kernels"] = kern
     gemm_ms = sum(kern[k]["ms_per_step"] for k in ("gemm_forward", "gemm_dx", "gemm_dw"))
     out["gemm_tflops"] = flops * (N + 2) / (gemm_ms * 1e-3) / 1e12
-    out["roofline"] = {"bound": "mfma", "kernel": "gemm_nt_kernel (bf16, fp32 accumulate), "
+    out["roofline"] = {"bound": "mfma", "kernel": "gemm_kernel (bf16, fp32 accumulate), "
                                                    "all 10 launches of the step",
                        "achieved": out["gemm_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": out["gemm_tflops"] / MFMA_BF16_PEAK_TFLOPS,

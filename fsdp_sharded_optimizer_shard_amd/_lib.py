@@ -31,6 +31,7 @@ OK, ERR_INVALID_ARG, ERR_ALIGNMENT, ERR_OOM, ERR_HIP, ERR_UNSUPPORTED = range(6)
 DDP, STAGE1, STAGE2, STAGE3, FSDP, MEGATRON_DO = range(6)
 BF16, FP32 = 0, 1
 INDEX_FULL, INDEX_SHARD = 0, 1
+K_INNER, K_OUTER = 0, 1
 MAX_RANKS_PER_CALL = 64
 
 STRATEGY = {"ddp": DDP, "zero1": STAGE1, "zero1_allreduce": STAGE1, "zero2": STAGE2,
@@ -90,15 +91,18 @@ class _UnitIO(ctypes.Structure):
 _lib.zero_fsdp_sweep.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _I32,
                                  ctypes.POINTER(_UnitIO), _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_sweep.restype = _I32
+_lib.zero_gemm_bf16.argtypes = [_I64, _I64, _I64, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I32,
+                                _P]
+_lib.zero_gemm_bf16.restype = _I32
 _lib.zero_gemm_bf16_nt.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I32, _P]
 _lib.zero_gemm_bf16_nt.restype = _I32
 _lib.zero_transpose_bf16.argtypes = [_I64, _I64, _P, _I64, _P, _I64, _P]
 _lib.zero_transpose_bf16.restype = _I32
 _lib.zero_fsdp_linear_forward.argtypes = [_P, _I32, ctypes.POINTER(ctypes.c_void_p), _I64, _P, _P,
-                                          _P, _P, _I32, _P]
+                                          _P, _I32, _P]
 _lib.zero_fsdp_linear_forward.restype = _I32
 _lib.zero_fsdp_linear_backward.argtypes = [_P, _I32, ctypes.POINTER(ctypes.c_void_p), _I64, _P,
-                                           _P, _P, _P, _P, _P, _I32, _P, _P]
+                                           _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_linear_backward.restype = _I32
 _lib.zero_grad_accumulate.argtypes = [_P, _P, _I64, _P]
 _lib.zero_grad_accumulate.restype = _I32
@@ -109,7 +113,7 @@ _lib.zero_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy", "zero_layout_info", "zero_layout_query",
            "zero_reduce_shard", "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
-           "zero_gather_params", "zero_grad_accumulate", "zero_fsdp_sweep", "zero_gemm_bf16_nt",
+           "zero_gather_params", "zero_grad_accumulate", "zero_fsdp_sweep", "zero_gemm_bf16", "zero_gemm_bf16_nt",
            "zero_transpose_bf16", "zero_fsdp_linear_forward", "zero_fsdp_linear_backward",
            "zero_status_str", "zero_last_error")
 
@@ -290,6 +294,12 @@ def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, gra
            "zero_fsdp_sweep")
 
 
+def gemm_bf16(M: int, N: int, K: int, A, lda: int, a_order: int, B, ldb: int, b_order: int, C,
+              ldc: int, c_dtype: int = FP32, stream=None) -> None:
+    _check(_lib.zero_gemm_bf16(M, N, K, _addr(A), lda, a_order, _addr(B), ldb, b_order, _addr(C),
+                               ldc, c_dtype, _stream(stream)), "zero_gemm_bf16")
+
+
 def gemm_bf16_nt(M: int, N: int, K: int, A, lda: int, B, ldb: int, C, ldc: int,
                  c_dtype: int = FP32, stream=None) -> None:
     _check(_lib.zero_gemm_bf16_nt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, c_dtype,
@@ -305,18 +315,18 @@ def _ptrs(bufs):
     return (ctypes.c_void_p * max(1, len(bufs)))(*[_addr(b) for b in bufs])
 
 
-def fsdp_linear_forward(layout: Layout, unit: int, w_shards, batch: int, x, w_full, w_t, y,
+def fsdp_linear_forward(layout: Layout, unit: int, w_shards, batch: int, x, w_full, y,
                         y_dtype: int = BF16, stream=None) -> None:
     _check(_lib.zero_fsdp_linear_forward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
-                                         _addr(w_full), _addr(w_t), _addr(y), y_dtype,
-                                         _stream(stream)), "zero_fsdp_linear_forward")
+                                         _addr(w_full), _addr(y), y_dtype, _stream(stream)),
+           "zero_fsdp_linear_forward")
 
 
-def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy, w_full, x_t,
-                         dy_t, dx, dw_full, dx_dtype: int = BF16, stream=None) -> None:
+def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy, w_full, dx,
+                         dw_full, dx_dtype: int = BF16, stream=None) -> None:
     _check(_lib.zero_fsdp_linear_backward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
-                                          _addr(dy), _addr(w_full), _addr(x_t), _addr(dy_t),
-                                          _addr(dx), dx_dtype, _addr(dw_full), _stream(stream)),
+                                          _addr(dy), _addr(w_full), _addr(dx), dx_dtype,
+                                          _addr(dw_full), _stream(stream)),
            "zero_fsdp_linear_backward")
 
 

@@ -2,18 +2,39 @@
 // a hand-written FSDP linear layer ("DP, ZeRO-1/2/3, FSDP" notes, follow-up
 // on writing one FSDP linear layer by hand).
 //
-//   zero_gemm_bf16_nt:  C[M x N] = A[M x K] * B[N x K]^T, A and B bf16
-//                       row-major (K contiguous in both -- the operand layout
-//                       the MFMA fragments want), fp32 accumulation, C fp32
-//                       or bf16 (round to nearest even).
+//   zero_gemm_bf16:     C[i][j] = sum_k a(i, k) b(j, k), fp32 accumulation, C
+//                       fp32 or bf16 (round to nearest even).  Each operand is
+//                       stored either K-inner (A as M x K, B as N x K) or
+//                       K-outer (A as K x M, B as K x N), so X W, dY W^T and
+//                       X^T dY all run without a separate transpose.
+//   zero_gemm_bf16_nt:  the K-inner / K-inner case.
 //   zero_transpose_bf16: dst[c][r] = src[r][c].
 //
-// GEMM tiling: 256-thread blocks (4 waves) own a 128 x 128 tile of C; each
-// wave owns 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_bf16.  K advances
-// 32 at a time through double-buffered LDS tiles (rows padded to 40 bf16),
-// loaded with 128-bit global loads; the next K-tile is fetched into
-// registers while the current one feeds the MFMAs, and one barrier per K
-// step separates the two LDS buffers.
+// GEMM tiling.  A 256-thread block (4 waves, one per SIMD) owns a 256 x 256
+// tile of C; each wave owns 128 x 128 as 4 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16, so its 256 fp32 accumulators per lane live in
+// the accumulation registers.  K advances 64 at a time through two LDS
+// buffers of 256 x 64 bf16 per operand (128 KB).  LDS rows are 128 bytes
+// with the 16-byte chunk c of row r stored at position c ^ s(r),
+// s(r) = (r ^ (r >> 3)) & 7, which keeps both the staging writes and the
+// fragment reads free of bank conflicts.
+//
+// Staging.  A K-inner operand is read as 16-byte chunks along K (thread t:
+// rows t/8 + 32 i, chunk t % 8).  A K-outer operand is read as one 8 x 8
+// block per thread (k-block t / 32, row-block t % 32) that is transposed in
+// registers with v_perm_b32 before it is written to LDS, so the fragment
+// reads are the same for both orders.
+//
+// Pipeline per K tile of 64 (four MFMA substeps of k = 16): the global loads
+// of the next tile are issued during the first substep; the fragment reads
+// of substep s + 1 are issued during the MFMAs of substep s; the next tile is
+// written to the other LDS buffer during the first half of the last substep,
+// then one barrier, then the next tile's first fragments are read during the
+// second half.  sched_group_barrier fixes that interleave.
+//
+// Tile order.  Block b runs on XCD b % 8; each XCD gets a contiguous range of
+// tiles, walked 8 tile rows at a time, so the blocks that share an L2 share
+// A rows and B columns.
 //
 // MFMA 32x32x16 bf16 lane layout (checked on the device against an exact
 // CPU product): lane l holds A row (l % 32), k = 8 (l / 32) .. +7, and B
@@ -21,6 +42,7 @@
 // 8 (v / 4) + 4 (l / 32) + (v % 4), column l % 32.
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdint>
 
 #include "internal.h"
@@ -28,9 +50,9 @@
 namespace zs {
 namespace {
 
-constexpr int kGT = 256;          // threads per GEMM block
-constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kLdsRow = kBK + 8;  // padded LDS row (bf16 elements), 80 bytes
+constexpr int kGT = 256;  // threads per GEMM block
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kGroupM = 8;  // tile rows walked together
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -44,107 +66,255 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// One 128 x 32 bf16 tile of a K-contiguous matrix: 512 chunks of 8
-// elements, two per thread; rows past `rows` and k past K read as zero.
-struct TileRegs {
-    u32x4 v[2];
-};
+// LDS position (in elements) of the 16-byte chunk `c` of tile row `r`.
+__device__ __forceinline__ int lds_pos(int r, int c)
+{
+    return r * kBK + ((c ^ ((r ^ (r >> 3)) & 7)) * 8);
+}
 
-__device__ __forceinline__ void load_tile(TileRegs &r, const uint16_t *base, int64_t ld,
-                                          int64_t row0, int64_t rows, int64_t k0, int64_t K)
+// Per-thread source pointers of one operand's 256 x 64 tile (at k = 0).
+// K-inner: chunk i is row (row0 + t/8 + 32 i) clamped to the last row, k
+// chunk t % 8.  K-outer: row i of the 8 x 8 block is k = 8 (t / 32) + i, rows
+// row0 + 8 (t % 32) .. +7 (clamped to the last 8; rows % 8 == 0).  Clamped
+// rows only feed C rows or columns that are never stored.
+template <bool KOUTER>
+__device__ __forceinline__ void tile_sources(const uint16_t *(&src)[8], const uint16_t *base,
+                                             int64_t ld, int64_t row0, int64_t rows, int t)
+{
+    if (!KOUTER) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int64_t row = row0 + (t >> 3) + 32 * i;
+            row = row < rows ? row : rows - 1;
+            src[i] = base + row * ld + (t & 7) * 8;
+        }
+    } else {
+        int64_t c = row0 + (t & 31) * 8;
+        c = c < rows ? c : rows - 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            src[i] = base + (int64_t)((t >> 5) * 8 + i) * ld + c;
+    }
+}
+
+template <bool KOUTER>
+__device__ __forceinline__ void tile_dests(int (&dst)[8], int t)
 {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = threadIdx.x + h * kGT;
-        const int64_t row = row0 + (c >> 2);
-        const int64_t k = k0 + (c & 3) * 8;
-        if (row < rows && k < K)
-            r.v[h] = *reinterpret_cast<const u32x4 *>(base + row * ld + k);
+    for (int i = 0; i < 8; ++i)
+        dst[i] = KOUTER ? lds_pos((t & 31) * 8 + i, t >> 5) : lds_pos((t >> 3) + 32 * i, t & 7);
+}
+
+// k offset, within the tile, of the data thread t stages.
+template <bool KOUTER>
+__device__ __forceinline__ int tile_kofs(int t)
+{
+    return KOUTER ? (t >> 5) * 8 : (t & 7) * 8;
+}
+
+// Global -> registers for the tile at k0.  MASKED: the tile runs past K; the
+// thread's 8 k values are all in range or all out (K % 8 == 0) and out of
+// range ones read as zero.
+template <bool KOUTER, bool MASKED>
+__device__ __forceinline__ void tile_load(u32x4 (&v)[8], const uint16_t *const (&src)[8],
+                                          int64_t ld, int64_t k0, int64_t K, int kofs)
+{
+    const int64_t adv = KOUTER ? k0 * ld : k0;
+    const bool ok = !MASKED || k0 + kofs < K;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (MASKED)
+            v[i] = ok ? *reinterpret_cast<const u32x4 *>(src[i] + adv) : u32x4{0u, 0u, 0u, 0u};
         else
-            r.v[h] = u32x4{0u, 0u, 0u, 0u};
+            v[i] = *reinterpret_cast<const u32x4 *>(src[i] + adv);
     }
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs &r, uint16_t *lds)
+// Registers -> LDS.  K-outer: v[i] holds rows 0..7 at k = i; row j's eight
+// k values are gathered with v_perm_b32 (low or high halves of a pair).
+template <bool KOUTER>
+__device__ __forceinline__ void tile_store(const u32x4 (&v)[8], uint16_t *lds, const int (&dst)[8])
 {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = threadIdx.x + h * kGT;
-        *reinterpret_cast<u32x4 *>(lds + (c >> 2) * kLdsRow + (c & 3) * 8) = r.v[h];
+    for (int j = 0; j < 8; ++j) {
+        u32x4 w;
+        if (!KOUTER) {
+            w = v[j];
+        } else {
+            const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[q] = __builtin_amdgcn_perm(v[2 * q + 1][j >> 1], v[2 * q][j >> 1], sel);
+        }
+        *reinterpret_cast<u32x4 *>(lds + dst[j]) = w;
     }
 }
 
-template <bool OUT_BF16>
-__global__ __launch_bounds__(kGT) void gemm_nt_kernel(int64_t M, int64_t N, int64_t K,
-                                                      const uint16_t *__restrict__ A, int64_t lda,
-                                                      const uint16_t *__restrict__ B, int64_t ldb,
-                                                      void *__restrict__ C, int64_t ldc)
+template <bool A_KOUTER, bool B_KOUTER, bool OUT_BF16>
+__global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t K,
+                                                   const uint16_t *__restrict__ A, int64_t lda,
+                                                   const uint16_t *__restrict__ B, int64_t ldb,
+                                                   void *__restrict__ C, int64_t ldc, int tiles_m,
+                                                   int tiles_n)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kLdsRow];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kLdsRow];
+    constexpr int TM = 4, TN = 4;      // 32 x 32 MFMA tiles per wave
+    constexpr int NF = TM + TN;        // fragment reads per substep
+    constexpr int NMF = TM * TN;       // MFMAs per substep
+    constexpr int NG = 16;             // global loads (and LDS writes) per K tile
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
 
-    const int64_t m0 = (int64_t)blockIdx.y * kBM;
-    const int64_t n0 = (int64_t)blockIdx.x * kBN;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-    const int fr = lane & 31;          // fragment row / column
-    const int fk = (lane >> 5) * 8;    // fragment k offset
+    // XCD-contiguous, grouped tile order.
+    const int T = tiles_m * tiles_n;
+    const int b = blockIdx.x;
+    const int per = T / 8, rem = T % 8, x = b % 8;
+    const int logical = x * per + (x < rem ? x : rem) + b / 8;
+    const int gsz = kGroupM * tiles_n;
+    const int g = logical / gsz;
+    const int first_m = g * kGroupM;
+    const int gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+    const int in_g = logical - g * gsz;
+    const int64_t m0 = (int64_t)(first_m + in_g % gm) * kBM;
+    const int64_t n0 = (int64_t)(in_g / gm) * kBN;
 
-    f32x16 acc[2][2];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 1) * (kBM / 2), wn = (wave & 1) * (kBN / 2);
+    const int fr = lane & 31, fh = lane >> 5;
+
+    const uint16_t *sa[8], *sb[8];
+    tile_sources<A_KOUTER>(sa, A, lda, m0, M, t);
+    tile_sources<B_KOUTER>(sb, B, ldb, n0, N, t);
+    int da[8], db[8];
+    tile_dests<A_KOUTER>(da, t);
+    tile_dests<B_KOUTER>(db, t);
+    const int ka = tile_kofs<A_KOUTER>(t), kb = tile_kofs<B_KOUTER>(t);
+
+    // Fragment read positions for the four substeps.
+    int fa_pos[TM][4], fb_pos[TN][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int s = 0; s < 4; ++s) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < TM; ++i)
+            fa_pos[i][s] = lds_pos(wm + 32 * i + fr, 2 * s + fh);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb_pos[j][s] = lds_pos(wn + 32 * j + fr, 2 * s + fh);
+    }
+
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[i][j][v] = 0.0f;
 
-    const int64_t kt_n = (K + kBK - 1) / kBK;
-    TileRegs ra, rb;
-    load_tile(ra, A, lda, m0, M, 0, K);
-    load_tile(rb, B, ldb, n0, N, 0, K);
-    store_tile(ra, As[0]);
-    store_tile(rb, Bs[0]);
-    __syncthreads();
+    u32x4 ra[8], rb[8];
+    bf16x8 fa0[TM], fb0[TN], fa1[TM], fb1[TN];
 
-    for (int64_t kt = 0; kt < kt_n; ++kt) {
+    auto frags = [&](int buf, int s, bf16x8 (&fa)[TM], bf16x8 (&fb)[TN]) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][fa_pos[i][s]]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][fb_pos[j][s]]);
+    };
+    auto mma = [&](const bf16x8 (&fa)[TM], const bf16x8 (&fb)[TN], int lo, int hi) {
+#pragma unroll
+        for (int q = 0; q < NMF; ++q)
+            if (q >= lo && q < hi)
+                acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    fa[q / TN], fb[q % TN], acc[q / TN][q % TN], 0, 0, 0);
+    };
+    auto load = [&](int64_t k0, bool masked) {
+        if (masked) {
+            tile_load<A_KOUTER, true>(ra, sa, lda, k0, K, ka);
+            tile_load<B_KOUTER, true>(rb, sb, ldb, k0, K, kb);
+        } else {
+            tile_load<A_KOUTER, false>(ra, sa, lda, k0, K, ka);
+            tile_load<B_KOUTER, false>(rb, sb, ldb, k0, K, kb);
+        }
+    };
+    auto store = [&](int buf) {
+        tile_store<A_KOUTER>(ra, As[buf], da);
+        tile_store<B_KOUTER>(rb, Bs[buf], db);
+    };
+    // Interleave: per fragment read, NMF / NF MFMAs (and optionally NG / NF
+    // global loads).
+    auto interleave_reads = [&](bool with_loads) {
+#pragma unroll
+        for (int q = 0; q < NF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMF / NF, 0);  // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);         // LDS read
+            if (with_loads)
+                __builtin_amdgcn_sched_group_barrier(0x020, NG / NF, 0);  // global read
+        }
+    };
+
+    // One K tile.  next: 0 none, 1 full tile, 2 tile running past K.
+    auto tile = [&](int64_t kt, int next) {
         const int cur = (int)(kt & 1);
-        if (kt + 1 < kt_n) {
-            load_tile(ra, A, lda, m0, M, (kt + 1) * kBK, K);
-            load_tile(rb, B, ldb, n0, N, (kt + 1) * kBK, K);
-        }
+        if (next)
+            load((kt + 1) * kBK, next == 2);
+        frags(cur, 1, fa1, fb1);
+        mma(fa0, fb0, 0, NMF);
+        interleave_reads(next != 0);
+        frags(cur, 2, fa0, fb0);
+        mma(fa1, fb1, 0, NMF);
+        interleave_reads(false);
+        frags(cur, 3, fa1, fb1);
+        mma(fa0, fb0, 0, NMF);
+        interleave_reads(false);
+        mma(fa1, fb1, 0, NMF / 2);
+        if (next) {
+            store(cur ^ 1);
 #pragma unroll
-        for (int ks = 0; ks < kBK; ks += 16) {
-            bf16x8 fa[2], fb[2];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                fa[t] = *reinterpret_cast<const bf16x8 *>(
-                    &As[cur][(wm + 32 * t + fr) * kLdsRow + ks + fk]);
-                fb[t] = *reinterpret_cast<const bf16x8 *>(
-                    &Bs[cur][(wn + 32 * t + fr) * kLdsRow + ks + fk]);
+            for (int q = 0; q < NMF / 2; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x200, NG / (NMF / 2), 0);  // LDS write
             }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
-                                                                         0, 0, 0);
-        }
-        if (kt + 1 < kt_n) {
-            store_tile(ra, As[cur ^ 1]);
-            store_tile(rb, Bs[cur ^ 1]);
         }
         __syncthreads();
+        if (next) {
+            frags(cur ^ 1, 0, fa0, fb0);
+            mma(fa1, fb1, NMF / 2, NMF);
+#pragma unroll
+            for (int q = 0; q < NF; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+        } else {
+            mma(fa1, fb1, NMF / 2, NMF);
+        }
+    };
+
+    const int64_t kt_n = (K + kBK - 1) / kBK;
+    const int64_t kt_full = K / kBK;
+    load(0, kt_full == 0);
+    store(0);
+    __syncthreads();
+    frags(0, 0, fa0, fb0);
+    // Tiles before `last_full_next` prefetch a full tile; then at most one
+    // prefetches the partial tail; the last prefetches nothing.
+    const int64_t last_full_next = kt_full < kt_n ? kt_full - 1 : kt_n - 1;
+    int64_t kt = 0;
+    for (; kt < last_full_next; ++kt)
+        tile(kt, 1);
+    if (kt < kt_n - 1) {
+        tile(kt, 2);
+        ++kt;
     }
+    tile(kt, 0);
 
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int64_t row = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * fh + (v & 3);
                 const int64_t col = n0 + wn + 32 * j + fr;
                 if (row < M && col < N) {
                     if (OUT_BF16)
@@ -220,38 +390,64 @@ zero_status zero_rows_fill(float *p, int64_t ld, int64_t r0, int64_t r1, int64_t
 
 extern "C" {
 
-zero_status zero_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
-                              const uint16_t *B, int64_t ldb, void *C, int64_t ldc,
-                              int32_t c_dtype, void *stream)
+zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                           int32_t a_order, const uint16_t *B, int64_t ldb, int32_t b_order,
+                           void *C, int64_t ldc, int32_t c_dtype, void *stream)
 {
     using zs::fail;
     if (M < 0 || N < 0 || K < 0)
         return fail(ZERO_ERR_INVALID_ARG, "negative GEMM size");
+    if ((a_order != ZERO_K_INNER && a_order != ZERO_K_OUTER) ||
+        (b_order != ZERO_K_INNER && b_order != ZERO_K_OUTER))
+        return fail(ZERO_ERR_INVALID_ARG, "unknown operand order (%d, %d)", a_order, b_order);
+    if (c_dtype != ZERO_BF16 && c_dtype != ZERO_FP32)
+        return fail(ZERO_ERR_INVALID_ARG, "unknown C dtype %d", c_dtype);
     if (M == 0 || N == 0)
         return ZERO_OK;
     if (!A || !B || !C)
         return fail(ZERO_ERR_INVALID_ARG, "A, B and C are required");
-    if (c_dtype != ZERO_BF16 && c_dtype != ZERO_FP32)
-        return fail(ZERO_ERR_INVALID_ARG, "unknown C dtype %d", c_dtype);
-    if (K % 8 || lda < K || ldb < K || ldc < N || lda % 8 || ldb % 8)
-        return fail(ZERO_ERR_UNSUPPORTED, "GEMM needs K, lda and ldb multiples of 8, "
-                    "lda, ldb >= K and ldc >= N");
+    const bool ao = a_order == ZERO_K_OUTER, bo = b_order == ZERO_K_OUTER;
+    if (K % 8 || lda % 8 || ldb % 8)
+        return fail(ZERO_ERR_UNSUPPORTED, "GEMM needs K, lda and ldb multiples of 8");
+    if ((ao && M % 8) || (bo && N % 8))
+        return fail(ZERO_ERR_UNSUPPORTED, "a K-outer operand needs its M or N a multiple of 8");
+    if (lda < (ao ? M : K) || ldb < (bo ? N : K) || ldc < N)
+        return fail(ZERO_ERR_INVALID_ARG, "leading dimension too small (lda %lld, ldb %lld, "
+                    "ldc %lld)", (long long)lda, (long long)ldb, (long long)ldc);
     if (!zs::a16(A) || !zs::a16(B))
         return fail(ZERO_ERR_ALIGNMENT, "A and B must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(C) % (c_dtype == ZERO_BF16 ? 2 : 4))
         return fail(ZERO_ERR_ALIGNMENT, "C is misaligned");
-    if ((M + zs::kBM - 1) / zs::kBM > 65535)
-        return fail(ZERO_ERR_UNSUPPORTED, "M too large for one launch");
-    const dim3 grid((unsigned)((N + zs::kBN - 1) / zs::kBN), (unsigned)((M + zs::kBM - 1) / zs::kBM));
+    const int64_t tm = (M + zs::kBM - 1) / zs::kBM, tn = (N + zs::kBN - 1) / zs::kBN;
+    if (tm > INT_MAX / tn)
+        return fail(ZERO_ERR_UNSUPPORTED, "too many GEMM tiles for one launch");
+    const dim3 grid((unsigned)(tm * tn)), block(zs::kGT);
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int code = (ao ? 1 : 0) | (bo ? 2 : 0) | (c_dtype == ZERO_BF16 ? 4 : 0);
     (void)hipGetLastError();
-    if (c_dtype == ZERO_BF16)
-        hipLaunchKernelGGL(zs::gemm_nt_kernel<true>, grid, dim3(zs::kGT), 0, s, M, N, K, A, lda, B,
-                           ldb, C, ldc);
-    else
-        hipLaunchKernelGGL(zs::gemm_nt_kernel<false>, grid, dim3(zs::kGT), 0, s, M, N, K, A, lda,
-                           B, ldb, C, ldc);
+#define ZS_GEMM(AO, BO, BF)                                                                      \
+    hipLaunchKernelGGL((zs::gemm_kernel<AO, BO, BF>), grid, block, 0, s, M, N, K, A, lda, B, ldb, \
+                       C, ldc, (int)tm, (int)tn)
+    switch (code) {
+    case 0: ZS_GEMM(false, false, false); break;
+    case 1: ZS_GEMM(true, false, false); break;
+    case 2: ZS_GEMM(false, true, false); break;
+    case 3: ZS_GEMM(true, true, false); break;
+    case 4: ZS_GEMM(false, false, true); break;
+    case 5: ZS_GEMM(true, false, true); break;
+    case 6: ZS_GEMM(false, true, true); break;
+    default: ZS_GEMM(true, true, true); break;
+    }
+#undef ZS_GEMM
     return zs::launched("gemm");
+}
+
+zero_status zero_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                              const uint16_t *B, int64_t ldb, void *C, int64_t ldc,
+                              int32_t c_dtype, void *stream)
+{
+    return zero_gemm_bf16(M, N, K, A, lda, ZERO_K_INNER, B, ldb, ZERO_K_INNER, C, ldc, c_dtype,
+                          stream);
 }
 
 zero_status zero_transpose_bf16(int64_t rows, int64_t cols, const uint16_t *src, int64_t lds,

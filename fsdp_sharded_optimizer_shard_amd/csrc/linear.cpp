@@ -43,58 +43,57 @@ extern "C" {
 
 zero_status zero_fsdp_linear_forward(const zero_layout *L, int32_t unit,
                                      const uint16_t *const *w_shards, int64_t batch,
-                                     const uint16_t *x, uint16_t *w_full, uint16_t *w_t, void *y,
+                                     const uint16_t *x, uint16_t *w_full, void *y,
                                      int32_t y_dtype, void *stream)
 {
     Dims d;
     zero_status st = layer_dims(L, unit, &d);
     if (st != ZERO_OK)
         return st;
-    if (!w_shards || !x || !w_full || !w_t || !y || batch < 0)
-        return zs::fail(ZERO_ERR_INVALID_ARG, "w_shards, x, w_full, w_t, y and batch >= 0 "
-                        "are required");
+    if (!w_shards || !x || !w_full || !y || batch < 0)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "w_shards, x, w_full, y and batch >= 0 are "
+                        "required");
     for (int32_t q = 0; q < L->parts; ++q)
         if (!w_shards[q])
             return zs::fail(ZERO_ERR_INVALID_ARG, "W shard of rank %d is NULL", q);
-    if (d.in % 8)
-        return zs::fail(ZERO_ERR_UNSUPPORTED, "in_features must be a multiple of 8");
+    if (d.in % 8 || d.out % 8)
+        return zs::fail(ZERO_ERR_UNSUPPORTED, "in_features and out_features must be "
+                        "multiples of 8");
     if ((st = zero_gather_params(L, unit, unit + 1, w_shards, L->parts, w_full, stream)) != ZERO_OK)
         return st;
-    if ((st = zero_transpose_bf16(d.in, d.out, w_full, d.out, w_t, d.in, stream)) != ZERO_OK)
-        return st;
-    return zero_gemm_bf16_nt(batch, d.out, d.in, x, d.in, w_t, d.in, y, d.out, y_dtype, stream);
+    // Y = X W: a(i, k) = X[i][k], b(j, k) = W[k][j]
+    return zero_gemm_bf16(batch, d.out, d.in, x, d.in, ZERO_K_INNER, w_full, d.out, ZERO_K_OUTER,
+                          y, d.out, y_dtype, stream);
 }
 
 zero_status zero_fsdp_linear_backward(const zero_layout *L, int32_t unit,
                                       const uint16_t *const *w_shards, int64_t batch,
                                       const uint16_t *x, const uint16_t *dy, uint16_t *w_full,
-                                      uint16_t *x_t, uint16_t *dy_t, void *dx, int32_t dx_dtype,
-                                      float *dw_full, void *stream)
+                                      void *dx, int32_t dx_dtype, float *dw_full, void *stream)
 {
     Dims d;
     zero_status st = layer_dims(L, unit, &d);
     if (st != ZERO_OK)
         return st;
-    if (!w_shards || !x || !dy || !w_full || !x_t || !dy_t || !dx || !dw_full || batch < 0)
+    if (!w_shards || !x || !dy || !w_full || !dx || !dw_full || batch < 0)
         return zs::fail(ZERO_ERR_INVALID_ARG, "every buffer and batch >= 0 are required");
     for (int32_t q = 0; q < L->parts; ++q)
         if (!w_shards[q])
             return zs::fail(ZERO_ERR_INVALID_ARG, "W shard of rank %d is NULL", q);
-    if (d.out % 8 || batch % 8)
-        return zs::fail(ZERO_ERR_UNSUPPORTED, "out_features and batch must be multiples of 8");
+    if (d.in % 8 || d.out % 8 || batch % 8)
+        return zs::fail(ZERO_ERR_UNSUPPORTED, "in_features, out_features and batch must be "
+                        "multiples of 8");
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // re-gather W (FSDP frees it after forward)
     if ((st = zero_gather_params(L, unit, unit + 1, w_shards, L->parts, w_full, stream)) != ZERO_OK)
         return st;
-    // dX = dY W^T: (batch x out) times (in x out)^T
-    if ((st = zero_gemm_bf16_nt(batch, d.in, d.out, dy, d.out, w_full, d.out, dx, d.in, dx_dtype,
-                                stream)) != ZERO_OK)
+    // dX = dY W^T: a(i, k) = dY[i][k], b(j, k) = W[j][k]
+    if ((st = zero_gemm_bf16(batch, d.in, d.out, dy, d.out, ZERO_K_INNER, w_full, d.out,
+                             ZERO_K_INNER, dx, d.in, dx_dtype, stream)) != ZERO_OK)
         return st;
-    // dW = X^T dY: (in x batch) times (out x batch)^T, fp32, full shape
-    if ((st = zero_transpose_bf16(batch, d.in, x, d.in, x_t, batch, stream)) != ZERO_OK ||
-        (st = zero_transpose_bf16(batch, d.out, dy, d.out, dy_t, batch, stream)) != ZERO_OK ||
-        (st = zero_gemm_bf16_nt(d.in, d.out, batch, x_t, batch, dy_t, batch, dw_full, d.out,
-                                ZERO_FP32, stream)) != ZERO_OK)
+    // dW = X^T dY, fp32, full shape: a(i, k) = X[k][i], b(j, k) = dY[k][j]
+    if ((st = zero_gemm_bf16(d.in, d.out, batch, x, d.in, ZERO_K_OUTER, dy, d.out, ZERO_K_OUTER,
+                             dw_full, d.out, ZERO_FP32, stream)) != ZERO_OK)
         return st;
     // padding rows of the row-sharded layout hold zero gradient
     return zs::zero_rows_fill(dw_full, d.out, d.in, d.in_pad, d.out, s);

@@ -311,13 +311,34 @@ zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro_bf16,
 
 /* ----------------------------------------------- FSDP linear layer -- */
 
-/* C[M x N] = A[M x K] * B[N x K]^T on the MFMA units: A and B bf16
-   row-major with leading dimensions lda, ldb (both operands contiguous
-   along K), fp32 accumulation, C row-major with leading dimension ldc, fp32
-   (c_dtype ZERO_FP32) or bf16 rounded to nearest even (ZERO_BF16).  Needs K,
-   lda, ldb multiples of 8, lda, ldb >= K, ldc >= N, and 16-byte aligned A
-   and B.  Accumulation order is the kernel's own (error within the usual
-   gamma_K bound of fp32 dot products). */
+/* How a GEMM operand is stored.  K_INNER: A as M x K, B as N x K (row-major,
+   K contiguous).  K_OUTER: A as K x M, B as K x N (row-major, M or N
+   contiguous). */
+typedef enum {
+    ZERO_K_INNER = 0,
+    ZERO_K_OUTER = 1
+} zero_operand_order;
+
+/* C[i][j] = sum_{k < K} a(i, k) * b(j, k) for i < M, j < N on the MFMA
+   units, where a(i, k) = A[i * lda + k] (K_INNER) or A[k * lda + i]
+   (K_OUTER), and b(j, k) = B[j * ldb + k] (K_INNER) or B[k * ldb + j]
+   (K_OUTER).  So with B K_OUTER this is C = A B, with both K_INNER
+   C = A B^T, with both K_OUTER C = A^T B.  A and B are bf16 bits; C is
+   row-major with leading dimension ldc, fp32 (c_dtype ZERO_FP32) or bf16
+   rounded to nearest even (ZERO_BF16).  Accumulation is fp32 in the
+   kernel's own order (error within the usual gamma_K bound of fp32 dot
+   products).  Needs K, lda and ldb multiples of 8, M (N) a multiple of 8
+   when A (B) is K_OUTER, lda >= K or M and ldb >= K or N by order,
+   ldc >= N, and 16-byte aligned A and B; ZERO_ERR_UNSUPPORTED or
+   ZERO_ERR_ALIGNMENT otherwise, with nothing launched.  M = 0 or N = 0 is
+   a no-op; K = 0 writes zeros.  All pointers are device memory owned by the
+   caller. */
+zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A,
+                           int64_t lda, int32_t a_order, const uint16_t *B,
+                           int64_t ldb, int32_t b_order, void *C, int64_t ldc,
+                           int32_t c_dtype, void *stream);
+
+/* zero_gemm_bf16 with both operands K_INNER: C = A B^T. */
 zero_status zero_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const uint16_t *A,
                               int64_t lda, const uint16_t *B, int64_t ldb,
                               void *C, int64_t ldc, int32_t c_dtype,
@@ -336,31 +357,30 @@ zero_status zero_transpose_bf16(int64_t rows, int64_t cols, const uint16_t *src,
    (zero_shard_init_rows): rows = in_features (in), cols = out_features
    (out), so rank r's W shard is its c_u x out rows.
    forward:  w_full = all-gather(w_shards) (device, L_u bf16 workspace);
-             w_t = W^T (device, out x in bf16 workspace);
              y = x W (x: batch x in bf16; y: batch x out, y_dtype).
    backward: w_full = all-gather(w_shards) again; dx = dy W^T (dy: batch x
-             out bf16; dx: batch x in, dx_dtype); x_t, dy_t (in x batch and
-             out x batch bf16 workspaces) = transposes; dw_full = x^T dy
-             (fp32, the padded unit: in rows then zeroed padding rows, L_u
+             out bf16; dx: batch x in, dx_dtype); dw_full = x^T dy (fp32,
+             the padded unit: in rows then zeroed padding rows, L_u
              elements).  The reduce-scatter of the N ranks' dw_full is
              zero_reduce_shard (fp32 grads, ZERO_INDEX_FULL) on this unit,
              and zero_adam_step(grad_fp32 = its output) steps the shard.
+   Every GEMM reads its operands in place (zero_gemm_bf16 with K_OUTER
+   operands), so no transposed copies are made.
    `w_shards` is a host array of world_n device pointers (s_u bf16 each, this
-   rank's own included).  in must be a multiple of 8 (forward), out and
-   batch multiples of 8 (backward). */
+   rank's own included).  in and out must be multiples of 8, and batch too
+   for the backward; x, dy, w_full and the shards 16-byte aligned. */
 zero_status zero_fsdp_linear_forward(const zero_layout *layout, int32_t unit,
                                      const uint16_t *const *w_shards,
                                      int64_t batch, const uint16_t *x,
-                                     uint16_t *w_full, uint16_t *w_t, void *y,
-                                     int32_t y_dtype, void *stream);
+                                     uint16_t *w_full, void *y, int32_t y_dtype,
+                                     void *stream);
 
 zero_status zero_fsdp_linear_backward(const zero_layout *layout, int32_t unit,
                                       const uint16_t *const *w_shards,
                                       int64_t batch, const uint16_t *x,
                                       const uint16_t *dy, uint16_t *w_full,
-                                      uint16_t *x_t, uint16_t *dy_t, void *dx,
-                                      int32_t dx_dtype, float *dw_full,
-                                      void *stream);
+                                      void *dx, int32_t dx_dtype,
+                                      float *dw_full, void *stream);
 
 /* ---------------------------------------------------------- errors -- */
 

@@ -257,3 +257,41 @@ def test_rows_layout_rejects_bad_shapes():
     # element-granular layouts report rows = elements
     L = zs.shard_init("zero2", 4, 3, [10])
     assert L.rows(0) == {"cols": 1, "first_row": 9, "row_count": 1}
+
+
+def test_gemm_and_linear_validation_launches_nothing():
+    def g(*a):
+        return zs.gemm_bf16(*a, stream=0)
+
+    KI, KO = zs.K_INNER, zs.K_OUTER
+    assert _err(g, 16, 16, 12, FAKE, 16, KI, FAKE, 16, KI, FAKE, 16).status == zs.ERR_UNSUPPORTED
+    assert _err(g, 16, 16, 16, FAKE, 16, 2, FAKE, 16, KI, FAKE, 16).status == zs.ERR_INVALID_ARG
+    assert _err(g, 16, 16, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE, 16, 7).status == \
+        zs.ERR_INVALID_ARG
+    # a K-outer operand needs its M (or N) a multiple of 8 and ld >= M (N)
+    assert _err(g, 12, 16, 16, FAKE, 16, KO, FAKE, 16, KI, FAKE, 16).status == zs.ERR_UNSUPPORTED
+    assert _err(g, 16, 12, 16, FAKE, 16, KI, FAKE, 16, KO, FAKE, 16).status == zs.ERR_UNSUPPORTED
+    assert _err(g, 32, 16, 16, FAKE, 24, KO, FAKE, 16, KI, FAKE, 16).status == zs.ERR_INVALID_ARG
+    assert _err(g, 16, 32, 16, FAKE, 16, KI, FAKE, 24, KO, FAKE, 32).status == zs.ERR_INVALID_ARG
+    assert _err(g, 16, 16, 16, FAKE, 8, KI, FAKE, 16, KI, FAKE, 16).status == zs.ERR_INVALID_ARG
+    assert _err(g, 16, 16, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE, 8).status == zs.ERR_INVALID_ARG
+    assert _err(g, 16, 16, 16, FAKE + 2, 16, KI, FAKE, 16, KI, FAKE, 16).status == \
+        zs.ERR_ALIGNMENT
+    assert _err(g, 16, 16, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE + 2, 16).status == \
+        zs.ERR_ALIGNMENT
+    assert _err(g, 16, 16, 16, None, 16, KI, FAKE, 16, KI, FAKE, 16).status == zs.ERR_INVALID_ARG
+    # empty outputs launch nothing
+    g(0, 16, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE, 16)
+    g(16, 0, 16, FAKE, 16, KO, FAKE, 16, KO, FAKE, 16)
+    assert _err(zs.transpose_bf16, 4, 8, FAKE, 4, FAKE, 4, stream=0).status == zs.ERR_INVALID_ARG
+    # linear layer: sizes that the GEMMs cannot take are refused before the gather
+    L = zs.shard_init_rows("fsdp2", 4, 1, [(12, 16)])
+    assert _err(zs.fsdp_linear_forward, L, 0, [FAKE] * 4, 8, FAKE, FAKE, FAKE, stream=0).status == \
+        zs.ERR_UNSUPPORTED
+    L = zs.shard_init_rows("fsdp2", 4, 1, [(16, 16)])
+    assert _err(zs.fsdp_linear_backward, L, 0, [FAKE] * 4, 12, FAKE, FAKE, FAKE, FAKE,
+                FAKE, stream=0).status == zs.ERR_UNSUPPORTED
+    assert _err(zs.fsdp_linear_forward, L, 0, [FAKE, None, FAKE, FAKE], 8, FAKE, FAKE,
+                FAKE, stream=0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.fsdp_linear_forward, L, 1, [FAKE] * 4, 8, FAKE, FAKE, FAKE, stream=0).status == \
+        zs.ERR_INVALID_ARG

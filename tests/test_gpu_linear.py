@@ -67,6 +67,54 @@ def test_gemm_nt_within_fp32_bound(M, N, K, extra):
     check_f32(cb, exact, bound + 2.0 ** -8 * (np.abs(exact) + bound), "bf16 C")
 
 
+ORDERS = [(0, 0), (1, 0), (0, 1), (1, 1)]
+
+
+@pytest.mark.parametrize("ao,bo", ORDERS)
+@pytest.mark.parametrize("M,N,K,pad", [(8, 8, 8, 0), (200, 312, 72, 8), (264, 520, 200, 16),
+                                       (520, 256, 1096, 0)])
+def test_gemm_operand_orders_within_fp32_bound(ao, bo, M, N, K, pad):
+    """Every operand order (K-inner: stored rows x K; K-outer: stored K x
+    rows), ragged in M, N and K (several 256-tiles, K past a 64 multiple),
+    with leading dimensions wider than the matrix."""
+    rng = np.random.default_rng(M + 3 * N + 7 * K + 11 * ao + 13 * bo)
+    a = rand_bf16(rng, (M, K))
+    b = rand_bf16(rng, (N, K))
+    def stored(x, outer):
+        rows, k = x.shape
+        st = np.full((k, rows + pad) if outer else (rows, k + pad), 0x7FC0, np.uint16)
+        if outer:
+            st[:, :rows] = x.T
+        else:
+            st[:, :k] = x
+        return st
+    A, B = stored(a, ao), stored(b, bo)
+    av, bv = linear.bf16_values(a), linear.bf16_values(b)
+    exact = av @ bv.T
+    bound = linear.gemm_bound(av, bv.T)
+    C = torch.full((M, N + 5), 7.0, device=DEV)
+    Cb = torch.zeros((M, N), dtype=torch.int16, device=DEV)
+    order = (zs.K_INNER, zs.K_OUTER)
+    zs.gemm_bf16(M, N, K, dev16(A), A.shape[1], order[ao], dev16(B), B.shape[1], order[bo], C,
+                 N + 5, zs.FP32)
+    zs.gemm_bf16(M, N, K, dev16(A), A.shape[1], order[ao], dev16(B), B.shape[1], order[bo], Cb,
+                 N, zs.BF16)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy()
+    check_f32(c[:, :N], exact, bound, "fp32 C")
+    assert np.all(c[:, N:] == 7.0)          # columns past N untouched (the padding holds NaN)
+    cb = linear.bf16_values(host16(Cb))
+    check_f32(cb, exact, bound + 2.0 ** -8 * (np.abs(exact) + bound), "bf16 C")
+
+
+def test_gemm_k_zero_writes_zeros():
+    C = torch.full((16, 24), 3.0, device=DEV)
+    buf = torch.zeros(64, dtype=torch.int16, device=DEV)
+    zs.gemm_bf16(16, 24, 0, buf, 16, zs.K_OUTER, buf, 24, zs.K_OUTER, C, 24, zs.FP32)
+    torch.cuda.synchronize()
+    assert not C.cpu().numpy().any()
+
+
 def test_transpose_exact():
     rng = np.random.default_rng(3)
     for rows, cols in [(1, 1), (64, 64), (130, 77), (1000, 33)]:
@@ -100,17 +148,14 @@ def _run_layer(L, n, rank, inf, outf, batch, c, shards, xs, dys):
     Lu = L.query(0)["padded_len"]
     dsh = [dev16(s) for s in shards]
     w_full = torch.empty(Lu, dtype=torch.int16, device=DEV)
-    w_t = torch.empty(outf * inf, dtype=torch.int16, device=DEV)
-    x_t = torch.empty(inf * batch, dtype=torch.int16, device=DEV)
-    dy_t = torch.empty(outf * batch, dtype=torch.int16, device=DEV)
     y = torch.empty((batch, outf), device=DEV)
-    zs.fsdp_linear_forward(L, 0, dsh, batch, dev16(xs[rank]), w_full, w_t, y, zs.FP32)
+    zs.fsdp_linear_forward(L, 0, dsh, batch, dev16(xs[rank]), w_full, y, zs.FP32)
     dws, dx = [], None
     for q in range(n):
         dw = torch.full((Lu,), 9.0, device=DEV)
         dxq = torch.empty((batch, inf), device=DEV)
-        zs.fsdp_linear_backward(L, 0, dsh, batch, dev16(xs[q]), dev16(dys[q]), w_full, x_t, dy_t,
-                                dxq, dw, zs.FP32)
+        zs.fsdp_linear_backward(L, 0, dsh, batch, dev16(xs[q]), dev16(dys[q]), w_full, dxq, dw,
+                                zs.FP32)
         dws.append(dw)
         if q == rank:
             dx = dxq
