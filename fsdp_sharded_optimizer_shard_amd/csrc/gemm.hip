@@ -57,6 +57,7 @@ constexpr int kGroupM = 8;  // tile rows walked together
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
@@ -72,37 +73,49 @@ __device__ __forceinline__ int lds_pos(int r, int c)
     return r * kBK + ((c ^ ((r ^ (r >> 3)) & 7)) * 8);
 }
 
-// Per-thread source pointers of one operand's 256 x 64 tile (at k = 0).
-// K-inner: chunk i is row (row0 + t/8 + 32 i) clamped to the last row, k
-// chunk t % 8.  K-outer: row i of the 8 x 8 block is k = 8 (t / 32) + i, rows
-// row0 + 8 (t % 32) .. +7 (clamped to the last 8; rows % 8 == 0).  Clamped
-// rows only feed C rows or columns that are never stored.
-template <bool KOUTER>
+// Staging of one operand's R x 64 tile (R = 256, or 128 for a half tile).
+// K-inner: thread t reads the 16-byte chunks (row t/8 + 32 i, k chunk t % 8),
+// i < R / 32.  K-outer: thread t reads the block of rows RB (t % 32) .. +RB-1
+// (RB = R / 32) at k = 8 (t / 32) .. +7 -- eight loads of RB elements -- and
+// transposes it in registers into RB chunks of 8 k values.  Both give R / 32
+// LDS writes per thread.  Rows past the matrix are clamped to real rows
+// (K-outer: to the last RB; rows % 8 == 0): they only feed C rows or
+// columns that are never stored.
+template <int R, bool KOUTER>
+struct Stage {
+    static constexpr int RB = R / 32;              // K-outer rows per block
+    static constexpr int NL = KOUTER ? 8 : R / 32;  // global loads per thread
+    static constexpr int NW = R / 32;               // LDS writes per thread
+};
+
+template <int R, bool KOUTER>
 __device__ __forceinline__ void tile_sources(const uint16_t *(&src)[8], const uint16_t *base,
                                              int64_t ld, int64_t row0, int64_t rows, int t)
 {
+    constexpr int RB = Stage<R, KOUTER>::RB;
     if (!KOUTER) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < R / 32; ++i) {
             int64_t row = row0 + (t >> 3) + 32 * i;
             row = row < rows ? row : rows - 1;
             src[i] = base + row * ld + (t & 7) * 8;
         }
     } else {
-        int64_t c = row0 + (t & 31) * 8;
-        c = c < rows ? c : rows - 8;
+        int64_t c = row0 + (t & 31) * RB;
+        c = c < rows ? c : rows - RB;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             src[i] = base + (int64_t)((t >> 5) * 8 + i) * ld + c;
     }
 }
 
-template <bool KOUTER>
+template <int R, bool KOUTER>
 __device__ __forceinline__ void tile_dests(int (&dst)[8], int t)
 {
+    constexpr int RB = Stage<R, KOUTER>::RB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        dst[i] = KOUTER ? lds_pos((t & 31) * 8 + i, t >> 5) : lds_pos((t >> 3) + 32 * i, t & 7);
+    for (int i = 0; i < R / 32; ++i)
+        dst[i] = KOUTER ? lds_pos((t & 31) * RB + i, t >> 5) : lds_pos((t >> 3) + 32 * i, t & 7);
 }
 
 // k offset, within the tile, of the data thread t stages.
@@ -115,28 +128,38 @@ __device__ __forceinline__ int tile_kofs(int t)
 // Global -> registers for the tile at k0.  MASKED: the tile runs past K; the
 // thread's 8 k values are all in range or all out (K % 8 == 0) and out of
 // range ones read as zero.
-template <bool KOUTER, bool MASKED>
+template <int R, bool KOUTER, bool MASKED>
 __device__ __forceinline__ void tile_load(u32x4 (&v)[8], const uint16_t *const (&src)[8],
                                           int64_t ld, int64_t k0, int64_t K, int kofs)
 {
     const int64_t adv = KOUTER ? k0 * ld : k0;
     const bool ok = !MASKED || k0 + kofs < K;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if (MASKED)
-            v[i] = ok ? *reinterpret_cast<const u32x4 *>(src[i] + adv) : u32x4{0u, 0u, 0u, 0u};
-        else
-            v[i] = *reinterpret_cast<const u32x4 *>(src[i] + adv);
+    for (int i = 0; i < Stage<R, KOUTER>::NL; ++i) {
+        if (!KOUTER || R == 256) {
+            if (MASKED)
+                v[i] = ok ? *reinterpret_cast<const u32x4 *>(src[i] + adv) : u32x4{0u, 0u, 0u, 0u};
+            else
+                v[i] = *reinterpret_cast<const u32x4 *>(src[i] + adv);
+        } else {  // K-outer half tile: 4 rows (8 bytes) per load
+            u32x2 h;
+            if (MASKED)
+                h = ok ? *reinterpret_cast<const u32x2 *>(src[i] + adv) : u32x2{0u, 0u};
+            else
+                h = *reinterpret_cast<const u32x2 *>(src[i] + adv);
+            v[i][0] = h[0];
+            v[i][1] = h[1];
+        }
     }
 }
 
-// Registers -> LDS.  K-outer: v[i] holds rows 0..7 at k = i; row j's eight
-// k values are gathered with v_perm_b32 (low or high halves of a pair).
-template <bool KOUTER>
+// Registers -> LDS.  K-outer: v[i] holds rows 0..RB-1 at k = i; row j's
+// eight k values are gathered with v_perm_b32 (low or high halves of a pair).
+template <int R, bool KOUTER>
 __device__ __forceinline__ void tile_store(const u32x4 (&v)[8], uint16_t *lds, const int (&dst)[8])
 {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < Stage<R, KOUTER>::NW; ++j) {
         u32x4 w;
         if (!KOUTER) {
             w = v[j];
@@ -150,43 +173,53 @@ __device__ __forceinline__ void tile_store(const u32x4 (&v)[8], uint16_t *lds, c
     }
 }
 
-template <bool A_KOUTER, bool B_KOUTER, bool OUT_BF16>
-__global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t K,
-                                                   const uint16_t *__restrict__ A, int64_t lda,
-                                                   const uint16_t *__restrict__ B, int64_t ldb,
-                                                   void *__restrict__ C, int64_t ldc, int tiles_m,
-                                                   int tiles_n)
+// XCD-contiguous order over a range of `n` blocks: block i of the range runs
+// on XCD (first + i) % 8, and each XCD gets a contiguous run of the range.
+__device__ __forceinline__ int xcd_order(int i, int n)
 {
-    constexpr int TM = 4, TN = 4;      // 32 x 32 MFMA tiles per wave
-    constexpr int NF = TM + TN;        // fragment reads per substep
-    constexpr int NMF = TM * TN;       // MFMAs per substep
-    constexpr int NG = 16;             // global loads (and LDS writes) per K tile
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
+    const int per = n / 8, rem = n % 8, x = i % 8;
+    return x * per + (x < rem ? x : rem) + i / 8;
+}
 
-    // XCD-contiguous, grouped tile order.
-    const int T = tiles_m * tiles_n;
-    const int b = blockIdx.x;
-    const int per = T / 8, rem = T % 8, x = b % 8;
-    const int logical = x * per + (x < rem ? x : rem) + b / 8;
+// Grouped order: big tile `logical` -> (tile row, tile column), kGroupM tile
+// rows at a time.
+__device__ __forceinline__ void grouped(int logical, int tiles_m, int tiles_n, int &tm, int &tn)
+{
     const int gsz = kGroupM * tiles_n;
     const int g = logical / gsz;
     const int first_m = g * kGroupM;
     const int gm = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
     const int in_g = logical - g * gsz;
-    const int64_t m0 = (int64_t)(first_m + in_g % gm) * kBM;
-    const int64_t n0 = (int64_t)(in_g / gm) * kBN;
+    tm = first_m + in_g % gm;
+    tn = in_g / gm;
+}
+
+// One BM x 256 tile of C (BM = 256, or 128 for half tiles): 4 waves, each
+// (BM / 2) x 128 as (BM / 64) x 4 MFMA tiles.
+template <int BM, bool A_KOUTER, bool B_KOUTER, bool OUT_BF16>
+__device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
+                                          const uint16_t *__restrict__ A, int64_t lda,
+                                          const uint16_t *__restrict__ B, int64_t ldb,
+                                          void *__restrict__ C, int64_t ldc, int64_t m0,
+                                          int64_t n0, uint16_t (*As)[kBM * kBK],
+                                          uint16_t (*Bs)[kBN * kBK])
+{
+    constexpr int TM = BM / 64, TN = 4;  // 32 x 32 MFMA tiles per wave
+    constexpr int NF = TM + TN;          // fragment reads per substep
+    constexpr int NMF = TM * TN;         // MFMAs per substep
+    constexpr int NG = Stage<BM, A_KOUTER>::NL + Stage<kBN, B_KOUTER>::NL;  // global loads
+    constexpr int NW = Stage<BM, A_KOUTER>::NW + Stage<kBN, B_KOUTER>::NW;  // LDS writes
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * (kBM / 2), wn = (wave & 1) * (kBN / 2);
+    const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (kBN / 2);
     const int fr = lane & 31, fh = lane >> 5;
 
     const uint16_t *sa[8], *sb[8];
-    tile_sources<A_KOUTER>(sa, A, lda, m0, M, t);
-    tile_sources<B_KOUTER>(sb, B, ldb, n0, N, t);
+    tile_sources<BM, A_KOUTER>(sa, A, lda, m0, M, t);
+    tile_sources<kBN, B_KOUTER>(sb, B, ldb, n0, N, t);
     int da[8], db[8];
-    tile_dests<A_KOUTER>(da, t);
-    tile_dests<B_KOUTER>(db, t);
+    tile_dests<BM, A_KOUTER>(da, t);
+    tile_dests<kBN, B_KOUTER>(db, t);
     const int ka = tile_kofs<A_KOUTER>(t), kb = tile_kofs<B_KOUTER>(t);
 
     // Fragment read positions for the four substeps.
@@ -230,16 +263,16 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t
     };
     auto load = [&](int64_t k0, bool masked) {
         if (masked) {
-            tile_load<A_KOUTER, true>(ra, sa, lda, k0, K, ka);
-            tile_load<B_KOUTER, true>(rb, sb, ldb, k0, K, kb);
+            tile_load<BM, A_KOUTER, true>(ra, sa, lda, k0, K, ka);
+            tile_load<kBN, B_KOUTER, true>(rb, sb, ldb, k0, K, kb);
         } else {
-            tile_load<A_KOUTER, false>(ra, sa, lda, k0, K, ka);
-            tile_load<B_KOUTER, false>(rb, sb, ldb, k0, K, kb);
+            tile_load<BM, A_KOUTER, false>(ra, sa, lda, k0, K, ka);
+            tile_load<kBN, B_KOUTER, false>(rb, sb, ldb, k0, K, kb);
         }
     };
     auto store = [&](int buf) {
-        tile_store<A_KOUTER>(ra, As[buf], da);
-        tile_store<B_KOUTER>(rb, Bs[buf], db);
+        tile_store<BM, A_KOUTER>(ra, As[buf], da);
+        tile_store<kBN, B_KOUTER>(rb, Bs[buf], db);
     };
     // Interleave: per fragment read, NMF / NF MFMAs (and optionally NG / NF
     // global loads).
@@ -272,8 +305,8 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t
             store(cur ^ 1);
 #pragma unroll
             for (int q = 0; q < NMF / 2; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x200, NG / (NMF / 2), 0);  // LDS write
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x200, NW / (NMF / 2), 0);  // LDS write
             }
         }
         __syncthreads();
@@ -326,6 +359,34 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t
             }
 }
 
+// Blocks [0, n_big) compute whole 256 x 256 tiles (big tiles 0 .. n_big-1 in
+// grouped order); the remaining blocks split the last big tiles into
+// 128 x 256 halves, two blocks per tile, so a partial last wave of big
+// tiles becomes a wave of half-length work.
+template <bool A_KOUTER, bool B_KOUTER, bool OUT_BF16>
+__global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t K,
+                                                   const uint16_t *__restrict__ A, int64_t lda,
+                                                   const uint16_t *__restrict__ B, int64_t ldb,
+                                                   void *__restrict__ C, int64_t ldc, int tiles_m,
+                                                   int tiles_n, int n_big)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBN * kBK];
+    const int b = blockIdx.x;
+    int tm, tn;
+    if (b < n_big) {
+        grouped(xcd_order(b, n_big), tiles_m, tiles_n, tm, tn);
+        gemm_tile<kBM, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc,
+                                                     (int64_t)tm * kBM, (int64_t)tn * kBN, As, Bs);
+    } else {
+        const int h = xcd_order(b - n_big, (int)gridDim.x - n_big);
+        grouped(n_big + h / 2, tiles_m, tiles_n, tm, tn);
+        gemm_tile<kBM / 2, A_KOUTER, B_KOUTER, OUT_BF16>(
+            M, N, K, A, lda, B, ldb, C, ldc, (int64_t)tm * kBM + (h & 1) * (kBM / 2),
+            (int64_t)tn * kBN, As, Bs);
+    }
+}
+
 // 64 x 64 tiles through LDS (one padding column against bank conflicts):
 // reads along src rows and writes along dst rows are both coalesced.
 constexpr int kTT = 64;
@@ -361,6 +422,24 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(float *p, int64_t ld, in
 }
 
 bool a16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Compute units of the current device (cached per device).
+int cu_count()
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        dev = -1;
+    if (dev >= 0 && dev < 64 && cache[dev] > 0)
+        return cache[dev];
+    int n = 0;
+    if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                       hipSuccess || n <= 0)
+        n = 256;
+    if (dev >= 0 && dev < 64)
+        cache[dev] = n;
+    return n;
+}
 
 zero_status launched(const char *what)
 {
@@ -419,15 +498,20 @@ zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, i
     if (reinterpret_cast<uintptr_t>(C) % (c_dtype == ZERO_BF16 ? 2 : 4))
         return fail(ZERO_ERR_ALIGNMENT, "C is misaligned");
     const int64_t tm = (M + zs::kBM - 1) / zs::kBM, tn = (N + zs::kBN - 1) / zs::kBN;
-    if (tm > INT_MAX / tn)
+    if (tm > INT_MAX / 2 / tn)
         return fail(ZERO_ERR_UNSUPPORTED, "too many GEMM tiles for one launch");
-    const dim3 grid((unsigned)(tm * tn)), block(zs::kGT);
+    // One block per CU at a time (128 KB of LDS).  A last wave of at most
+    // half the CUs runs as twice as many half tiles.
+    const int64_t T = tm * tn, P = zs::cu_count();
+    const int64_t rem = T % P;
+    const int64_t n_big = rem > 0 && rem <= P / 2 ? T - rem : T;
+    const dim3 grid((unsigned)(n_big + 2 * (T - n_big))), block(zs::kGT);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int code = (ao ? 1 : 0) | (bo ? 2 : 0) | (c_dtype == ZERO_BF16 ? 4 : 0);
     (void)hipGetLastError();
 #define ZS_GEMM(AO, BO, BF)                                                                      \
     hipLaunchKernelGGL((zs::gemm_kernel<AO, BO, BF>), grid, block, 0, s, M, N, K, A, lda, B, ldb, \
-                       C, ldc, (int)tm, (int)tn)
+                       C, ldc, (int)tm, (int)tn, (int)n_big)
     switch (code) {
     case 0: ZS_GEMM(false, false, false); break;
     case 1: ZS_GEMM(true, false, false); break;
