@@ -36,6 +36,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "fused_step_7b_n8_counters.md")
 KERNELS_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_shard_amd", "csrc", "kernels.hip")
+GEMM_COUNTERS = os.path.join(ROOT, "profiles", "gemm_fsdp_linear_mistral_up_counters.md")
+GEMM_SRC = os.path.join(ROOT, "fsdp_sharded_optimizer_shard_amd", "csrc", "gemm.hip")
 HEADLINE_METRIC = "shard optimizer-step params/sec at 7B N=8; achieved HBM GB/s vs peak"
 
 
@@ -84,7 +86,9 @@ class Phases:
         for name, a, b in self.marks:
             per.setdefault(name, []).append(a.elapsed_time(b))
         return {k: {"ms_per_step": sum(v) / steps, "launches_per_step": len(v) // steps,
-                    "ms_per_launch_mean": sum(v) / len(v), "ms_per_launch_min": min(v)}
+                    "ms_per_launch_mean": sum(v) / len(v), "ms_per_launch_min": min(v),
+                    "ms_per_launch_median": sorted(v)[len(v) // 2],
+                    "ms_per_launch_max": max(v)}
                 for k, v in per.items()}
 
 
@@ -549,7 +553,10 @@ def run_fsdp_linear(args, torch, zs, np):
                                                    "all 10 launches of the step",
                        "achieved": out["gemm_tflops"], "peak": MFMA_BF16_PEAK_TFLOPS,
                        "unit": "TFLOP/s", "frac": out["gemm_tflops"] / MFMA_BF16_PEAK_TFLOPS,
-                       "traffic": None}
+                       "traffic": counter_traffic(GEMM_COUNTERS, GEMM_SRC, "gemm_hip_sha256",
+                                                  "gemm_traffic_bytes_per_step"),
+                       "traffic_unit": "HBM bytes of the 10 GEMM launches of one step "
+                                       "(rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
     out["cpu_baseline"] = None
     return out
 
@@ -573,18 +580,19 @@ def calibrate_copy(args, torch, zs, np):
     return {"calibrate_copy_bytes": 2 * n, "ms": ms, "GBps": 4 * n / ms / 1e6}
 
 
-def counter_traffic():
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE summary (already scaled by the copy calibration),
-    or None if that summary was taken on a different kernels.hip."""
+def counter_traffic(path=COUNTERS, src=KERNELS_SRC, sha_key="kernels_hip_sha256",
+                    key="fused_traffic_bytes_per_launch"):
+    """HBM bytes from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    (already scaled by the copy calibration), or None if that summary was
+    taken on a different version of the kernel source."""
     import hashlib
     try:
-        kv = dict(line.split(": ", 1) for line in open(COUNTERS).read().splitlines()
-                  if line.startswith(("kernels_hip_sha256: ", "fused_traffic_bytes_per_launch: ")))
-        sha = hashlib.sha256(open(KERNELS_SRC, "rb").read()).hexdigest()
-        if kv.get("kernels_hip_sha256") != sha:
+        kv = dict(line.split(": ", 1) for line in open(path).read().splitlines()
+                  if line.startswith((sha_key + ": ", key + ": ")))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if kv.get(sha_key) != sha:
             return None
-        return float(kv["fused_traffic_bytes_per_launch"])
+        return float(kv[key])
     except (OSError, KeyError, ValueError):
         return None
 
