@@ -546,8 +546,8 @@ zero_status zero_transpose_bf16(int64_t rows, int64_t cols, const uint16_t *src,
         return fail(ZERO_ERR_INVALID_ARG, "transpose needs src, dst, lds >= cols, ldd >= rows");
     if (reinterpret_cast<uintptr_t>(src) % 2 || reinterpret_cast<uintptr_t>(dst) % 2)
         return fail(ZERO_ERR_ALIGNMENT, "transpose buffers are misaligned");
-    if ((rows + zs::kTT - 1) / zs::kTT > 65535)
-        return fail(ZERO_ERR_UNSUPPORTED, "too many rows for one launch");
+    if ((rows + zs::kTT - 1) / zs::kTT > 65535 || (cols + zs::kTT - 1) / zs::kTT > INT_MAX)
+        return fail(ZERO_ERR_UNSUPPORTED, "transpose too large for one launch");
     const dim3 grid((unsigned)((cols + zs::kTT - 1) / zs::kTT),
                     (unsigned)((rows + zs::kTT - 1) / zs::kTT));
     (void)hipGetLastError();

@@ -582,12 +582,16 @@ int resident_blocks(Kernel kernel, int threads = kThreads)
 
 // `resident` (blocks of the kernel that fit on one CU) caps the persistent
 // width so a persistent grid is fully resident from the start.
+// Every kernel walks its tiles with a grid stride, so capping the width at
+// the largest grid dimension keeps any tile count launchable.
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
 int64_t stream_grid(int64_t n_tiles, int resident)
 {
     const int o = blocks_per_cu_override();
-    if (o == 0)
-        return n_tiles;
-    const int64_t g = (int64_t)device_cus() * (o < resident ? o : resident);
+    int64_t g = kMaxGrid;
+    if (o != 0)
+        g = (int64_t)device_cus() * (o < resident ? o : resident);
     return n_tiles < g ? n_tiles : g;
 }
 
@@ -933,14 +937,14 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
             a.n_tiles = tiles;
             a.dst = param_full;
             a.vec_ptrs = al;
-                if (tiles == 0)
+            if (tiles == 0)
                 return ZERO_OK;
             // default: one block per (tile, source) -- paired runs on the 7-
             // and 63-source shapes measured 6.2-6.3 TB/s against 5.4-5.6 with
             // each block walking n_src tiles; a persistent override spreads
             // its width over the sources
             static const int resident = resident_blocks(gather_kernel);
-            int64_t gx = blocks_per_cu_override() == 0 ? tiles
+            int64_t gx = blocks_per_cu_override() == 0 ? stream_grid(tiles, resident)
                                                       : stream_grid(tiles, resident) / a.n_src;
             gx = gx < 1 ? 1 : gx;
             (void)hipGetLastError();
