@@ -98,16 +98,28 @@ struct StepArgs {
 
 // ------------------------------------------------------------ helpers --
 
-// Tiles a block walks: a grid-stride over the launch's tile space.  The
-// default launch has one block per tile (a single iteration); the
-// persistent width (ZERO_SHARD_BLOCKS_PER_CU) walks several.  Every tile is
-// visited exactly once, in increasing order per block.
+// Tiles a block walks.  The default launch has one block per tile.  With
+// `by_xcd`, the tiles are dealt out so that each XCD (block b runs on XCD
+// b % 8) gets a contiguous eighth of the tile space, walked in order: each
+// XCD's L2 and address translation then see one compact window per stream
+// instead of a slice of every window.  Paired runs (same process, same
+// buffers) measured it 2-4 % faster for the gather and the fp32
+// accumulation, 1.4 % for the fused bf16 step (up to 2 % where the buffer
+// placement was slow), neutral for the reduce and the fp32 fused step, and
+// 1-5 % slower for the apply pass, which therefore keeps the plain order.
+// A persistent width (ZERO_SHARD_BLOCKS_PER_CU) walks the tiles with a grid
+// stride instead.  Every tile is visited exactly once.
 struct TileWalk {
     int64_t t, end, stride;
 };
 
-__device__ __forceinline__ TileWalk tile_walk(int64_t n_tiles)
+__device__ __forceinline__ TileWalk tile_walk(int64_t n_tiles, bool by_xcd)
 {
+    if (by_xcd && (int64_t)gridDim.x == n_tiles) {
+        const int64_t i = blockIdx.x, per = n_tiles / 8, rem = n_tiles % 8, x = i % 8;
+        const int64_t t = x * per + (x < rem ? x : rem) + i / 8;
+        return {t, t + 1, 1};
+    }
     return {(int64_t)blockIdx.x, n_tiles, (int64_t)gridDim.x};
 }
 
@@ -401,7 +413,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs a)
     const float coef = (MODE == kApply && a.clip) ? *a.clip : 1.0f;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const TileWalk tw = tile_walk(a.n_tiles);
+    const TileWalk tw = tile_walk(a.n_tiles, MODE != kApply);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         const Seg &sg = a.seg[find_seg(a.seg, a.n_segs, t)];
         const int64_t j[1] = {(t - sg.tile0) * kTile + wave * kStepWaveElems + lane * 4};
@@ -451,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a)
     const int y = blockIdx.y;
     const uint16_t *src = a.src[y];
     const int64_t q = a.rank_of[y];
-    const TileWalk tw = tile_walk(a.n_tiles);
+    const TileWalk tw = tile_walk(a.n_tiles, true);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         const GSeg &sg = a.seg[find_seg(a.seg, a.n_segs, t)];
         const int64_t j = (t - sg.tile0) * kTile + (int64_t)threadIdx.x * kVec;
@@ -478,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(float *acc, const 
                                                               int64_t n, int32_t vec)
 {
     const int64_t lane_off = (threadIdx.x >> 6) * kWaveElems + (threadIdx.x & 63) * 4;
-    const TileWalk tw = tile_walk((n + kTile - 1) / kTile);
+    const TileWalk tw = tile_walk((n + kTile - 1) / kTile, true);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         const int64_t b = t * kTile;
 #pragma unroll
