@@ -39,9 +39,8 @@
 namespace zs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kVec = 8;                     // elements per thread per tile
-constexpr int kTile = kThreads * kVec;      // elements per tile
+constexpr int kTile = 2048;                 // elements per tile
+constexpr int kVec = 8;                     // gather: bf16 elements per 16-byte chunk
 constexpr int kMaxSegs = 32;                // units per launch (kernarg table)
 constexpr int kStepThreads = 512;           // step kernel: one 4-element group per lane
 constexpr int kStepWaveElems = kTile / (kStepThreads / 64);  // 256
@@ -457,7 +456,12 @@ struct GatherArgs {
 };
 
 // blockIdx.y selects the source rank; x walks the tiles of every slice.
-__global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a)
+// 128-thread blocks: thread i copies the 8-element chunks at 8i and
+// 1024 + 8i of its tile (each wave instruction moves 1 KiB contiguous).
+// Paired runs measured this 0.1-4.6 % faster for 7 sources and 0.6-1.1 %
+// for 63 than 256 threads with one chunk each.
+constexpr int kGatherThreads = 128;
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(const GatherArgs a)
 {
     const int y = blockIdx.y;
     const uint16_t *src = a.src[y];
@@ -465,18 +469,22 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(const GatherArgs a)
     const TileWalk tw = tile_walk(a.n_tiles, true);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         const GSeg &sg = a.seg[find_seg(a.seg, a.n_segs, t)];
-        const int64_t j = (t - sg.tile0) * kTile + (int64_t)threadIdx.x * kVec;
-        if (j >= sg.len)
-            continue;
-        const int64_t si = sg.shard_off + j;
-        const int64_t di = sg.flat_base + q * sg.len + j;
-        if (sg.vec && a.vec_ptrs && j + kVec <= sg.len) {
-            st_nt(reinterpret_cast<u32x4 *>(a.dst + di),
-                  ld_nt(reinterpret_cast<const u32x4 *>(src + si)));
-        } else {
-            const int64_t cnt = (sg.len - j) < kVec ? (sg.len - j) : kVec;
-            for (int64_t e = 0; e < cnt; ++e)
-                a.dst[di + e] = src[si + e];
+#pragma unroll
+        for (int h = 0; h < kTile / (kGatherThreads * kVec); ++h) {
+            const int64_t j = (t - sg.tile0) * kTile + (int64_t)h * (kGatherThreads * kVec) +
+                              (int64_t)threadIdx.x * kVec;
+            if (j >= sg.len)
+                continue;
+            const int64_t si = sg.shard_off + j;
+            const int64_t di = sg.flat_base + q * sg.len + j;
+            if (sg.vec && a.vec_ptrs && j + kVec <= sg.len) {
+                st_nt(reinterpret_cast<u32x4 *>(a.dst + di),
+                      ld_nt(reinterpret_cast<const u32x4 *>(src + si)));
+            } else {
+                const int64_t cnt = (sg.len - j) < kVec ? (sg.len - j) : kVec;
+                for (int64_t e = 0; e < cnt; ++e)
+                    a.dst[di + e] = src[si + e];
+            }
         }
     }
 }
@@ -581,7 +589,7 @@ int blocks_per_cu_override()
 }
 
 template <typename Kernel>
-int resident_blocks(Kernel kernel, int threads = kThreads)
+int resident_blocks(Kernel kernel, int threads)
 {
     int nb = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess ||
@@ -953,13 +961,13 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
             // and 63-source shapes measured 6.2-6.3 TB/s against 5.4-5.6 with
             // each block walking n_src tiles; a persistent override spreads
             // its width over the sources
-            static const int resident = resident_blocks(gather_kernel);
+            static const int resident = resident_blocks(gather_kernel, kGatherThreads);
             int64_t gx = blocks_per_cu_override() == 0 ? stream_grid(tiles, resident)
                                                       : stream_grid(tiles, resident) / a.n_src;
             gx = gx < 1 ? 1 : gx;
             (void)hipGetLastError();
-            hipLaunchKernelGGL(gather_kernel, dim3((unsigned)gx, (unsigned)a.n_src), dim3(kThreads),
-                               0, s, a);
+            hipLaunchKernelGGL(gather_kernel, dim3((unsigned)gx, (unsigned)a.n_src),
+                               dim3(kGatherThreads), 0, s, a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return fail(ZERO_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e));
