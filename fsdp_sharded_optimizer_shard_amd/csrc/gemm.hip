@@ -33,7 +33,7 @@
 // second half.  sched_group_barrier fixes that interleave.
 //
 // Tile order.  Block b runs on XCD b % 8; each XCD gets a contiguous range of
-// tiles, walked 8 tile rows at a time, so the blocks that share an L2 share
+// tiles, walked 4 tile rows at a time, so the blocks that share an L2 share
 // A rows and B columns.
 //
 // MFMA 32x32x16 bf16 lane layout (checked on the device against an exact
@@ -52,7 +52,10 @@ namespace {
 
 constexpr int kGT = 256;  // threads per GEMM block
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kGroupM = 8;  // tile rows walked together
+// Tile rows walked together.  Paired runs of the Mistral-7B MLP layer's
+// GEMMs (distinct operands per launch): 4 rows beat 8 by 9 % on the dW
+// products and 1-2 % on the others; 2, 6 and 16 were slower than 4.
+constexpr int kGroupM = 4;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
