@@ -477,6 +477,11 @@ def run_fsdp70b(args, torch, zs, np):
     out["roofline"] = roofline("step_kernel<fused, N=64, bf16> (81 launches, summed)", fb,
                                fk["ms_per_step"])
     out["cpu_baseline"] = None
+    if args.cpu_baseline_seconds > 0:
+        # one layer unit x 64 ranks on the CPU, extrapolated to the 81 units
+        s0 = q[0]["shard_len"]
+        out["cpu_baseline"] = cpu_baseline(w, grads, master, s0, r, args.cpu_baseline_seconds,
+                                           what="rank-{r} shard of layer unit 0", total=S)
     return out
 
 
@@ -597,10 +602,12 @@ def counter_traffic(path=COUNTERS, src=KERNELS_SRC, sha_key="kernels_hip_sha256"
         return None
 
 
-def cpu_baseline(w, grads, master, S, r, budget_s):
+def cpu_baseline(w, grads, master, S, r, budget_s, what="rank-{r} shard", total=None):
     """The oracle, single-threaded, on the first elements of the same shard:
     16M-element chunks are copied from the GPU and stepped (step 1) until the
-    oracle has run for `budget_s` seconds; only oracle time is counted."""
+    oracle has run for `budget_s` seconds or the S elements are done; only
+    oracle time is counted.  With `total`, the sample is one part of a
+    `total`-element shard and the time for all of it is extrapolated."""
     import numpy as np
 
     from oracle import _c
@@ -620,10 +627,14 @@ def cpu_baseline(w, grads, master, S, r, budget_s):
         _c.rank_step(hp, g, 1.0, p, m, v, out, tmp)
         spent += time.perf_counter() - t0
         done += n
+    sample = (f"first {done} of {S} elements of the {what.format(r=r)}, step 1, "
+              f"{chunk}-element chunks, {spent:.1f} s of oracle time "
+              f"(reduce {len(grads)} bf16 ranks + Adam + bf16 cast)")
+    if total:
+        sample += (f"; the whole {total}-element shard would take {spent * total / done:.1f} s "
+                   f"(extrapolated)")
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {done} of {S} elements of the rank-{r} shard, step 1, "
-                      f"{chunk}-element chunks, {spent:.1f} s of oracle time "
-                      f"(reduce 8 bf16 ranks + Adam + bf16 cast)"}
+            "sample": sample}
 
 
 def main():
