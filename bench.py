@@ -58,7 +58,7 @@ def parse():
                     help="config 2 only: the exact Mistral-7B per-parameter dim-0 layout "
                          "(291 parameters) instead of one flat unit")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=12.0,
-                    help="oracle time budget for the CPU baseline (headline only); 0 skips it")
+                    help="oracle time budget for the CPU baseline (headline and --config 4); 0 skips it")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
