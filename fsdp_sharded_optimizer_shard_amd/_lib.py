@@ -131,10 +131,16 @@ def _check(status: int, fn: str) -> None:
 
 
 def _addr(x) -> Optional[int]:
+    """Device address of a buffer: None, a raw int address, or a tensor that
+    lives on the GPU (a host tensor's pointer would fault inside a kernel,
+    so it is refused here)."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
+    if getattr(x, "is_cuda", True) is False:
+        raise ValueError("buffers passed to libzeroshard must be GPU tensors (got one on "
+                         f"{getattr(x, 'device', 'the host')})")
     return x.data_ptr()
 
 
@@ -161,9 +167,9 @@ class Layout:
         return self._h
 
     def destroy(self) -> None:
-        if self._h:
+        if self._h and _lib is not None:   # _lib may already be gone at exit
             _lib.zero_shard_destroy(self._h)
-            self._h = None
+        self._h = None
 
     __del__ = destroy
 

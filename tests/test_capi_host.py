@@ -295,3 +295,14 @@ def test_gemm_and_linear_validation_launches_nothing():
                 FAKE, stream=0).status == zs.ERR_INVALID_ARG
     assert _err(zs.fsdp_linear_forward, L, 1, [FAKE] * 4, 8, FAKE, FAKE, FAKE, stream=0).status == \
         zs.ERR_INVALID_ARG
+
+
+def test_host_tensors_are_refused_before_any_call():
+    import torch
+    L = zs.shard_init("zero2", 4, 0, [1024])
+    host = torch.zeros(256)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        zs.adam_step(L, 0, 1, zs.adam_cfg(step=1), host, host, host, host, stream=0,
+                     grad_fp32=host)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        zs.grad_accumulate(host, host, 16, stream=0)
