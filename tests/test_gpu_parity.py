@@ -12,8 +12,9 @@ Small cases span several 2048-element tiles, ragged tails, zero padding,
 slices that are not multiples of 8 (scalar path), N in {1, 2, 3, 4, 5, 8,
 64}, bf16 and fp32 gradients, full- and shard-indexed rank buffers, AdamW and
 L2 decay, whole-range and per-unit calls.  The full-size 7B / N = 8 shard
-is checked on sampled elements after 3 steps, in the launch configuration
-the benchmark times.
+is checked after 3 steps in the launch configuration the benchmark times:
+on sampled elements (with the gather into the 7.24e9-element buffer), and
+element by element over all 905,000,000 elements.
 """
 import numpy as np
 import pytest
@@ -408,3 +409,50 @@ def test_config2_full_size_sampled():
         got = host_bf16(full[q * S + tidx])
         want = par_h if q == r else np.full(idx.size, q + 1, np.uint16)
         assert np.array_equal(got, want), f"gather slot {q}"
+
+
+def test_config2_full_shard_every_element():
+    """The same Mistral-7B rank shard (905,000,000 elements, N = 8, rank 7,
+    3 fused Adam steps), compared element by element over the whole shard:
+    the oracle steps every element from the same gradients, streamed from
+    the GPU in 32M-element chunks, and master, m, v and the bf16 shard must
+    be bit-identical everywhere."""
+    w = WORKLOADS[2]
+    n, r = w.n_ranks, w.n_ranks - 1
+    L = zs.shard_init("zero3", n, r, list(w.units))
+    S = L.shard_len
+    CH = 1 << 25
+    master = master_init(w, S, device=DEV, rank=r)
+    m = torch.zeros(S, device=DEV)
+    v = torch.zeros(S, device=DEV)
+    own = torch.empty(S, dtype=torch.int16, device=DEV)
+    p_h = master.cpu().numpy()
+    m_h = np.zeros(S, np.float32)
+    v_h = np.zeros(S, np.float32)
+    par_h = np.empty(S, np.uint16)
+    tmp = np.empty(CH, np.float32)
+    for t in range(w.steps):
+        grads = [grad_bits(w, t, q, S, device=DEV) for q in range(n)]
+        zs.adam_step(L, 0, 1, cfg_of(w, t + 1), master, m, v, own, zs.INDEX_SHARD,
+                     grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
+        hp = oracle_cfg(w).hparams(t + 1)
+        for off in range(0, S, CH):
+            k = min(CH, S - off)
+            g = [host_bf16(gq[off:off + k]) for gq in grads]
+            _c.rank_step(hp, g, 1.0, p_h[off:off + k], m_h[off:off + k], v_h[off:off + k],
+                         par_h[off:off + k], tmp[:k])
+        del grads
+    torch.cuda.synchronize()
+    bad = {}
+    for name, dev_t, want in (("master", master, p_h), ("m", m, m_h), ("v", v, v_h)):
+        nbad = 0
+        for off in range(0, S, CH):
+            got = host_f32(dev_t[off:off + CH])
+            nbad += int(np.count_nonzero(got.view(np.uint32) !=
+                                         want[off:off + CH].view(np.uint32)))
+        bad[name] = nbad
+    nbad = 0
+    for off in range(0, S, CH):
+        nbad += int(np.count_nonzero(host_bf16(own[off:off + CH]) != par_h[off:off + CH]))
+    bad["bf16 shard"] = nbad
+    assert not any(bad.values()), f"elements differing from the oracle: {bad}"
