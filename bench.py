@@ -54,6 +54,9 @@ def parse():
                     help="the hand-written FSDP linear layer (Mistral-7B MLP up projection, "
                          "in 4096, out 14336, 4096 tokens per rank, N=8, rank 7) instead of a "
                          "config")
+    ap.add_argument("--vs-library", action="store_true",
+                    help="with --fsdp-linear: also time the three GEMMs against torch.mm "
+                         "(hipBLASLt) on the same operands, alternately")
     ap.add_argument("--fsdp2", action="store_true",
                     help="config 2 only: the exact Mistral-7B per-parameter dim-0 layout "
                          "(291 parameters) instead of one flat unit")
@@ -563,7 +566,52 @@ def run_fsdp_linear(args, torch, zs, np):
                        "traffic_unit": "HBM bytes of the 10 GEMM launches of one step "
                                        "(rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
     out["cpu_baseline"] = None
+    if args.vs_library:
+        out["library_comparison"] = gemm_vs_library(torch, zs, xs[r], w_full, dys[r], y, dx,
+                                                    dws[r], batch, inf, outf)
     return out
+
+
+def gemm_vs_library(torch, zs, x, w, dy, y, dx, dw, batch, inf, outf, rounds=5, iters=10):
+    """The three GEMMs of the linear layer, timed alternately with
+    zero_gemm_bf16 and with torch.mm (hipBLASLt) on the same operands and
+    streams; TFLOP/s as mean (min-max) over the rounds."""
+    KI, KO = zs.K_INNER, zs.K_OUTER
+    xb, wb = x.view(torch.bfloat16).view(batch, inf), w.view(torch.bfloat16).view(inf, outf)
+    dyb = dy.view(torch.bfloat16).view(batch, outf)
+    yb, dxb = y.view(torch.bfloat16), dx.view(torch.bfloat16)
+    cases = {
+        "gemm_forward": (lambda: zs.gemm_bf16(batch, outf, inf, x, inf, KI, w, outf, KO, y, outf,
+                                              zs.BF16),
+                         lambda: torch.mm(xb, wb, out=yb)),
+        "gemm_dx": (lambda: zs.gemm_bf16(batch, inf, outf, dy, outf, KI, w, outf, KI, dx, inf,
+                                         zs.BF16),
+                    lambda: torch.mm(dyb, wb.t(), out=dxb)),
+        "gemm_dw": (lambda: zs.gemm_bf16(inf, outf, batch, x, inf, KO, dy, outf, KO, dw, outf,
+                                         zs.FP32),
+                    lambda: torch.mm(xb.t(), dyb, out_dtype=torch.float32)),
+    }
+    flops = 2.0 * batch * inf * outf
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fns in cases.items():
+        tf = [[], []]
+        for f in fns:
+            f()
+        torch.cuda.synchronize()
+        for _ in range(rounds):
+            for i, f in enumerate(fns):
+                e0.record()
+                for _ in range(iters):
+                    f()
+                e1.record()
+                torch.cuda.synchronize()
+                tf[i].append(flops / (e0.elapsed_time(e1) / iters * 1e-3) / 1e12)
+        ours, lib = (sum(v) / len(v) for v in tf)
+        res[name] = {"ours_tflops": ours, "ours_range": [min(tf[0]), max(tf[0])],
+                     "torch_mm_tflops": lib, "torch_mm_range": [min(tf[1]), max(tf[1])],
+                     "ours_over_torch_mm": ours / lib}
+    return res
 
 
 def calibrate_copy(args, torch, zs, np):
@@ -643,6 +691,10 @@ def main():
         print("bench.py measures one GPU only: this build simulates the N data-parallel ranks "
               "inside one GPU's memory and has no multi-GPU path; run with --gpus 1.",
               file=sys.stderr)
+        sys.exit(2)
+
+    if args.vs_library and not args.fsdp_linear:
+        print("--vs-library applies to --fsdp-linear only.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

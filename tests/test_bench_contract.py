@@ -1,6 +1,7 @@
 """The parts of bench.py's contract that need no GPU: a request for more
-than one GPU (by flag or by a launcher's WORLD_SIZE) exits at once with a
-message and a non-zero status, before torch or the library is touched."""
+than one GPU (by flag or by a launcher's WORLD_SIZE), or for the library
+comparison outside the linear-layer workload, exits at once with a message
+and a non-zero status, before torch or the library is touched."""
 import os
 import subprocess
 import sys
@@ -24,3 +25,8 @@ def test_more_than_one_gpu_is_refused():
 def test_launcher_world_size_is_refused():
     r = _run(["--steps", "1"], {"WORLD_SIZE": "4", "RANK": "0", "LOCAL_RANK": "0"})
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_library_comparison_needs_the_linear_workload():
+    r = _run(["--vs-library", "--steps", "1"])
+    assert r.returncode == 2 and "--fsdp-linear" in r.stderr and r.stdout == ""
