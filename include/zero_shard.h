@@ -329,8 +329,11 @@ typedef enum {
    kernel's own order (error within the usual gamma_K bound of fp32 dot
    products).  Needs K, lda and ldb multiples of 8, M (N) a multiple of 8
    when A (B) is K_OUTER, lda >= K or M and ldb >= K or N by order,
-   ldc >= N, and 16-byte aligned A and B; ZERO_ERR_UNSUPPORTED or
-   ZERO_ERR_ALIGNMENT otherwise, with nothing launched.  M = 0 or N = 0 is
+   ldc >= N, and 16-byte aligned A and B.  Operands are read through 32-bit
+   buffer offsets, so a K_INNER operand's leading dimension must be at most
+   2^22 = 4,194,304 elements and a K_OUTER one's at most 2^25 = 33,554,432.
+   ZERO_ERR_UNSUPPORTED or ZERO_ERR_ALIGNMENT otherwise, with nothing
+   launched.  M = 0 or N = 0 is
    a no-op; K = 0 writes zeros.  All pointers are device memory owned by the
    caller. */
 zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A,

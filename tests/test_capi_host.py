@@ -280,6 +280,19 @@ def test_gemm_and_linear_validation_launches_nothing():
     assert _err(g, 16, 16, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE + 2, 16).status == \
         zs.ERR_ALIGNMENT
     assert _err(g, 16, 16, 16, None, 16, KI, FAKE, 16, KI, FAKE, 16).status == zs.ERR_INVALID_ARG
+    # operands are read through 32-bit offsets: K-inner ld <= 2^22, K-outer ld <= 2^25
+    big_ki, big_ko = (1 << 22) + 8, (1 << 25) + 8
+    e = _err(g, 16, 16, 16, FAKE, big_ki, KI, FAKE, 16, KI, FAKE, 16)
+    assert e.status == zs.ERR_UNSUPPORTED and "32-bit" in str(e)
+    assert _err(g, 16, 16, 16, FAKE, 16, KI, FAKE, big_ki, KI, FAKE, 16).status == \
+        zs.ERR_UNSUPPORTED
+    assert _err(g, 16, 16, 16, FAKE, big_ko, KO, FAKE, 16, KI, FAKE, 16).status == \
+        zs.ERR_UNSUPPORTED
+    assert _err(g, 16, 16, 16, FAKE, 16, KI, FAKE, big_ko, KO, FAKE, 16).status == \
+        zs.ERR_UNSUPPORTED
+    # at the limits the checks pass (then the misaligned C is what is refused)
+    assert _err(g, 16, 16, 16, FAKE, 1 << 22, KI, FAKE, 1 << 25, KO, FAKE + 2, 16).status == \
+        zs.ERR_ALIGNMENT
     # empty outputs launch nothing
     g(0, 16, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE, 16)
     g(16, 0, 16, FAKE, 16, KO, FAKE, 16, KO, FAKE, 16)

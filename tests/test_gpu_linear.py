@@ -73,11 +73,14 @@ ORDERS = [(0, 0), (1, 0), (0, 1), (1, 1)]
 @pytest.mark.parametrize("ao,bo", ORDERS)
 @pytest.mark.parametrize("M,N,K,pad", [(8, 8, 8, 0), (200, 312, 72, 8), (264, 520, 200, 16),
                                        (520, 256, 1096, 0), (3104, 2904, 136, 8),
-                                       (2040, 9448, 72, 0)])
+                                       (2040, 9448, 72, 0), (256, 264, 40, 0),
+                                       (136, 256, 256, 8), (272, 528, 1024, 0)])
 def test_gemm_operand_orders_within_fp32_bound(ao, bo, M, N, K, pad):
     """Every operand order (K-inner: stored rows x K; K-outer: stored K x
-    rows), ragged in M, N and K (several 256-tiles, K past a 64 multiple),
-    with leading dimensions wider than the matrix.  On a 256-CU part the
+    rows), ragged in M, N and K, with leading dimensions wider than the
+    matrix.  K runs through 1, 2, 3, 5, 7, 8, 32 and 35 stages of 32, with
+    and without a partial last stage; 256 and 1024 end on whole stages, and
+    1024 and 1096 run the four-stage steady loop.  On a 256-CU part the
     small shapes run as 128 x 256 half tiles only, 3104 x 2904 (156 tiles)
     as whole tiles only, and 2040 x 9448 (296 tiles) as one wave of whole
     tiles plus 80 half tiles."""
