@@ -10,11 +10,12 @@
 //   zero_gemm_bf16_nt:  the K-inner / K-inner case.
 //   zero_transpose_bf16: dst[c][r] = src[r][c].
 //
-// GEMM tiling.  A 256-thread block (4 waves, one per SIMD) owns a 256 x 256
-// tile of C; each wave owns 128 x 128 as 4 x 4 tiles of
-// v_mfma_f32_32x32x16_bf16, so its 256 fp32 accumulators per lane live in
-// the accumulation registers.  K advances 32 at a time through four LDS
-// stages of 256 x 32 bf16 per operand (128 KB in all).
+// GEMM tiling.  A 512-thread block (8 waves, two per SIMD) owns a 256 x 256
+// tile of C; each wave owns 64 x 128 as 2 x 4 tiles of
+// v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane), so while one
+// wave of a SIMD waits on its fragment reads the other issues MFMAs.  K
+// advances 32 at a time through four LDS stages of 256 x 32 bf16 per
+// operand (128 KB in all).
 //
 // Loads.  Operands go from HBM straight into LDS with buffer_load ... lds
 // (16 bytes per lane, 1 KB per wave instruction): no register staging and
@@ -40,8 +41,9 @@
 // tile k + 1's first substep.  sched_group_barrier fixes that interleave.
 // Measured against the previous design (register staging, two 64-k LDS
 // buffers, one tile ahead), paired on the Mistral-7B MLP shapes with random
-// operands: dX +8.5 %, forward +4.2 %, dW +6.7 %, 8192^3 +9.1 %, with
-// bit-identical results.
+// operands: dX +8.5 %, forward +4.2 %, dW +6.7 %, 8192^3 +9.1 %; then eight
+// waves instead of four (128 x 128 each): dX +4.9 %, forward +15 %, dW +9 %.
+// Every step gave bit-identical results.
 //
 // Tile order.  Block b runs on XCD b % 8; each XCD gets a contiguous range of
 // tiles, walked 4 tile rows at a time, so the blocks that share an L2 share
@@ -62,7 +64,8 @@
 namespace zs {
 namespace {
 
-constexpr int kGT = 256;  // threads per GEMM block
+constexpr int kNW = 8;          // waves per GEMM block: two per SIMD
+constexpr int kGT = 64 * kNW;   // threads per GEMM block
 constexpr int kBM = 256, kBN = 256, kBK = 32;
 constexpr int kStages = 4;                 // LDS stages of kBK
 constexpr int kStage = kBM * kBK * 2;      // bytes of one operand's stage
@@ -127,9 +130,9 @@ __device__ __forceinline__ void seq()
     }
 }
 
-// One operand's R x 32 stage.  Each wave issues R / 64 DMA instructions of
-// 1 KB; instruction n of wave w fills stage bytes [1024 I, 1024 I + 1024),
-// I = w + 4 n, lane l landing at 16 l.
+// One operand's R x 32 stage.  Each of the 8 waves issues R / 128 DMA
+// instructions of 1 KB; instruction n of wave w fills stage bytes
+// [1024 I, 1024 I + 1024), I = w + 8 n, lane l landing at 16 l.
 //   K-inner (rows of 64 B): rows 16 I .. +15; lane l takes row 16 I + l / 4
 //     and stage slot l % 4, which holds k chunk slot ^ ((row >> 2) & 3).
 //   K-outer (k-major, 2R bytes per k row): KPI = 1024 / 2R k rows per
@@ -140,7 +143,7 @@ __device__ __forceinline__ void seq()
 //     halves of the banks (2-way conflicts without the last term).
 template <int R, bool KOUTER>
 struct Op {
-    static constexpr int NI = R / 64;                  // DMA instructions per wave per stage
+    static constexpr int NI = R / (16 * kNW);          // DMA instructions per wave per stage
     static constexpr int KPI = 1024 / (2 * R);         // K-outer: k rows per instruction
     static constexpr int NRD = KOUTER ? 2 : 1;         // LDS reads per fragment
 };
@@ -156,7 +159,7 @@ __device__ __forceinline__ int unit_at(int pos, int kr)
 template <int R, bool KOUTER>
 __device__ __forceinline__ uint32_t dma_offset(int64_t ld, int wave, int lane, int n)
 {
-    const int I = wave + 4 * n;
+    const int I = wave + kNW * n;
     if (!KOUTER) {
         const int r = 16 * I + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
         return (uint32_t)((r * ld + 8 * c) * 2);
@@ -170,7 +173,7 @@ __device__ __forceinline__ uint32_t dma_offset(int64_t ld, int wave, int lane, i
 // The k offset within the stage of a K-inner lane's chunk (for the K tail).
 __device__ __forceinline__ int dma_kofs(int wave, int lane, int n)
 {
-    const int r = 16 * (wave + 4 * n) + (lane >> 2);
+    const int r = 16 * (wave + kNW * n) + (lane >> 2);
     return 8 * ((lane & 3) ^ ((r >> 2) & 3));
 }
 
@@ -224,8 +227,9 @@ __device__ __forceinline__ void grouped(int logical, int tiles_m, int tiles_n, i
     tn = in_g / gm;
 }
 
-// One BM x 256 tile of C (BM = 256, or 128 for half tiles): 4 waves, each
-// (BM / 2) x 128 as (BM / 64) x 4 MFMA tiles, over K stages of 32 (two
+// One BM x 256 tile of C (BM = 256, or 128 for half tiles): 8 waves in a
+// 4 x 2 grid, each (BM / 4) x 128 as (BM / 128) x 4 MFMA tiles, over K
+// stages of 32 (two
 // substeps of 16).  Tile kt lives in LDS stage kt % 4; its DMA went out at
 // the start of tile kt - 3, so three tiles of loads are in flight and no
 // register staging or LDS write instruction is involved.
@@ -237,7 +241,7 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
                                           ZS_LDS char *const (&As)[kStages],
                                           ZS_LDS char *const (&Bs)[kStages])
 {
-    constexpr int TM = BM / 64, TN = 4;  // 32 x 32 MFMA tiles per wave
+    constexpr int TM = BM / (16 * kNW), TN = 4;  // 32 x 32 MFMA tiles per wave
     constexpr int NF = TM + TN;          // fragments per substep
     constexpr int NMF = TM * TN;         // MFMAs per substep
     constexpr int NRD = TM * Op<BM, A_KOUTER>::NRD + TN * Op<kBN, B_KOUTER>::NRD;
@@ -245,7 +249,7 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
     constexpr int D = NIA + NIB;         // DMA instructions per wave per tile
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * (BM / 2), wn = (wave & 1) * (kBN / 2);
+    const int wm = (wave >> 1) * (BM / (kNW / 2)), wn = (wave & 1) * (kBN / 2);
     const int fr = lane & 31, fh = lane >> 5;
 
     uint32_t va[4], vb[4];
@@ -297,13 +301,13 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
 #pragma unroll
         for (int n = 0; n < NIA; ++n) {
             const uint32_t o = !WHOLE && !A_KOUTER && k0 + ka[n] >= K ? kOOB : va[n];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (ZS_LDS void *)(As[S] + (wave + 4 * n) * 1024),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (ZS_LDS void *)(As[S] + (wave + kNW * n) * 1024),
                                                      16, o, 0, 0, 0);
         }
 #pragma unroll
         for (int n = 0; n < NIB; ++n) {
             const uint32_t o = !WHOLE && !B_KOUTER && k0 + kb[n] >= K ? kOOB : vb[n];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ZS_LDS void *)(Bs[S] + (wave + 4 * n) * 1024),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ZS_LDS void *)(Bs[S] + (wave + kNW * n) * 1024),
                                                      16, o, 0, 0, 0);
         }
     };
