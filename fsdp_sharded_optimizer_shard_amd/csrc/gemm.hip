@@ -11,7 +11,7 @@
 //   zero_transpose_bf16: dst[c][r] = src[r][c].
 //
 // GEMM tiling.  A 512-thread block (8 waves, two per SIMD) owns a 256 x 256
-// tile of C; each wave owns 64 x 128 as 2 x 4 tiles of
+// tile of C; each wave owns 128 x 64 as 4 x 2 tiles of
 // v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane), so while one
 // wave of a SIMD waits on its fragment reads the other issues MFMAs.  K
 // advances 32 at a time through four LDS stages of 256 x 32 bf16 per
@@ -42,8 +42,9 @@
 // Measured against the previous design (register staging, two 64-k LDS
 // buffers, one tile ahead), paired on the Mistral-7B MLP shapes with random
 // operands: dX +8.5 %, forward +4.2 %, dW +6.7 %, 8192^3 +9.1 %; then eight
-// waves instead of four (128 x 128 each): dX +4.9 %, forward +15 %, dW +9 %.
-// Every step gave bit-identical results.
+// waves instead of four (128 x 128 each): dX +4.9 %, forward +15 %, dW +9 %;
+// a 2 x 4 wave grid (128 x 64 per wave) rather than 4 x 2 adds about 1 %
+// and needs no register spills.  Every step gave bit-identical results.
 //
 // Tile order.  Block b runs on XCD b % 8; each XCD gets a contiguous range of
 // tiles, walked 4 tile rows at a time, so the blocks that share an L2 share
@@ -228,7 +229,7 @@ __device__ __forceinline__ void grouped(int logical, int tiles_m, int tiles_n, i
 }
 
 // One BM x 256 tile of C (BM = 256, or 128 for half tiles): 8 waves in a
-// 4 x 2 grid, each (BM / 4) x 128 as (BM / 128) x 4 MFMA tiles, over K
+// 2 x 4 grid, each (BM / 2) x 64 as (BM / 64) x 2 MFMA tiles, over K
 // stages of 32 (two
 // substeps of 16).  Tile kt lives in LDS stage kt % 4; its DMA went out at
 // the start of tile kt - 3, so three tiles of loads are in flight and no
@@ -241,7 +242,7 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
                                           ZS_LDS char *const (&As)[kStages],
                                           ZS_LDS char *const (&Bs)[kStages])
 {
-    constexpr int TM = BM / (16 * kNW), TN = 4;  // 32 x 32 MFMA tiles per wave
+    constexpr int TM = BM / 64, TN = 2;  // 32 x 32 MFMA tiles per wave
     constexpr int NF = TM + TN;          // fragments per substep
     constexpr int NMF = TM * TN;         // MFMAs per substep
     constexpr int NRD = TM * Op<BM, A_KOUTER>::NRD + TN * Op<kBN, B_KOUTER>::NRD;
@@ -249,7 +250,7 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
     constexpr int D = NIA + NIB;         // DMA instructions per wave per tile
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = (wave >> 1) * (BM / (kNW / 2)), wn = (wave & 1) * (kBN / 2);
+    const int wm = (wave >> 2) * (BM / 2), wn = (wave & 3) * (kBN / 4);
     const int fr = lane & 31, fh = lane >> 5;
 
     uint32_t va[4], vb[4];
