@@ -28,7 +28,7 @@
 // LDS layouts.  A K-inner stage has 64-byte rows (32 k); 16-byte chunk c of
 // row r sits at slot c ^ ((r >> 2) & 3), which keeps the fragment reads
 // (ds_read_b128) free of bank conflicts.  A K-outer stage is k-major (one
-// 2R-byte row per k); its 32-byte units are permuted by k row & 3, and a
+// 2R-byte row per k); its 32-byte units are permuted per k row (unit_pos), and a
 // fragment is two ds_read_b64_tr_b16 that transpose 4 x 4 blocks of 16-bit
 // values across each 16-lane group.  A DMA lane's global address is chosen
 // so that it lands in the swizzled slot.  Both layouts read without bank
@@ -49,6 +49,9 @@
 // Tile order.  Block b runs on XCD b % 8; each XCD gets a contiguous range of
 // tiles, walked 4 tile rows at a time, so the blocks that share an L2 share
 // A rows and B columns.
+//
+// Both operands K-inner (dY W^T): the same pipeline on 16x16x32 MFMAs
+// (gemm_tile16) with its own chunk swizzle, about 6 % faster there.
 //
 // MFMA 32x32x16 bf16 lane layout (checked on the device against an exact
 // CPU product): lane l holds A row (l % 32), k = 8 (l / 32) .. +7, and B
@@ -92,8 +95,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// K-inner stage: byte offset of the 16-byte chunk c (of 4) of row r.
-__device__ __forceinline__ int ki_pos(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// K-inner stage: byte offset of the 16-byte chunk c (of 4) of row r, under
+// the chunk swizzle of the MFMA shape that reads it: (r >> 2) & 3 for the
+// 32x32x16 fragments (SW = 0), (r >> 1) & 3 for the 16x16x32 ones (SW = 1).
+// Each is free of bank conflicts for its own reads and not for the other's
+// (rocprofv3: 44 M and 29 M conflict cycles per launch the wrong way round).
+template <int SW>
+__device__ __forceinline__ int ki_swz(int r) { return SW ? (r >> 1) & 3 : (r >> 2) & 3; }
+template <int SW = 0>
+__device__ __forceinline__ int ki_pos(int r, int c) { return r * 64 + ((c ^ ki_swz<SW>(r)) << 4); }
 
 // Buffer descriptor over `bytes` bytes from `base` (clamped to 2^31 - 1;
 // the host bounds every offset below that).
@@ -157,12 +167,12 @@ __device__ __forceinline__ int unit_at(int pos, int kr)
     return x ^ ((x & 1) << 2);
 }
 
-template <int R, bool KOUTER>
+template <int R, bool KOUTER, int SW = 0>
 __device__ __forceinline__ uint32_t dma_offset(int64_t ld, int wave, int lane, int n)
 {
     const int I = wave + kNW * n;
     if (!KOUTER) {
-        const int r = 16 * I + (lane >> 2), c = (lane & 3) ^ ((r >> 2) & 3);
+        const int r = 16 * I + (lane >> 2), c = (lane & 3) ^ ki_swz<SW>(r);
         return (uint32_t)((r * ld + 8 * c) * 2);
     }
     constexpr int KPI = Op<R, true>::KPI, LPR = 64 / KPI;  // lanes per k row
@@ -172,10 +182,11 @@ __device__ __forceinline__ uint32_t dma_offset(int64_t ld, int wave, int lane, i
 }
 
 // The k offset within the stage of a K-inner lane's chunk (for the K tail).
+template <int SW = 0>
 __device__ __forceinline__ int dma_kofs(int wave, int lane, int n)
 {
     const int r = 16 * (wave + kNW * n) + (lane >> 2);
-    return 8 * ((lane & 3) ^ ((r >> 2) & 3));
+    return 8 * ((lane & 3) ^ ki_swz<SW>(r));
 }
 
 // First LDS read offset of the fragment of rows w0 .. w0 + 31 at k
@@ -421,6 +432,153 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
             }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The K-inner x K-inner tile on v_mfma_f32_16x16x32_bf16 (lane l: row l % 16,
+// k 8 (l / 16) .. +7; accumulator v: row 4 (l / 16) + v, column l % 16).  Each
+// wave owns (BM / 2) x 64 as (BM / 32) x 4 tiles of 16 x 16, one 32-k substep
+// per stage.  The wait and the barrier sit at the start of each tile, so the
+// next tile's fragments are read under all of this tile's MFMAs.  Its K-inner
+// stages use the SW = 1 chunk swizzle.  Paired against the 32x32x16 tile on
+// dX (4096 x 4096 x 14336, random operands): +4.4 %, and +1.8 % more with
+// that swizzle; bit-identical.  With a K-outer operand the 16x16x32 form was no
+// faster (forward 0.98 x) or spilled registers inside the loop (dW 0.60 x),
+// so those orders keep gemm_tile.
+template <int BM, bool OUT_BF16>
+__device__ __forceinline__ void gemm_tile16(int64_t M, int64_t N, int64_t K,
+                                            const uint16_t *__restrict__ A, int64_t lda,
+                                            const uint16_t *__restrict__ B, int64_t ldb,
+                                            void *__restrict__ C, int64_t ldc, int64_t m0, int64_t n0,
+                                            ZS_LDS char *const (&As)[kStages],
+                                            ZS_LDS char *const (&Bs)[kStages])
+{
+    constexpr int TM = BM / 32, TN = 4;
+    constexpr int NF = TM + TN, NMF = TM * TN;
+    constexpr int NIA = Op<BM, false>::NI, NIB = Op<kBN, false>::NI;
+    constexpr int D = NIA + NIB;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = (wave >> 2) * (BM / 2), wn = (wave & 3) * (kBN / 4);
+    const int r16 = lane & 15, g = lane >> 4;
+
+    uint32_t va[4], vb[4];
+    int ka[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        va[n] = n < NIA ? dma_offset<BM, false, 1>(lda, wave, lane, n) : 0u;
+        vb[n] = n < NIB ? dma_offset<kBN, false, 1>(ldb, wave, lane, n) : 0u;
+        ka[n] = dma_kofs<1>(wave, lane, n);
+    }
+    const int fa_off = ki_pos<1>(wm + r16, g), fb_off = ki_pos<1>(wn + r16, g);
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int64_t kt_n = (K + kBK - 1) / kBK, kt_full = K / kBK;
+    auto dma = [&](auto st, auto whole, int64_t kt) {
+        constexpr int S = decltype(st)::value;
+        constexpr bool WHOLE = decltype(whole)::value != 0;
+        const int64_t k0 = kt * kBK;
+        const __amdgpu_buffer_rsrc_t ra = rsrc(A + m0 * lda + k0, ((M - 1 - m0) * lda + K - k0) * 2);
+        const __amdgpu_buffer_rsrc_t rb = rsrc(B + n0 * ldb + k0, ((N - 1 - n0) * ldb + K - k0) * 2);
+#pragma unroll
+        for (int n = 0; n < NIA; ++n) {
+            const uint32_t o = !WHOLE && k0 + ka[n] >= K ? kOOB : va[n];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (ZS_LDS void *)(As[S] + (wave + kNW * n) * 1024), 16, o, 0, 0, 0);
+        }
+#pragma unroll
+        for (int n = 0; n < NIB; ++n) {
+            const uint32_t o = !WHOLE && k0 + ka[n] >= K ? kOOB : vb[n];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ZS_LDS void *)(Bs[S] + (wave + kNW * n) * 1024), 16, o, 0, 0, 0);
+        }
+    };
+    bf16x8 fa[2][TM], fb[2][TN];
+    auto frags = [&](auto st, auto set) {
+        constexpr int S = decltype(st)::value, F = decltype(set)::value;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[F][j] = *reinterpret_cast<const ZS_LDS bf16x8 *>(Bs[S] + fb_off + j * 1024);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[F][i] = *reinterpret_cast<const ZS_LDS bf16x8 *>(As[S] + fa_off + i * 1024);
+    };
+    auto mma = [&](auto set) {
+        constexpr int F = decltype(set)::value;
+#pragma unroll
+        for (int q = 0; q < NMF; ++q)
+            acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[F][q / TN], fb[F][q % TN], acc[q / TN][q % TN], 0, 0, 0);
+    };
+    auto tile = [&](auto st, auto set, auto steady, int64_t kt) {
+        constexpr int S = decltype(st)::value, F = decltype(set)::value;
+        constexpr bool STEADY = decltype(steady)::value != 0;
+        constexpr int SN = (S + kStages - 1) % kStages, S1 = (S + 1) % kStages;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (STEADY) {
+            wait_vm_lgkm0<D>();
+        } else {
+            if (kt + 2 < kt_n) wait_vm_lgkm0<D>();
+            else wait_vm_lgkm0<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (STEADY)
+            dma(IC<SN>{}, IC<1>{}, kt + kStages - 1);
+        else if (kt + kStages - 1 < kt_n)
+            dma(IC<SN>{}, IC<0>{}, kt + kStages - 1);
+        if (STEADY || kt + 1 < kt_n)
+            frags(IC<S1>{}, IC<F ^ 1>{});
+        mma(IC<F>{});
+        if constexpr (STEADY)
+            seq<NF, NMF, NF, D>();
+        else
+            seq<NF, NMF, NF, 0>();
+    };
+    if (kt_n > 0) {
+        dma(IC<0>{}, IC<0>{}, 0);
+        if (kt_n > 1) dma(IC<1>{}, IC<0>{}, 1);
+        if (kt_n > 2) dma(IC<2>{}, IC<0>{}, 2);
+        {
+            const int64_t after = kt_n - 1;
+            if (after >= 2) wait_vm_lgkm0<2 * D>();
+            else if (after == 1) wait_vm_lgkm0<D>();
+            else wait_vm_lgkm0<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+        frags(IC<0>{}, IC<0>{});
+        int64_t kt = 0;
+        for (; kt + 2 * kStages - 1 <= kt_full; kt += kStages) {
+            tile(IC<0>{}, IC<0>{}, IC<1>{}, kt);
+            tile(IC<1>{}, IC<1>{}, IC<1>{}, kt + 1);
+            tile(IC<2>{}, IC<0>{}, IC<1>{}, kt + 2);
+            tile(IC<3>{}, IC<1>{}, IC<1>{}, kt + 3);
+        }
+        for (; kt < kt_n; kt += kStages) {
+            tile(IC<0>{}, IC<0>{}, IC<0>{}, kt);
+            if (kt + 1 < kt_n) tile(IC<1>{}, IC<1>{}, IC<0>{}, kt + 1);
+            if (kt + 2 < kt_n) tile(IC<2>{}, IC<0>{}, IC<0>{}, kt + 2);
+            if (kt + 3 < kt_n) tile(IC<3>{}, IC<1>{}, IC<0>{}, kt + 3);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int64_t row = m0 + wm + 16 * i + 4 * g + v;
+                const int64_t col = n0 + wn + 16 * j + r16;
+                if (row < M && col < N) {
+                    if (OUT_BF16)
+                        static_cast<uint16_t *>(C)[row * ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+                    else
+                        static_cast<float *>(C)[row * ldc + col] = acc[i][j][v];
+                }
+            }
+}
+
 // Blocks [0, n_big) compute whole 256 x 256 tiles (big tiles 0 .. n_big-1 in
 // grouped order); the remaining blocks split the last big tiles into
 // 128 x 256 halves, two blocks per tile, so a partial last wave of big
@@ -444,14 +602,23 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t
     int tm, tn;
     if (b < n_big) {
         grouped(xcd_order(b, n_big), tiles_m, tiles_n, tm, tn);
-        gemm_tile<kBM, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc,
-                                                     (int64_t)tm * kBM, (int64_t)tn * kBN, As, Bs);
+        if constexpr (!A_KOUTER && !B_KOUTER)
+            gemm_tile16<kBM, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, (int64_t)tm * kBM,
+                                       (int64_t)tn * kBN, As, Bs);
+        else
+            gemm_tile<kBM, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc,
+                                                         (int64_t)tm * kBM, (int64_t)tn * kBN, As,
+                                                         Bs);
     } else {
         const int h = xcd_order(b - n_big, (int)gridDim.x - n_big);
         grouped(n_big + h / 2, tiles_m, tiles_n, tm, tn);
-        gemm_tile<kBM / 2, A_KOUTER, B_KOUTER, OUT_BF16>(
-            M, N, K, A, lda, B, ldb, C, ldc, (int64_t)tm * kBM + (h & 1) * (kBM / 2),
-            (int64_t)tn * kBN, As, Bs);
+        const int64_t hm0 = (int64_t)tm * kBM + (h & 1) * (kBM / 2);
+        if constexpr (!A_KOUTER && !B_KOUTER)
+            gemm_tile16<kBM / 2, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, hm0,
+                                           (int64_t)tn * kBN, As, Bs);
+        else
+            gemm_tile<kBM / 2, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, hm0,
+                                                             (int64_t)tn * kBN, As, Bs);
     }
 }
 
