@@ -83,6 +83,8 @@ _lib.zero_adam_step.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _P, _I3
 _lib.zero_adam_step.restype = _I32
 _lib.zero_gather_params.argtypes = [_P, _I32, _I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P]
 _lib.zero_gather_params.restype = _I32
+
+
 class _UnitIO(ctypes.Structure):
     _fields_ = [("rank_grads", ctypes.POINTER(ctypes.c_void_p)),
                 ("peer_shards", ctypes.POINTER(ctypes.c_void_p)), ("unit_full", _P)]
@@ -111,9 +113,10 @@ _lib.zero_status_str.restype = ctypes.c_char_p
 _lib.zero_last_error.argtypes = []
 _lib.zero_last_error.restype = ctypes.c_char_p
 
-EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy", "zero_layout_info", "zero_layout_query",
-           "zero_reduce_shard", "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
-           "zero_gather_params", "zero_grad_accumulate", "zero_fsdp_sweep", "zero_gemm_bf16", "zero_gemm_bf16_nt",
+EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy",
+           "zero_layout_info", "zero_layout_query", "zero_reduce_shard",
+           "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step", "zero_gather_params",
+           "zero_grad_accumulate", "zero_fsdp_sweep", "zero_gemm_bf16", "zero_gemm_bf16_nt",
            "zero_transpose_bf16", "zero_fsdp_linear_forward", "zero_fsdp_linear_backward",
            "zero_status_str", "zero_last_error")
 
@@ -280,12 +283,32 @@ def gather_params(layout: Layout, unit_begin: int, unit_end: int, shards, param_
                                    _addr(param_full), _stream(stream)), "zero_gather_params")
 
 
+def _parts(layout: Layout) -> int:
+    """Slices per unit: world_n, or 1 for a DDP layout."""
+    i = layout.info()
+    return 1 if i["strategy"] == DDP else i["world_n"]
+
+
+def _need_len(what: str, seq, n: int) -> None:
+    # The library reads exactly n entries of these host arrays; a shorter
+    # list would have it read past the ctypes array.
+    if len(seq) != n:
+        raise ValueError(f"{what}: expected {n} entries, got {len(seq)}")
+
+
 def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, grad_dtype: int,
                units, master, m, v, max_inflight: int = 2, step_stream=None,
                gather_stream=None) -> None:
     """units: one (rank_grads, peer_shards, unit_full) per unit of the range;
-    rank_grads / peer_shards are lists of world_n buffers (None allowed in
-    peer_shards).  gather_stream defaults to step_stream (sequential)."""
+    rank_grads are world_n buffers and peer_shards one per slice (world_n,
+    or 1 under DDP; None allowed).  gather_stream defaults to step_stream
+    (sequential)."""
+    if 0 <= unit_begin <= unit_end:
+        _need_len("units", units, unit_end - unit_begin)
+        n, parts = layout.info()["world_n"], _parts(layout)
+        for grads, peers, _ in units:
+            _need_len("rank_grads", grads, n)
+            _need_len("peer_shards", peers, parts)
     keep = []
     arr = (_UnitIO * max(1, len(units)))()
     for i, (grads, peers, full) in enumerate(units):
@@ -323,6 +346,7 @@ def _ptrs(bufs):
 
 def fsdp_linear_forward(layout: Layout, unit: int, w_shards, batch: int, x, w_full, y,
                         y_dtype: int = BF16, stream=None) -> None:
+    _need_len("w_shards", w_shards, _parts(layout))
     _check(_lib.zero_fsdp_linear_forward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
                                          _addr(w_full), _addr(y), y_dtype, _stream(stream)),
            "zero_fsdp_linear_forward")
@@ -330,6 +354,7 @@ def fsdp_linear_forward(layout: Layout, unit: int, w_shards, batch: int, x, w_fu
 
 def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy, w_full, dx,
                          dw_full, dx_dtype: int = BF16, stream=None) -> None:
+    _need_len("w_shards", w_shards, _parts(layout))
     _check(_lib.zero_fsdp_linear_backward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
                                           _addr(dy), _addr(w_full), _addr(dx), dx_dtype,
                                           _addr(dw_full), _stream(stream)),

@@ -736,13 +736,17 @@ zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, i
         return fail(ZERO_ERR_UNSUPPORTED, "leading dimension too large for 32-bit operand offsets "
                     "(lda %lld, ldb %lld; K-inner at most %lld, K-outer at most %lld)",
                     (long long)lda, (long long)ldb, (long long)ki_max, (long long)ko_max);
+    // The dispatch counts the grid in work-items, 32 bits wide, and the grid
+    // has up to two blocks per tile.
+    const int64_t tm = (M + zs::kBM - 1) / zs::kBM, tn = (N + zs::kBN - 1) / zs::kBN;
+    constexpr int64_t kMaxTiles = int64_t(0xffffffffu) / (2 * zs::kGT);
+    if (tm > kMaxTiles / tn)
+        return fail(ZERO_ERR_UNSUPPORTED, "too many GEMM tiles for one launch (%lld x %lld)",
+                    (long long)tm, (long long)tn);
     if (!zs::a16(A) || !zs::a16(B))
         return fail(ZERO_ERR_ALIGNMENT, "A and B must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(C) % (c_dtype == ZERO_BF16 ? 2 : 4))
         return fail(ZERO_ERR_ALIGNMENT, "C is misaligned");
-    const int64_t tm = (M + zs::kBM - 1) / zs::kBM, tn = (N + zs::kBN - 1) / zs::kBN;
-    if (tm > INT_MAX / 2 / tn)
-        return fail(ZERO_ERR_UNSUPPORTED, "too many GEMM tiles for one launch");
     // One block per CU at a time (128 KB of LDS).  A last wave of at most
     // half the CUs runs as twice as many half tiles.
     const int64_t T = tm * tn, P = zs::cu_count();
@@ -789,7 +793,8 @@ zero_status zero_transpose_bf16(int64_t rows, int64_t cols, const uint16_t *src,
         return fail(ZERO_ERR_INVALID_ARG, "transpose needs src, dst, lds >= cols, ldd >= rows");
     if (reinterpret_cast<uintptr_t>(src) % 2 || reinterpret_cast<uintptr_t>(dst) % 2)
         return fail(ZERO_ERR_ALIGNMENT, "transpose buffers are misaligned");
-    if ((rows + zs::kTT - 1) / zs::kTT > 65535 || (cols + zs::kTT - 1) / zs::kTT > INT_MAX)
+    if ((rows + zs::kTT - 1) / zs::kTT > 65535 ||
+        (cols + zs::kTT - 1) / zs::kTT > int64_t(0xffffffffu) / 256)
         return fail(ZERO_ERR_UNSUPPORTED, "transpose too large for one launch");
     const dim3 grid((unsigned)((cols + zs::kTT - 1) / zs::kTT),
                     (unsigned)((rows + zs::kTT - 1) / zs::kTT));

@@ -599,17 +599,19 @@ int resident_blocks(Kernel kernel, int threads)
 }
 
 // `resident` (blocks of the kernel that fit on one CU) caps the persistent
-// width so a persistent grid is fully resident from the start.
-// Every kernel walks its tiles with a grid stride, so capping the width at
-// the largest grid dimension keeps any tile count launchable.
-constexpr int64_t kMaxGrid = 0x7fffffff;
-
-int64_t stream_grid(int64_t n_tiles, int resident)
+// width so a persistent grid is fully resident from the start.  The
+// dispatch packet counts a grid dimension in work-items, 32 bits wide, so
+// blocks x threads must stay below 2^32.  Every kernel walks its tiles with
+// a grid stride, so capping the width there keeps any tile count
+// launchable.
+int64_t stream_grid(int64_t n_tiles, int resident, int threads)
 {
     const int o = blocks_per_cu_override();
-    int64_t g = kMaxGrid;
-    if (o != 0)
-        g = (int64_t)device_cus() * (o < resident ? o : resident);
+    int64_t g = (int64_t)0xffffffffu / threads;
+    if (o != 0) {
+        const int64_t p = (int64_t)device_cus() * (o < resident ? o : resident);
+        g = p < g ? p : g;
+    }
     return n_tiles < g ? n_tiles : g;
 }
 
@@ -717,41 +719,40 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
     return s;
 }
 
-// grid > 0: that many blocks; grid == 0: the default launch width.
 template <int MODE, int NR, bool BF16>
-void launch_one(const StepArgs &a, int64_t grid, hipStream_t st)
+void launch_one(const StepArgs &a, hipStream_t st)
 {
     static const int resident = resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads);
-    const int64_t blocks = grid > 0 ? grid : stream_grid(a.n_tiles, resident);
+    const int64_t blocks = stream_grid(a.n_tiles, resident, kStepThreads);
     hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kStepThreads),
                        0, st, a);
 }
 
 template <int MODE, bool BF16>
-void launch_step(const StepArgs &a, int64_t grid, hipStream_t st)
+void launch_step(const StepArgs &a, hipStream_t st)
 {
     if constexpr (MODE == kApply) {
-        launch_one<kApply, 1, true>(a, grid, st);
+        launch_one<kApply, 1, true>(a, st);
     } else {
         switch (a.n_ranks) {
-        case 1: launch_one<MODE, 1, BF16>(a, grid, st); break;
-        case 2: launch_one<MODE, 2, BF16>(a, grid, st); break;
-        case 4: launch_one<MODE, 4, BF16>(a, grid, st); break;
-        case 8: launch_one<MODE, 8, BF16>(a, grid, st); break;
-        case 64: launch_one<MODE, 64, BF16>(a, grid, st); break;
-        default: launch_one<MODE, 0, BF16>(a, grid, st); break;
+        case 1: launch_one<MODE, 1, BF16>(a, st); break;
+        case 2: launch_one<MODE, 2, BF16>(a, st); break;
+        case 4: launch_one<MODE, 4, BF16>(a, st); break;
+        case 8: launch_one<MODE, 8, BF16>(a, st); break;
+        case 64: launch_one<MODE, 64, BF16>(a, st); break;
+        default: launch_one<MODE, 0, BF16>(a, st); break;
         }
     }
 }
 
 template <int MODE>
-zero_status launch_mode(StepArgs &a, bool bf16, int64_t grid, hipStream_t st)
+zero_status launch_mode(StepArgs &a, bool bf16, hipStream_t st)
 {
     (void)hipGetLastError();  // clear a stale error so the check below is ours
     if (MODE == kApply || bf16)
-        launch_step<MODE, true>(a, grid, st);
+        launch_step<MODE, true>(a, st);
     else
-        launch_step<MODE, false>(a, grid, st);
+        launch_step<MODE, false>(a, st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(ZERO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -816,8 +817,7 @@ zero_status zero_reduce_shard(const zero_layout *L, int32_t ub, int32_t ue,
         a.gout_full = out_index == ZERO_INDEX_FULL;
         a.partials = partials ? partials + poff : nullptr;
         poff += a.n_tiles;
-        return launch_mode<kReduce>(a, grads->dtype == ZERO_BF16, 0,
-                                    static_cast<hipStream_t>(stream));
+        return launch_mode<kReduce>(a, grads->dtype == ZERO_BF16, static_cast<hipStream_t>(stream));
     });
 }
 
@@ -898,8 +898,8 @@ zero_status zero_adam_step(const zero_layout *L, int32_t ub, int32_t ue,
         a.sc = sc;
         const hipStream_t s = static_cast<hipStream_t>(stream);
         if (grads)
-            return launch_mode<kFused>(a, grads->dtype == ZERO_BF16, 0, s);
-        return launch_mode<kApply>(a, true, 0, s);
+            return launch_mode<kFused>(a, grads->dtype == ZERO_BF16, s);
+        return launch_mode<kApply>(a, true, s);
     });
 }
 
@@ -962,8 +962,9 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
             // each block walking n_src tiles; a persistent override spreads
             // its width over the sources
             static const int resident = resident_blocks(gather_kernel, kGatherThreads);
-            int64_t gx = blocks_per_cu_override() == 0 ? stream_grid(tiles, resident)
-                                                      : stream_grid(tiles, resident) / a.n_src;
+            int64_t gx = blocks_per_cu_override() == 0
+                             ? stream_grid(tiles, resident, kGatherThreads)
+                             : stream_grid(tiles, resident, kGatherThreads) / a.n_src;
             gx = gx < 1 ? 1 : gx;
             (void)hipGetLastError();
             hipLaunchKernelGGL(gather_kernel, dim3((unsigned)gx, (unsigned)a.n_src),
@@ -989,7 +990,7 @@ zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro, int64_
         return ZERO_OK;
     const int64_t tiles = tiles_of(n);
     static const int resident = resident_blocks(accumulate_kernel, kStepThreads);
-    const int64_t grid = stream_grid(tiles, resident);
+    const int64_t grid = stream_grid(tiles, resident, kStepThreads);
     const int32_t vec = aligned16(main_grad) && aligned16(micro);
     (void)hipGetLastError();
     hipLaunchKernelGGL(accumulate_kernel, dim3((unsigned)grid), dim3(kStepThreads), 0,

@@ -7,9 +7,10 @@
 //
 // W is unit `unit` of a row layout (zero_shard_init_rows) with rows =
 // in_features and cols = out_features, so Y = X W takes (batch x in) to
-// (batch x out).  The contractions run on the MFMA GEMM in its natural
-// form C = A B^T (both operands contiguous along K); the other operand
-// orders come from the bf16 transpose.
+// (batch x out).  The contractions run on the MFMA GEMM, which reads each
+// operand in place, contiguous along K or along its rows, so no transposed
+// copy is made.  The batch is the K of the dW product, hence the GEMM's
+// multiple-of-8 rule on it.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"

@@ -332,6 +332,8 @@ typedef enum {
    ldc >= N, and 16-byte aligned A and B.  Operands are read through 32-bit
    buffer offsets, so a K_INNER operand's leading dimension must be at most
    2^22 = 4,194,304 elements and a K_OUTER one's at most 2^25 = 33,554,432.
+   C may span at most 4,194,303 tiles of 256 x 256 (the launch, up to two
+   512-thread blocks per tile, stays below 2^32 work-items).
    ZERO_ERR_UNSUPPORTED or ZERO_ERR_ALIGNMENT otherwise, with nothing
    launched.  M = 0 or N = 0 is
    a no-op; K = 0 writes zeros.  All pointers are device memory owned by the

@@ -231,6 +231,32 @@ def test_fsdp_sweep_validation_launches_nothing():
     zs.fsdp_sweep(L, 1, 1, cfg, zs.BF16, [], FAKE, FAKE, FAKE, 2, 0, 0)
 
 
+def test_binding_refuses_short_pointer_arrays():
+    # these C entry points take host pointer arrays without a count; the
+    # binding checks the lengths, so the library never reads past them
+    L = zs.shard_init("fsdp", 4, 3, [4096, 100])
+    cfg = zs.adam_cfg(step=1)
+    good = ([FAKE] * 4, [FAKE, FAKE, FAKE, None], FAKE)
+    with pytest.raises(ValueError, match="units"):
+        zs.fsdp_sweep(L, 0, 2, cfg, zs.BF16, [good], FAKE, FAKE, FAKE, 2, 0, 0)
+    with pytest.raises(ValueError, match="rank_grads"):
+        zs.fsdp_sweep(L, 0, 2, cfg, zs.BF16, [good, ([FAKE] * 3, good[1], FAKE)], FAKE, FAKE,
+                      FAKE, 2, 0, 0)
+    with pytest.raises(ValueError, match="peer_shards"):
+        zs.fsdp_sweep(L, 0, 2, cfg, zs.BF16, [good, (good[0], [FAKE, None], FAKE)], FAKE, FAKE,
+                      FAKE, 2, 0, 0)
+    W = zs.shard_init_rows("fsdp2", 4, 1, [(16, 16)])
+    with pytest.raises(ValueError, match="w_shards"):
+        zs.fsdp_linear_forward(W, 0, [FAKE] * 3, 8, FAKE, FAKE, FAKE, stream=0)
+    with pytest.raises(ValueError, match="w_shards"):
+        zs.fsdp_linear_backward(W, 0, [FAKE] * 5, 8, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    # a DDP layout has one slice per unit
+    D = zs.shard_init("ddp", 4, 0, [64])
+    with pytest.raises(ValueError, match="peer_shards"):
+        zs.fsdp_sweep(D, 0, 1, cfg, zs.BF16, [([FAKE] * 4, [FAKE] * 4, FAKE)], FAKE, FAKE, FAKE,
+                      2, 0, 0)
+
+
 @settings(max_examples=150, deadline=None)
 @given(shapes=st.lists(st.tuples(st.integers(0, 300), st.integers(1, 40)), min_size=1,
                        max_size=30),
@@ -293,6 +319,13 @@ def test_gemm_and_linear_validation_launches_nothing():
     # at the limits the checks pass (then the misaligned C is what is refused)
     assert _err(g, 16, 16, 16, FAKE, 1 << 22, KI, FAKE, 1 << 25, KO, FAKE + 2, 16).status == \
         zs.ERR_ALIGNMENT
+    # a grid past 2^32 work-items (up to two 512-thread blocks per 256 x 256
+    # tile) is refused: 2048 x 2048 tiles is one tile too many, 2048 x 2047
+    # fits (then the misaligned C is what is refused)
+    e = _err(g, 2048 * 256, 2048 * 256, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE, 2048 * 256)
+    assert e.status == zs.ERR_UNSUPPORTED and "tiles" in str(e)
+    assert _err(g, 2048 * 256, 2047 * 256, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE + 2,
+                2047 * 256).status == zs.ERR_ALIGNMENT
     # empty outputs launch nothing
     g(0, 16, 16, FAKE, 16, KI, FAKE, 16, KI, FAKE, 16)
     g(16, 0, 16, FAKE, 16, KO, FAKE, 16, KO, FAKE, 16)
