@@ -6,6 +6,12 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+# test_mutants_oracle.py runs the oracle's pins in a child process against a
+# copy of oracle/ with one planted mistake; this variable names the folder
+# holding that copy, so `import oracle` finds it before the real one.
+_MUTANT_ROOT = os.environ.get("ZS_ORACLE_MUTANT_ROOT")
+if _MUTANT_ROOT:
+    sys.path.insert(0, _MUTANT_ROOT)
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 

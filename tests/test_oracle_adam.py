@@ -177,3 +177,40 @@ def test_fp32_oracle_tracks_fp64_evaluation():
     # m is a sum of terms of size up to max|m|; each step rounds twice
     m_ulp = float(np.spacing(np.abs(m32).max()))
     assert np.abs(m32 - m64).max() <= T * 2 * m_ulp
+
+
+@pytest.mark.parametrize("dtype", [np.uint16, np.float32])
+@pytest.mark.parametrize("clip", [1.0, 0.37])
+def test_rank_step_is_the_pinned_chain_in_order(dtype, clip):
+    """The per-rank chain (the expected values of the GPU parity tests) is,
+    bit for bit, the separately pinned steps in the pages' order: the rank
+    mean, the clip scale when its coefficient is below 1, one Adam step, and
+    the bf16 rounding of the updated master."""
+    rng = np.random.default_rng(7)
+    n, k = 5, 3000
+    raw = [rng.standard_normal(k).astype(np.float32) * np.float32(1e-3) for _ in range(n)]
+    ranks = [_c.f32_to_bf16(r) for r in raw] if dtype == np.uint16 else raw
+    p0 = rng.standard_normal(k).astype(np.float32) * np.float32(0.02)
+    m0 = rng.standard_normal(k).astype(np.float32) * np.float32(1e-4)
+    v0 = rng.random(k).astype(np.float32) * np.float32(1e-7)
+    hp = _c.hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 3, True)
+
+    def chain(c):
+        g = _c.average(ranks)
+        if c < 1.0:
+            _c.scale(g, c)
+        p, m, v = p0.copy(), m0.copy(), v0.copy()
+        _c.adam(hp, g, p, m, v)
+        return p, m, v
+
+    p, m, v = p0.copy(), m0.copy(), v0.copy()
+    out = np.empty(k, np.uint16)
+    _c.rank_step(hp, ranks, clip, p, m, v, out)
+    pe, me, ve = chain(clip)
+    for got, want in ((p, pe), (m, me), (v, ve)):
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(out, _c.f32_to_bf16(pe))
+    # the cast is of the new master, and a coefficient below 1 changes the step
+    assert (out != _c.f32_to_bf16(p0)).mean() > 0.5
+    if clip < 1.0:
+        assert not np.array_equal(pe, chain(1.0)[0])

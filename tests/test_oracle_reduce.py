@@ -60,6 +60,14 @@ def test_summation_is_ascending_from_zero():
     assert _c.average(rev)[0] == np.float32(0.25 + 2.0 ** -24)
 
 
+def test_fp32_summation_is_ascending_from_zero():
+    # the same four values as fp32 rank buffers (the Megatron fp32 path):
+    # descending, 3 * 2^-24 is summed first and 1 + 3 * 2^-24 ties to 1 + 2^-22
+    bufs = [np.array([v], np.float32) for v in (1.0, 2.0 ** -24, 2.0 ** -24, 2.0 ** -24)]
+    assert _c.average(bufs)[0] == np.float32(0.25)
+    assert _c.average(list(reversed(bufs)))[0] == np.float32(0.25 + 2.0 ** -24)
+
+
 @pytest.mark.parametrize("n", [2, 4, 8, 64])
 def test_general_inputs_within_recursive_summation_bound(n):
     rng = np.random.default_rng(100 + n)
