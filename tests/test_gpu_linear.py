@@ -114,6 +114,34 @@ def test_gemm_operand_orders_within_fp32_bound(ao, bo, M, N, K, pad):
     check_f32(cb, exact, bound + 2.0 ** -8 * (np.abs(exact) + bound), "bf16 C")
 
 
+def test_gemm_at_the_leading_dimension_limits():
+    """The largest leading dimensions the host accepts: a K-inner A with
+    lda = 2^22 (a 256-row panel then spans 255 * 2^23 bytes, just under the
+    2^31 of a buffer offset) and a K-outer B with ldb = 2^25 (k row 31 of a
+    stage at 31 * 2^26 bytes).  M = 264 runs one whole tile and one half
+    tile.  Rows past M and columns past N of C stay untouched."""
+    M, N, K = 264, 136, 40
+    lda, ldb = 1 << 22, 1 << 25
+    rng = np.random.default_rng(22)
+    a = rand_bf16(rng, (M, K))
+    b = rand_bf16(rng, (N, K))
+    A = torch.zeros((M, lda), dtype=torch.int16, device=DEV)        # 2.2 GB
+    A[:, :K] = dev16(a)
+    B = torch.zeros((K, ldb), dtype=torch.int16, device=DEV)        # 2.7 GB
+    B[:, :N] = dev16(np.ascontiguousarray(b.T))
+    av, bv = linear.bf16_values(a), linear.bf16_values(b)
+    exact = av @ bv.T
+    bound = linear.gemm_bound(av, bv.T)
+    C = torch.full((M + 2, N + 5), 7.0, device=DEV)
+    zs.gemm_bf16(M, N, K, A, lda, zs.K_INNER, B, ldb, zs.K_OUTER, C, N + 5, zs.FP32)
+    torch.cuda.synchronize()
+    c = C.cpu().numpy()
+    del A, B
+    torch.cuda.empty_cache()
+    check_f32(c[:M, :N], exact, bound, "fp32 C")
+    assert np.all(c[:, N:] == 7.0) and np.all(c[M:, :] == 7.0)
+
+
 def test_gemm_k_zero_writes_zeros():
     C = torch.full((16, 24), 3.0, device=DEV)
     buf = torch.zeros(64, dtype=torch.int16, device=DEV)
