@@ -56,6 +56,12 @@
  *     description of the last error on the calling thread.
  *   - The library allocates no device memory; a layout is host memory only
  *     and is immutable after init (safe to share between threads).
+ *   - Every compute call only launches kernels (no memset, no copy, no
+ *     allocation), so it may be captured into a HIP graph and replayed.
+ *     zero_fsdp_sweep forks its gather stream from the step stream through
+ *     events and joins it back before returning, so a capture of the step
+ *     stream takes in both.  A graph keeps the argument values of its
+ *     capture, the Adam step number included.
  *   - Calls that write disjoint buffers may run concurrently on different
  *     streams.  An fp32 buffer pointer must be 4-byte aligned and a bf16
  *     one 2-byte aligned; 16-byte aligned buffers with slice offsets that are

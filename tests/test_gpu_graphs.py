@@ -1,0 +1,205 @@
+"""The library's calls under HIP graph capture (torch.cuda.CUDAGraph).
+
+The library records no memset and allocates nothing, so a caller may capture
+its launches in a graph. Each graph here is replayed several times. Between
+the replays the program runs eager work of its own and synchronizes the
+device. Every replay's output is compared bit for bit with the same calls
+run eagerly on a second copy of the state, so a replay that reused stale
+arguments or skipped a node would show.
+"""
+import numpy as np
+import pytest
+import torch
+
+from synthetic import grad_bits, small_workload
+
+pytestmark = pytest.mark.gpu
+
+zs = None
+DEV = "cuda:0"
+REPLAYS = 4
+
+
+def setup_module(module):
+    global zs
+    from fsdp_sharded_optimizer_shard_amd import zs as _zs
+    zs = _zs
+
+
+def _bits(t):
+    return t.detach().cpu().numpy().view(np.uint32 if t.dtype == torch.float32 else np.uint16)
+
+
+def _same(a, b, what):
+    assert np.array_equal(_bits(a), _bits(b)), what
+
+
+def _noise():
+    # eager work of the program's own between replays
+    x = torch.randn(1 << 20, device=DEV)
+    return float((x * x).sum())
+
+
+def _state(S, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    master = (torch.randn(S, generator=g) * 0.02).to(DEV)
+    m = (torch.randn(S, generator=g) * 1e-4).to(DEV)
+    v = (torch.rand(S, generator=g) * 1e-7).to(DEV)
+    return master, m, v
+
+
+def _replay_and_compare(capture, eager, outputs_g, outputs_e):
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        capture()
+    for rep in range(REPLAYS):
+        eager()
+        graph.replay()
+        _noise()
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(outputs_g, outputs_e)):
+            _same(a, b, f"replay {rep}, output {k}")
+
+
+def test_fused_step_and_gather_in_a_graph():
+    units, n, r = [5000, 3000, 777], 4, 1
+    L = zs.shard_init("zero3", n, r, units)
+    S, P = L.shard_len, L.flat_len
+    w = small_workload(units, n, "zero3", cfg=12)
+    grads = [grad_bits(w, 0, q, S, device=DEV) for q in range(n)]
+    peers = [None if q == r else grad_bits(w, 1, q, S, device=DEV) for q in range(n)]
+    cfg = zs.adam_cfg(lr=1e-3, weight_decay=0.01, decoupled=True, step=3)
+    G = list(_state(S, 5)) + [torch.zeros(P, dtype=torch.int16, device=DEV)]
+    E = [t.clone() for t in G]
+
+    def step(st):
+        zs.adam_step(L, 0, len(units), cfg, st[0], st[1], st[2], st[3],
+                     grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
+        zs.gather_params(L, 0, len(units), peers, st[3])
+
+    W = [t.clone() for t in G]          # warm-up call before capture
+    step(W)
+    torch.cuda.synchronize()
+    _replay_and_compare(lambda: step(G), lambda: step(E), G, E)
+
+
+def test_two_pass_clip_in_a_graph():
+    units, n, r = [25000, 9001], 4, 2
+    L = zs.shard_init("zero2", n, r, units)
+    S, P = L.shard_len, L.flat_len
+    w = small_workload(units, n, "zero2", cfg=12)
+    grads = [grad_bits(w, 0, q, P, device=DEV) for q in range(n)]
+    cfg = zs.adam_cfg(lr=1e-3, step=2)
+    npart = zs.reduce_partials_count(L, 0, len(units))
+
+    def buffers():
+        master, m, v = _state(S, 6)
+        return [master, m, v, torch.zeros(P, dtype=torch.int16, device=DEV),
+                torch.empty(S, device=DEV), torch.empty(npart, dtype=torch.float64, device=DEV),
+                torch.empty(1, device=DEV), torch.empty(1, dtype=torch.float64, device=DEV)]
+
+    def step(b):
+        master, m, v, out, gsh, part, coef, norm = b
+        zs.reduce_shard(L, 0, len(units), zs.Grads(grads, zs.BF16, zs.INDEX_FULL), gsh,
+                        part, npart)
+        # a small max_norm, so that the coefficient is below 1 and applied
+        zs.clip_coef(part, npart, 1e-3, coef, norm)
+        zs.adam_step(L, 0, len(units), cfg, master, m, v, out, grad_fp32=gsh, clip_coef=coef)
+
+    G, E = buffers(), buffers()
+    step(buffers())
+    torch.cuda.synchronize()
+    _replay_and_compare(lambda: step(G), lambda: step(E), G, E)
+    assert float(E[6]) < 1.0
+
+
+@pytest.mark.parametrize("ao,bo", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_gemm_in_a_graph(ao, bo):
+    M, N, K = 264, 520, 200
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(100 + 2 * ao + bo)
+    A = (torch.randn((K, M) if ao else (M, K), generator=gen)).to(torch.bfloat16).to(DEV)
+    B = (torch.randn((K, N) if bo else (N, K), generator=gen)).to(torch.bfloat16).to(DEV)
+    order = (zs.K_INNER, zs.K_OUTER)
+    Cg = torch.empty((M, N), device=DEV)
+    Ce = torch.empty((M, N), device=DEV)
+
+    def run(C):
+        zs.gemm_bf16(M, N, K, A.view(torch.int16), A.shape[1], order[ao], B.view(torch.int16),
+                     B.shape[1], order[bo], C, N, zs.FP32)
+
+    def eager():
+        Cg.fill_(float("nan"))           # each replay must rewrite every element
+        run(Ce)
+
+    run(Ce)
+    torch.cuda.synchronize()
+    _replay_and_compare(lambda: run(Cg), eager, [Cg], [Ce])
+
+
+def test_two_stream_sweep_in_a_graph():
+    """The FSDP sweep forks its gather stream from the capturing step stream
+    through events and joins it back before returning, so the whole
+    two-stream schedule is captured as one graph."""
+    units, n, r = [4096, 1000, 2500, 777], 4, 3
+    U = len(units)
+    L = zs.shard_init("fsdp", n, r, units)
+    q = [L.query(u) for u in range(U)]
+    S = L.shard_len
+    w = small_workload(units, n, "fsdp", cfg=12)
+    grads = [[grad_bits(w, 0, k, q[u]["shard_len"], device=DEV, unit=u) for k in range(n)]
+             for u in range(U)]
+    peers = [[None if k == r else grad_bits(w, 1, k, q[u]["shard_len"], device=DEV, unit=u)
+              for k in range(n)] for u in range(U)]
+    cfg = zs.adam_cfg(lr=1e-3, weight_decay=0.01, decoupled=True, step=2)
+    gs = torch.cuda.Stream()
+
+    def buffers():
+        return list(_state(S, 7)) + [torch.zeros(x["padded_len"], dtype=torch.int16, device=DEV)
+                                     for x in q]
+
+    def sweep(b):
+        ios = [(grads[u], peers[u], b[3 + u]) for u in range(U)]
+        zs.fsdp_sweep(L, 0, U, cfg, zs.BF16, ios, b[0], b[1], b[2], 2, gather_stream=gs)
+
+    G, E = buffers(), buffers()
+    sweep(buffers())
+    torch.cuda.synchronize()
+    _replay_and_compare(lambda: sweep(G), lambda: sweep(E), G, E)
+
+
+def test_linear_layer_in_a_graph():
+    # forward and backward of the FSDP linear layer, padding rows included
+    inf, outf, n, r, batch = 200, 136, 4, 1, 64
+    L = zs.shard_init_rows("fsdp2", n, r, [(inf, outf)])
+    s = L.query(0)["shard_len"]
+    P = L.flat_len
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(8)
+
+    def bf(*shape):
+        return torch.randn(shape, generator=gen).to(torch.bfloat16).view(torch.int16).to(DEV)
+
+    shards = [bf(s) for _ in range(n)]
+    x, dy = bf(batch, inf), bf(batch, outf)
+
+    def buffers():
+        return [torch.zeros(P, dtype=torch.int16, device=DEV),
+                torch.empty((batch, outf), device=DEV), torch.empty((batch, inf), device=DEV),
+                torch.empty(P, device=DEV)]
+
+    def layer(b):
+        w_full, y, dx, dw = b
+        zs.fsdp_linear_forward(L, 0, shards, batch, x, w_full, y, zs.FP32)
+        zs.fsdp_linear_backward(L, 0, shards, batch, x, dy, w_full, dx, dw, zs.FP32)
+
+    def eager():
+        for t in G[1:]:
+            t.fill_(float("nan"))
+        layer(E)
+
+    G, E = buffers(), buffers()
+    layer(buffers())
+    torch.cuda.synchronize()
+    _replay_and_compare(lambda: layer(G), eager, G, E)
