@@ -59,6 +59,7 @@
 // 8 (v / 4) + 4 (l / 32) + (v % 4), column l % 32.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <type_traits>
@@ -658,21 +659,25 @@ __global__ __launch_bounds__(256) void zero_rows_kernel(float *p, int64_t ld, in
 
 bool a16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device (atomics: calls
+// may come from several host threads at once).
 int cu_count()
 {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         dev = -1;
-    if (dev >= 0 && dev < 64 && cache[dev] > 0)
-        return cache[dev];
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
     int n = 0;
     if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
                        hipSuccess || n <= 0)
         n = 256;
     if (dev >= 0 && dev < 64)
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 

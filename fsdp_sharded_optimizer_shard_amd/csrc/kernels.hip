@@ -28,6 +28,7 @@
 // the exact reciprocal when N is a power of two, which rounds identically).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -553,20 +554,22 @@ __global__ __launch_bounds__(kClipThreads) void clip_kernel(const double *partia
 
 // ------------------------------------------------------------- host --
 
+// Compute units of the current device, cached per device (atomics: calls
+// may come from several host threads at once).
 int device_cus()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (!cached[dev]) {
-        int cus = 0;
+    int cus = cached[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        cached[dev] = cus;
+        cached[dev].store(cus, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return cus;
 }
 
 // Launch width.  Default: one block per 2048-element tile.  Measured on
