@@ -352,3 +352,26 @@ def test_host_tensors_are_refused_before_any_call():
                      grad_fp32=host)
     with pytest.raises(ValueError, match="GPU tensors"):
         zs.grad_accumulate(host, host, 16, stream=0)
+
+
+def test_last_error_is_per_thread():
+    # each thread provokes its own error and must read back its own message
+    import threading
+    bad = []
+
+    def worker(k):
+        for _ in range(200):
+            try:
+                zs.shard_init("zero2", 4, 4 + k, [8])
+            except zs.ZeroShardError as e:
+                if f"rank {4 + k} outside" not in str(e):
+                    bad.append(str(e))
+            else:
+                bad.append("no error")
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
