@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--vs-library", action="store_true",
                     help="with --fsdp-linear: also time the three GEMMs against torch.mm "
                          "(hipBLASLt) on the same operands, alternately")
+    ap.add_argument("--vs-torch", action="store_true",
+                    help="headline workload: also time the same step composed from PyTorch "
+                         "ops (rank sum, torch.optim.Adam(fused=True), bf16 cast) on the same "
+                         "inputs, alternating with the fused kernel")
     ap.add_argument("--fsdp2", action="store_true",
                     help="config 2 only: the exact Mistral-7B per-parameter dim-0 layout "
                          "(291 parameters) instead of one flat unit")
@@ -197,7 +201,65 @@ def run_headline(args, torch, zs, np):
                                kern["fused_reduce_adam_cast"]["ms_per_launch_mean"],
                                counter_traffic())
     out["cpu_baseline"] = cpu
+    if args.vs_torch:
+        out["torch_comparison"] = step_vs_torch(torch, zs, L, U, w, grads, master, m, v, full, G,
+                                                r, S)
     return out
+
+
+def step_vs_torch(torch, zs, L, U, w, grads, master, m, v, full, G, r, S, rounds=5, iters=5):
+    """The rank's reduce + Adam + bf16 cast composed from PyTorch ops on the
+    same inputs: the fp32 sum of the N bf16 gradients in rank order (in-place
+    mixed-dtype adds), one division by N, torch.optim.Adam(fused=True) on an
+    fp32 copy of the master, and the bf16 cast into the rank's slice of the
+    flat buffer.  Timed alternately with zero_adam_step (the fused kernel),
+    `iters` steps per round, on the current stream with HIP events."""
+    N = len(grads)
+    gb = [g.view(torch.bfloat16) for g in grads]
+    own = full.view(torch.bfloat16)[r * S:(r + 1) * S]
+    p = torch.nn.Parameter(master.detach().clone())
+    acc = torch.empty(S, device=master.device)
+    try:
+        opt = torch.optim.Adam([p], lr=w.lr, betas=(w.beta1, w.beta2), eps=w.eps, fused=True)
+        kind = "torch.optim.Adam(fused=True)"
+    except (RuntimeError, ValueError):
+        opt = torch.optim.Adam([p], lr=w.lr, betas=(w.beta1, w.beta2), eps=w.eps, foreach=True)
+        kind = "torch.optim.Adam(foreach=True)"
+
+    def torch_step():
+        acc.copy_(gb[0])
+        for q in range(1, N):
+            acc.add_(gb[q])
+        acc.div_(N)
+        p.grad = acc
+        opt.step()
+        own.copy_(p.detach())
+
+    t = [1000]
+
+    def ours():
+        t[0] += 1
+        cfg = zs.adam_cfg(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps, step=t[0])
+        zs.adam_step(L, 0, U, cfg, master, m, v, full, zs.INDEX_FULL, grads=G)
+
+    E = torch.cuda.Event
+    res = {"ours": [], "torch": []}
+    for fn in (ours, torch_step):        # warm-up
+        fn()
+    for _ in range(rounds):
+        for name, fn in (("ours", ours), ("torch", torch_step)):
+            a, b = E(enable_timing=True), E(enable_timing=True)
+            a.record()
+            for _ in range(iters):
+                fn()
+            b.record()
+            b.synchronize()
+            res[name].append(a.elapsed_time(b) / iters)
+    mo, mt = sum(res["ours"]) / rounds, sum(res["torch"]) / rounds
+    return {"torch_pipeline": kind + " after an fp32 rank sum; bf16 cast into the flat buffer",
+            "ms_ours": mo, "ms_torch": mt, "speedup": mt / mo,
+            "ms_ours_range": [min(res["ours"]), max(res["ours"])],
+            "ms_torch_range": [min(res["torch"]), max(res["torch"])]}
 
 
 def run_tiny(args, torch, zs, np):
@@ -695,6 +757,10 @@ def main():
 
     if args.vs_library and not args.fsdp_linear:
         print("--vs-library applies to --fsdp-linear only.", file=sys.stderr)
+        sys.exit(2)
+    if args.vs_torch and (args.fsdp_linear or args.fsdp2 or args.config != 2 or
+                          args.calibrate_copy):
+        print("--vs-torch applies to the headline workload (--config 2) only.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -1,6 +1,7 @@
 """The parts of bench.py's contract that need no GPU: a request for more
 than one GPU (by flag or by a launcher's WORLD_SIZE), or for the library
-comparison outside the linear-layer workload, exits at once with a message
+comparison outside the linear-layer workload, or for the PyTorch comparison
+outside the headline workload, exits at once with a message
 and a non-zero status, before torch or the library is touched."""
 import os
 import subprocess
@@ -30,3 +31,9 @@ def test_launcher_world_size_is_refused():
 def test_library_comparison_needs_the_linear_workload():
     r = _run(["--vs-library", "--steps", "1"])
     assert r.returncode == 2 and "--fsdp-linear" in r.stderr and r.stdout == ""
+
+
+def test_torch_comparison_needs_the_headline_workload():
+    for extra in (["--config", "1"], ["--fsdp-linear"]):
+        r = _run(["--vs-torch", "--steps", "1", *extra])
+        assert r.returncode == 2 and "--vs-torch" in r.stderr and r.stdout == ""
