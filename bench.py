@@ -738,30 +738,52 @@ def counter_traffic(path=COUNTERS, src=KERNELS_SRC, sha_key="kernels_hip_sha256"
 
 
 def cpu_baseline(w, grads, master, S, r, budget_s, what="rank-{r} shard", total=None):
-    """The oracle, single-threaded, on the first elements of the same shard:
+    """The oracle, as it stands, on the first elements of the same shard:
     16M-element chunks are copied from the GPU and stepped (step 1) until the
-    oracle has run for `budget_s` seconds or the S elements are done; only
-    oracle time is counted.  With `total`, the sample is one part of a
-    `total`-element shard and the time for all of it is extrapolated."""
+    single-threaded oracle has run for `budget_s` seconds or the S elements
+    are done; only oracle time is counted.  Each chunk is also stepped by
+    the same oracle function on all host cores, each thread taking a
+    contiguous slice (ctypes releases the GIL), and both results must be
+    bit-identical.  With `total`, the sample is one part of a `total`-element
+    shard and the time for all of it is extrapolated."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     from oracle import _c
 
+    cores = len(os.sched_getaffinity(0))
+    pool = cf.ThreadPoolExecutor(cores)
     chunk = 1 << 24
     hp = _c.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, 1, w.decoupled)
-    done, spent = 0, 0.0
+    done, spent, spent_all, same = 0, 0.0, 0.0, True
     while spent < budget_s and done < S:
         n = min(chunk, S - done)
         g = [x[done:done + n].cpu().numpy().view(np.uint16) for x in grads]
-        p = master[done:done + n].cpu().numpy().copy()
-        m = np.zeros(n, np.float32)
-        v = np.zeros(n, np.float32)
-        out = np.empty(n, np.uint16)
-        tmp = np.empty(n, np.float32)
+        p0 = master[done:done + n].cpu().numpy()
+        p, m, v = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+        out, tmp = np.empty(n, np.uint16), np.empty(n, np.float32)
         t0 = time.perf_counter()
         _c.rank_step(hp, g, 1.0, p, m, v, out, tmp)
         spent += time.perf_counter() - t0
+        pa, ma, va = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
+        outa, tmpa = np.empty(n, np.uint16), np.empty(n, np.float32)
+        cuts = [n * k // cores for k in range(cores + 1)]
+
+        def part(k):
+            lo, hi = cuts[k], cuts[k + 1]
+            if hi > lo:
+                _c.rank_step(hp, [x[lo:hi] for x in g], 1.0, pa[lo:hi], ma[lo:hi], va[lo:hi],
+                             outa[lo:hi], tmpa[lo:hi])
+
+        t0 = time.perf_counter()
+        list(pool.map(part, range(cores)))
+        spent_all += time.perf_counter() - t0
+        same = same and np.array_equal(out, outa) and np.array_equal(p.view(np.uint32),
+                                                                     pa.view(np.uint32))
         done += n
+    pool.shutdown()
+    assert same, "the oracle on all cores must match the single-threaded oracle"
     sample = (f"first {done} of {S} elements of the {what.format(r=r)}, step 1, "
               f"{chunk}-element chunks, {spent:.1f} s of oracle time "
               f"(reduce {len(grads)} bf16 ranks + Adam + bf16 cast)")
@@ -769,7 +791,10 @@ def cpu_baseline(w, grads, master, S, r, budget_s, what="rank-{r} shard", total=
         sample += (f"; the whole {total}-element shard would take {spent * total / done:.1f} s "
                    f"(extrapolated)")
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": sample}
+            "sample": sample,
+            "all_cores": {"value": done / spent_all, "unit": "params/s", "cores": cores,
+                          "how": "the same oracle function on contiguous slices, one host "
+                                 "thread per core; bit-identical to the single-threaded run"}}
 
 
 def main():

@@ -37,3 +37,21 @@ def test_torch_comparison_needs_the_headline_workload():
     for extra in (["--config", "1"], ["--fsdp-linear"]):
         r = _run(["--vs-torch", "--steps", "1", *extra])
         assert r.returncode == 2 and "--vs-torch" in r.stderr and r.stdout == ""
+
+
+def test_cpu_baseline_all_cores_matches_single_thread():
+    # the CPU-baseline leg on a small host-resident sample: the all-cores run
+    # of the oracle must be bit-identical to the single-threaded one
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    from synthetic import grad_bits, master_init, small_workload
+    w = small_workload([70_001], 8, "zero3", cfg=3)
+    S = 70_001
+    grads = [grad_bits(w, 0, q, S) for q in range(8)]
+    master = master_init(w, S)
+    out = bench.cpu_baseline(w, grads, master, S, 7, budget_s=5.0)
+    assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
+    allc = out["all_cores"]
+    assert allc["cores"] == len(os.sched_getaffinity(0)) and allc["value"] > 0
+    assert f"first {S} of {S}" in out["sample"]
