@@ -737,6 +737,17 @@ def counter_traffic(path=COUNTERS, src=KERNELS_SRC, sha_key="kernels_hip_sha256"
         return None
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, grads, master, S, r, budget_s, what="rank-{r} shard", total=None):
     """The oracle, as it stands, on the first elements of the same shard:
     16M-element chunks are copied from the GPU and stepped (step 1) until the
@@ -791,7 +802,7 @@ def cpu_baseline(w, grads, master, S, r, budget_s, what="rank-{r} shard", total=
         sample += (f"; the whole {total}-element shard would take {spent * total / done:.1f} s "
                    f"(extrapolated)")
     return {"value": done / spent, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": sample,
+            "sample": sample, "cpu_model": host_cpu_model(),
             "all_cores": {"value": done / spent_all, "unit": "params/s", "cores": cores,
                           "how": "the same oracle function on contiguous slices, one host "
                                  "thread per core; bit-identical to the single-threaded run"}}

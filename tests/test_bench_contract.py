@@ -55,3 +55,4 @@ def test_cpu_baseline_all_cores_matches_single_thread():
     allc = out["all_cores"]
     assert allc["cores"] == len(os.sched_getaffinity(0)) and allc["value"] > 0
     assert f"first {S} of {S}" in out["sample"]
+    assert isinstance(out["cpu_model"], str) and out["cpu_model"]
