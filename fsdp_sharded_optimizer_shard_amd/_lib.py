@@ -58,6 +58,13 @@ def adam_cfg(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, decoup
     return AdamCfg(lr, beta1, beta2, eps, weight_decay, int(bool(decoupled)), int(step))
 
 
+class AdamTableEntry(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_float) for k in ("lr", "beta1", "beta2", "eps", "weight_decay",
+                                               "one_minus_beta1", "one_minus_beta2", "bias1",
+                                               "bias2", "decay")] + \
+               [("has_decay", _I32), ("decoupled", _I32)]
+
+
 _lib.zero_shard_init.argtypes = [ctypes.POINTER(_P), _I32, _I32, _I32, _I32, ctypes.POINTER(_I64)]
 _lib.zero_shard_init.restype = _I32
 _lib.zero_shard_init_rows.argtypes = [ctypes.POINTER(_P), _I32, _I32, _I32, _I32,
@@ -81,6 +88,13 @@ _lib.zero_clip_coef.restype = _I32
 _lib.zero_adam_step.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _P, _I32, _P,
                                 ctypes.POINTER(_Grads), _P, _P, _P, _P, _I32, _P]
 _lib.zero_adam_step.restype = _I32
+_lib.zero_adam_table_fill.argtypes = [ctypes.POINTER(AdamCfg), _I64, _P]
+_lib.zero_adam_table_fill.restype = _I32
+_lib.zero_adam_step_table.argtypes = [_P, _I32, _I32, _P, _I64, _P, _P, _I32, _P,
+                                      ctypes.POINTER(_Grads), _P, _P, _P, _P, _I32, _P]
+_lib.zero_adam_step_table.restype = _I32
+_lib.zero_step_advance.argtypes = [_P, _P]
+_lib.zero_step_advance.restype = _I32
 _lib.zero_gather_params.argtypes = [_P, _I32, _I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P]
 _lib.zero_gather_params.restype = _I32
 
@@ -115,7 +129,8 @@ _lib.zero_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy",
            "zero_layout_info", "zero_layout_query", "zero_reduce_shard",
-           "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step", "zero_gather_params",
+           "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
+           "zero_adam_table_fill", "zero_adam_step_table", "zero_step_advance", "zero_gather_params",
            "zero_grad_accumulate", "zero_fsdp_sweep", "zero_gemm_bf16", "zero_gemm_bf16_nt",
            "zero_transpose_bf16", "zero_fsdp_linear_forward", "zero_fsdp_linear_backward",
            "zero_status_str", "zero_last_error")
@@ -273,6 +288,39 @@ def adam_step(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, mast
                                grads.ref() if grads else None,
                                _addr(master), _addr(m), _addr(v), _addr(param_out), param_index,
                                _stream(stream)), "zero_adam_step")
+
+
+def adam_table(cfgs):
+    """Host table of step scalars, one entry per configuration (entry k is
+    used when the device step counter holds k + 1): an array of
+    AdamTableEntry; bytes(table) is what goes to the device."""
+    n = len(cfgs)
+    arr = (AdamCfg * max(1, n))(*cfgs)
+    out = (AdamTableEntry * max(1, n))()
+    _check(_lib.zero_adam_table_fill(arr, n, out), "zero_adam_table_fill")
+    return out
+
+
+def adam_table_device(cfgs, device="cuda"):
+    """adam_table(cfgs) copied into a device uint8 tensor."""
+    import torch
+    t = adam_table(cfgs)
+    return torch.frombuffer(bytearray(bytes(t)), dtype=torch.uint8).to(device)
+
+
+def adam_step_table(layout: Layout, unit_begin: int, unit_end: int, table, n_entries: int,
+                    step_counter, master, m, v, param_out, param_index: int = INDEX_FULL,
+                    grad_fp32=None, clip_coef=None, grads: Optional[Grads] = None, stream=None,
+                    grad_index: int = INDEX_SHARD) -> None:
+    _check(_lib.zero_adam_step_table(layout.handle, unit_begin, unit_end, _addr(table), n_entries,
+                                     _addr(step_counter), _addr(grad_fp32), grad_index,
+                                     _addr(clip_coef), grads.ref() if grads else None,
+                                     _addr(master), _addr(m), _addr(v), _addr(param_out),
+                                     param_index, _stream(stream)), "zero_adam_step_table")
+
+
+def step_advance(step_counter, stream=None) -> None:
+    _check(_lib.zero_step_advance(_addr(step_counter), _stream(stream)), "zero_step_advance")
 
 
 def gather_params(layout: Layout, unit_begin: int, unit_end: int, shards, param_full,

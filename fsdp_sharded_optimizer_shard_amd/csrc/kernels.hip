@@ -30,6 +30,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <cstddef>
 #include <cstdlib>
 #include <cstring>
 
@@ -61,11 +62,19 @@ struct Seg {
     int64_t vec;        // 1 if both offsets are multiples of 4 (vector path)
 };
 
+// The step scalars; the same layout as zero_adam_table_entry, so a table of
+// them in device memory can be read as is.
 struct AdamScalars {
     float lr, b1, b2, eps, wd;
     float omb1, omb2, bias1, bias2, decay;
     int32_t has_wd, decoupled;
 };
+static_assert(sizeof(AdamScalars) == sizeof(zero_adam_table_entry), "table entry layout");
+static_assert(offsetof(AdamScalars, omb1) == offsetof(zero_adam_table_entry, one_minus_beta1) &&
+                  offsetof(AdamScalars, decay) == offsetof(zero_adam_table_entry, decay) &&
+                  offsetof(AdamScalars, has_wd) == offsetof(zero_adam_table_entry, has_decay) &&
+                  offsetof(AdamScalars, decoupled) == offsetof(zero_adam_table_entry, decoupled),
+              "table entry layout");
 
 enum Mode { kFused = 0, kReduce = 1, kApply = 2 };
 
@@ -92,6 +101,9 @@ struct StepArgs {
     int32_t pout_full;   // 1: full-indexed, 0: shard-indexed
     int32_t _pad;
     AdamScalars sc;
+    const AdamScalars *table;  // non-null: scalars from table[*step - 1] instead of sc
+    const int64_t *step;
+    int64_t n_table;
     Seg seg[kMaxSegs];
 };
 
@@ -308,7 +320,8 @@ __device__ double block_sum(double x)
 
 // The fused / reduce / apply work for G full groups of 4 elements.
 template <int MODE, int NR, bool BF16, int G>
-__device__ __forceinline__ void step_groups(const StepArgs &a, const Seg &sg, const int64_t *j,
+__device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars &sc,
+                                            const Seg &sg, const int64_t *j,
                                             float coef, double &sq)
 {
     int64_t si[G], fi[G];
@@ -365,7 +378,7 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const Seg &sg, co
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            adam1(a.sc, g[h][e], p[h][e], m[h][e], v[h][e]);
+            adam1(sc, g[h][e], p[h][e], m[h][e], v[h][e]);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         st_nt(reinterpret_cast<f32x4 *>(a.master + si[h]), f32x4{p[h][0], p[h][1], p[h][2], p[h][3]});
@@ -380,7 +393,8 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const Seg &sg, co
 
 // The same work one element at a time: ragged tails and unaligned slices.
 template <int MODE, int NR, bool BF16>
-__device__ __forceinline__ void step_scalar(const StepArgs &a, const Seg &sg, int64_t j,
+__device__ __forceinline__ void step_scalar(const StepArgs &a, const AdamScalars &sc,
+                                            const Seg &sg, int64_t j,
                                             int64_t cnt, float coef, double &sq)
 {
     const int64_t si = sg.shard_off + j;
@@ -397,7 +411,7 @@ __device__ __forceinline__ void step_scalar(const StepArgs &a, const Seg &sg, in
             sq = sq + (double)g * (double)g;
         } else {
             float p = a.master[si + e], m = a.m[si + e], v = a.v[si + e];
-            adam1(a.sc, g, p, m, v);
+            adam1(sc, g, p, m, v);
             a.master[si + e] = p;
             a.m[si + e] = m;
             a.v[si + e] = v;
@@ -409,6 +423,15 @@ __device__ __forceinline__ void step_scalar(const StepArgs &a, const Seg &sg, in
 template <int MODE, int NR, bool BF16>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs a)
 {
+    AdamScalars sc = a.sc;
+    if (MODE != kReduce && a.table) {
+        // the whole grid reads one counter: a value outside the table
+        // leaves every buffer untouched
+        const int64_t t = *a.step;
+        if (t < 1 || t > a.n_table)
+            return;
+        sc = a.table[t - 1];
+    }
     const float coef = (MODE == kApply && a.clip) ? *a.clip : 1.0f;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -420,9 +443,9 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs a)
         double sq = 0.0;  // kReduce: this thread's sum of squares in this tile
         if (j[0] < sg.len) {
             if (vec && j[0] + 4 <= sg.len)
-                step_groups<MODE, NR, BF16, 1>(a, sg, j, coef, sq);
+                step_groups<MODE, NR, BF16, 1>(a, sc, sg, j, coef, sq);
             else
-                step_scalar<MODE, NR, BF16>(a, sg, j[0], sg.len - j[0] < 4 ? sg.len - j[0] : 4,
+                step_scalar<MODE, NR, BF16>(a, sc, sg, j[0], sg.len - j[0] < 4 ? sg.len - j[0] : 4,
                                             coef, sq);
         }
         if (MODE == kReduce && a.partials) {
@@ -521,6 +544,15 @@ __global__ __launch_bounds__(kStepThreads) void accumulate_kernel(float *acc,
                 acc[i + e] = acc[i + e] + bf16f(micro[i + e]);
         }
     }
+}
+
+// ---------------------------------------------------- step counter --
+
+// *step += 1, one lane (a graph node that advances the table step).
+__global__ __launch_bounds__(64) void step_advance_kernel(int64_t *step)
+{
+    if (threadIdx.x == 0)
+        *step = *step + 1;
 }
 
 // ------------------------------------------------------- clip kernel --
@@ -762,6 +794,76 @@ zero_status launch_mode(StepArgs &a, bool bf16, hipStream_t st)
     return ZERO_OK;
 }
 
+zero_status check_cfg(const zero_adam_cfg *cfg)
+{
+    if (!cfg)
+        return fail(ZERO_ERR_INVALID_ARG, "cfg is NULL");
+    if (cfg->step < 1)
+        return fail(ZERO_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)cfg->step);
+    if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f) || !(cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f))
+        return fail(ZERO_ERR_INVALID_ARG, "betas must lie in [0, 1)");
+    if (!std::isfinite(cfg->lr) || !(cfg->eps >= 0.0f) || !std::isfinite(cfg->eps) ||
+        !(cfg->weight_decay >= 0.0f) || !std::isfinite(cfg->weight_decay))
+        return fail(ZERO_ERR_INVALID_ARG, "lr, eps and weight_decay must be finite, eps, wd >= 0");
+    return ZERO_OK;
+}
+
+// The Adam step with its scalars either in the launch (table == nullptr) or
+// read on the device from table[*step - 1].
+zero_status adam_launch(const zero_layout *L, int32_t ub, int32_t ue, const AdamScalars &sc,
+                        const AdamScalars *table, int64_t n_table, const int64_t *step,
+                        const float *grad_fp32, int32_t grad_index, const float *clip_coef,
+                        const zero_grads *grads, float *master, float *m, float *v,
+                        uint16_t *param_out, int32_t param_index, void *stream)
+{
+    zero_status st;
+    if ((grad_fp32 != nullptr) == (grads != nullptr))
+        return fail(ZERO_ERR_INVALID_ARG, "give exactly one of grad_fp32 and grads");
+    if (grads && clip_coef)
+        return fail(ZERO_ERR_INVALID_ARG, "clip_coef needs the two-pass path (grad_fp32)");
+    if (!master || !m || !v || !param_out)
+        return fail(ZERO_ERR_INVALID_ARG, "master, m, v and param_out are required");
+    if (param_index != ZERO_INDEX_FULL && param_index != ZERO_INDEX_SHARD)
+        return fail(ZERO_ERR_INVALID_ARG, "unknown param_index %d", param_index);
+    if (grad_index != ZERO_INDEX_FULL && grad_index != ZERO_INDEX_SHARD)
+        return fail(ZERO_ERR_INVALID_ARG, "unknown grad_index %d", grad_index);
+    if (reinterpret_cast<uintptr_t>(master) % 4 || reinterpret_cast<uintptr_t>(m) % 4 ||
+        reinterpret_cast<uintptr_t>(v) % 4 || reinterpret_cast<uintptr_t>(param_out) % 2 ||
+        reinterpret_cast<uintptr_t>(grad_fp32) % 4 || reinterpret_cast<uintptr_t>(clip_coef) % 4)
+        return fail(ZERO_ERR_ALIGNMENT, "misaligned state / parameter buffer");
+    if (grads && (st = check_grads(L, grads)) != ZERO_OK)
+        return st;
+    return for_each_chunk(ub, ue, [&](int32_t u0, int32_t u1) -> zero_status {
+        StepArgs a;
+        std::memset(&a, 0, sizeof a);
+        bool al = aligned16(master) && aligned16(m) && aligned16(v) && aligned16(param_out);
+        if (grads)
+            fill_grads(grads, a, al);
+        else
+            al = al && aligned16(grad_fp32);
+        a.vec_ptrs = al;
+        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs);
+        if (a.n_tiles == 0)
+            return ZERO_OK;
+        a.master = master;
+        a.m = m;
+        a.v = v;
+        a.gin = grad_fp32;
+        a.gin_full = grad_index == ZERO_INDEX_FULL;
+        a.clip = clip_coef;
+        a.pout = param_out;
+        a.pout_full = param_index == ZERO_INDEX_FULL;
+        a.sc = sc;
+        a.table = table;
+        a.step = step;
+        a.n_table = n_table;
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if (grads)
+            return launch_mode<kFused>(a, grads->dtype == ZERO_BF16, s);
+        return launch_mode<kApply>(a, true, s);
+    });
+}
+
 }  // namespace
 }  // namespace zs
 
@@ -852,58 +954,63 @@ zero_status zero_adam_step(const zero_layout *L, int32_t ub, int32_t ue,
     zero_status st = check_range(L, ub, ue);
     if (st != ZERO_OK)
         return st;
-    if (!cfg)
-        return fail(ZERO_ERR_INVALID_ARG, "cfg is NULL");
-    if (cfg->step < 1)
-        return fail(ZERO_ERR_INVALID_ARG, "step must be >= 1 (got %lld)", (long long)cfg->step);
-    if (!(cfg->beta1 >= 0.0f && cfg->beta1 < 1.0f) || !(cfg->beta2 >= 0.0f && cfg->beta2 < 1.0f))
-        return fail(ZERO_ERR_INVALID_ARG, "betas must lie in [0, 1)");
-    if (!std::isfinite(cfg->lr) || !(cfg->eps >= 0.0f) || !std::isfinite(cfg->eps) ||
-        !(cfg->weight_decay >= 0.0f) || !std::isfinite(cfg->weight_decay))
-        return fail(ZERO_ERR_INVALID_ARG, "lr, eps and weight_decay must be finite, eps, wd >= 0");
-    if ((grad_fp32 != nullptr) == (grads != nullptr))
-        return fail(ZERO_ERR_INVALID_ARG, "give exactly one of grad_fp32 and grads");
-    if (grads && clip_coef)
-        return fail(ZERO_ERR_INVALID_ARG, "clip_coef needs the two-pass path (grad_fp32)");
-    if (!master || !m || !v || !param_out)
-        return fail(ZERO_ERR_INVALID_ARG, "master, m, v and param_out are required");
-    if (param_index != ZERO_INDEX_FULL && param_index != ZERO_INDEX_SHARD)
-        return fail(ZERO_ERR_INVALID_ARG, "unknown param_index %d", param_index);
-    if (grad_index != ZERO_INDEX_FULL && grad_index != ZERO_INDEX_SHARD)
-        return fail(ZERO_ERR_INVALID_ARG, "unknown grad_index %d", grad_index);
-    if (reinterpret_cast<uintptr_t>(master) % 4 || reinterpret_cast<uintptr_t>(m) % 4 ||
-        reinterpret_cast<uintptr_t>(v) % 4 || reinterpret_cast<uintptr_t>(param_out) % 2 ||
-        reinterpret_cast<uintptr_t>(grad_fp32) % 4 || reinterpret_cast<uintptr_t>(clip_coef) % 4)
-        return fail(ZERO_ERR_ALIGNMENT, "misaligned state / parameter buffer");
-    if (grads && (st = check_grads(L, grads)) != ZERO_OK)
+    if ((st = check_cfg(cfg)) != ZERO_OK)
         return st;
-    const AdamScalars sc = make_scalars(cfg);
-    return for_each_chunk(ub, ue, [&](int32_t u0, int32_t u1) -> zero_status {
-        StepArgs a;
-        std::memset(&a, 0, sizeof a);
-        bool al = aligned16(master) && aligned16(m) && aligned16(v) && aligned16(param_out);
-        if (grads)
-            fill_grads(grads, a, al);
-        else
-            al = al && aligned16(grad_fp32);
-        a.vec_ptrs = al;
-        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs);
-        if (a.n_tiles == 0)
-            return ZERO_OK;
-        a.master = master;
-        a.m = m;
-        a.v = v;
-        a.gin = grad_fp32;
-        a.gin_full = grad_index == ZERO_INDEX_FULL;
-        a.clip = clip_coef;
-        a.pout = param_out;
-        a.pout_full = param_index == ZERO_INDEX_FULL;
-        a.sc = sc;
-        const hipStream_t s = static_cast<hipStream_t>(stream);
-        if (grads)
-            return launch_mode<kFused>(a, grads->dtype == ZERO_BF16, s);
-        return launch_mode<kApply>(a, true, s);
-    });
+    return adam_launch(L, ub, ue, make_scalars(cfg), nullptr, 0, nullptr, grad_fp32, grad_index,
+                       clip_coef, grads, master, m, v, param_out, param_index, stream);
+}
+
+zero_status zero_adam_table_fill(const zero_adam_cfg *cfgs, int64_t n,
+                                 zero_adam_table_entry *host_out)
+{
+    if (!cfgs || !host_out || n < 1)
+        return fail(ZERO_ERR_INVALID_ARG, "cfgs, host_out and n >= 1 are required");
+    for (int64_t k = 0; k < n; ++k) {
+        const zero_status st = check_cfg(&cfgs[k]);
+        if (st != ZERO_OK)
+            return fail(st, "entry %lld: %s", (long long)k, zero_last_error());
+    }
+    for (int64_t k = 0; k < n; ++k) {
+        const AdamScalars sc = make_scalars(&cfgs[k]);
+        std::memcpy(&host_out[k], &sc, sizeof sc);
+    }
+    return ZERO_OK;
+}
+
+zero_status zero_adam_step_table(const zero_layout *L, int32_t ub, int32_t ue,
+                                 const zero_adam_table_entry *table, int64_t n_entries,
+                                 const int64_t *step_counter, const float *grad_fp32,
+                                 int32_t grad_index, const float *clip_coef,
+                                 const zero_grads *grads, float *master, float *m, float *v,
+                                 uint16_t *param_out, int32_t param_index, void *stream)
+{
+    zero_status st = check_range(L, ub, ue);
+    if (st != ZERO_OK)
+        return st;
+    if (!table || !step_counter || n_entries < 1)
+        return fail(ZERO_ERR_INVALID_ARG, "table, step_counter and n_entries >= 1 are required");
+    if (reinterpret_cast<uintptr_t>(table) % 4 || reinterpret_cast<uintptr_t>(step_counter) % 8)
+        return fail(ZERO_ERR_ALIGNMENT, "misaligned step table or counter");
+    AdamScalars none;
+    std::memset(&none, 0, sizeof none);
+    return adam_launch(L, ub, ue, none, reinterpret_cast<const AdamScalars *>(table), n_entries,
+                       step_counter, grad_fp32, grad_index, clip_coef, grads, master, m, v,
+                       param_out, param_index, stream);
+}
+
+zero_status zero_step_advance(int64_t *step_counter, void *stream)
+{
+    if (!step_counter)
+        return fail(ZERO_ERR_INVALID_ARG, "step_counter is NULL");
+    if (reinterpret_cast<uintptr_t>(step_counter) % 8)
+        return fail(ZERO_ERR_ALIGNMENT, "step_counter is misaligned");
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(step_advance_kernel, dim3(1), dim3(64), 0,
+                       static_cast<hipStream_t>(stream), step_counter);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(ZERO_ERR_HIP, "step advance launch failed: %s", hipGetErrorString(e));
+    return ZERO_OK;
 }
 
 zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,

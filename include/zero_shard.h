@@ -250,6 +250,49 @@ zero_status zero_adam_step(const zero_layout *layout, int32_t unit_begin,
                            float *v, uint16_t *param_out, int32_t param_index,
                            void *stream);
 
+/* Step scalars read on the device, for graph replay.  A captured graph keeps
+   the arguments of its capture, so zero_adam_step replayed from a graph
+   would repeat one step number (and one learning rate).
+   zero_adam_step_table instead reads the step's scalars when its kernels
+   run, from entry (*step_counter - 1) of a table that the caller fills once
+   on the host with zero_adam_table_fill and copies to the device.
+   zero_step_advance increments the counter on the device.  A graph of
+   [zero_adam_step_table, ..., zero_step_advance] then replays as steps 1,
+   2, 3, ... with the arithmetic of zero_adam_step, bit for bit.
+   The entry is the set of fp32 scalars of one step, each evaluated in fp64
+   from that step's configuration and rounded once (as zero_adam_step). */
+typedef struct zero_adam_table_entry {
+    float lr, beta1, beta2, eps, weight_decay;
+    float one_minus_beta1, one_minus_beta2;
+    float bias1, bias2;  /* 1 - beta1^t, 1 - beta2^t of the entry's step t */
+    float decay;         /* 1 - lr * weight_decay */
+    int32_t has_decay;   /* weight_decay != 0 */
+    int32_t decoupled;
+} zero_adam_table_entry;
+
+/* host_out[k] = the step scalars of cfgs[k], k < n (host arrays; each cfg
+   validated as in zero_adam_step).  cfgs[k].step is the t of entry k,
+   normally k + 1; lr may change from entry to entry (a schedule). */
+zero_status zero_adam_table_fill(const zero_adam_cfg *cfgs, int64_t n,
+                                 zero_adam_table_entry *host_out);
+
+/* zero_adam_step with the scalars of table[*step_counter - 1].  `table` is
+   a device array of n_entries >= 1 entries (4-byte aligned), `step_counter`
+   a device int64 (8-byte aligned), both read when the kernels run; a
+   counter outside [1, n_entries] leaves every buffer untouched.  The other
+   arguments, and the host-side errors, are those of zero_adam_step. */
+zero_status zero_adam_step_table(const zero_layout *layout, int32_t unit_begin,
+                                 int32_t unit_end, const zero_adam_table_entry *table,
+                                 int64_t n_entries, const int64_t *step_counter,
+                                 const float *grad_fp32, int32_t grad_index,
+                                 const float *clip_coef, const zero_grads *grads,
+                                 float *master, float *m, float *v, uint16_t *param_out,
+                                 int32_t param_index, void *stream);
+
+/* *step_counter += 1 on the device, in stream order (device int64,
+   8-byte aligned). */
+zero_status zero_step_advance(int64_t *step_counter, void *stream);
+
 /* ------------------------------------------------------------ gather -- */
 
 /* All-gather data movement: for every rank q < n with shards[q] != NULL

@@ -375,3 +375,43 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert not bad, bad[:3]
+
+
+def test_adam_table_entries_are_the_step_scalars():
+    # each entry: the fp32 hyper-parameters, and 1 - beta, 1 - beta^t and
+    # 1 - lr*wd evaluated in fp64 from them and rounded once to fp32
+    f32 = np.float32
+    cfgs = [zs.adam_cfg(lr=3e-4 * (1 + k), beta1=0.9, beta2=0.95, eps=1e-8,
+                        weight_decay=0.1 * (k % 2), decoupled=k % 3 == 0, step=k + 1)
+            for k in range(7)]
+    tab = zs.adam_table(cfgs)
+    for k, c in enumerate(cfgs):
+        e = tab[k]
+        lr, b1, b2, wd = (float(f32(x)) for x in (c.lr, c.beta1, c.beta2, c.weight_decay))
+        t = c.step
+        want = {"lr": f32(lr), "beta1": f32(b1), "beta2": f32(b2), "eps": f32(c.eps),
+                "weight_decay": f32(wd), "one_minus_beta1": f32(1.0 - b1),
+                "one_minus_beta2": f32(1.0 - b2), "bias1": f32(1.0 - b1 ** t),
+                "bias2": f32(1.0 - b2 ** t), "decay": f32(1.0 - lr * wd)}
+        for name, value in want.items():
+            assert f32(getattr(e, name)).view(np.uint32) == value.view(np.uint32), (k, name)
+        assert e.has_decay == int(wd != 0.0) and e.decoupled == int(c.decoupled)
+
+
+def test_adam_table_validation():
+    e = _err(zs.adam_table, [zs.adam_cfg(step=1), zs.adam_cfg(step=0)])
+    assert e.status == zs.ERR_INVALID_ARG and "entry 1" in str(e)
+    assert _err(zs.adam_table, [zs.adam_cfg(beta1=1.0)]).status == zs.ERR_INVALID_ARG
+    L = _layout()
+    g = zs.Grads([FAKE] * 4, zs.BF16, zs.INDEX_FULL)
+
+    def step(table=FAKE, n=4, counter=FAKE):
+        zs.adam_step_table(L, 0, 2, table, n, counter, FAKE, FAKE, FAKE, FAKE, grads=g, stream=0)
+
+    assert _err(step, table=None).status == zs.ERR_INVALID_ARG
+    assert _err(step, n=0).status == zs.ERR_INVALID_ARG
+    assert _err(step, counter=None).status == zs.ERR_INVALID_ARG
+    assert _err(step, counter=FAKE + 4).status == zs.ERR_ALIGNMENT
+    assert _err(step, table=FAKE + 2).status == zs.ERR_ALIGNMENT
+    assert _err(zs.step_advance, None, stream=0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.step_advance, FAKE + 4, stream=0).status == zs.ERR_ALIGNMENT

@@ -203,3 +203,56 @@ def test_linear_layer_in_a_graph():
     layer(buffers())
     torch.cuda.synchronize()
     _replay_and_compare(lambda: layer(G), eager, G, E)
+
+
+def test_table_steps_replayed_from_one_graph():
+    """One captured step [zero_adam_step_table, gather, zero_step_advance]
+    replays as steps 1..T with a learning-rate schedule, each replay
+    bit-identical to zero_adam_step with that step's configuration; a
+    counter past the table leaves every buffer untouched."""
+    units, n, r, T = [5000, 3000, 777], 4, 1, 5
+    L = zs.shard_init("zero3", n, r, units)
+    S, P = L.shard_len, L.flat_len
+    w = small_workload(units, n, "zero3", cfg=13)
+    grads = [grad_bits(w, 0, q, S, device=DEV) for q in range(n)]
+    peers = [None if q == r else grad_bits(w, 1, q, S, device=DEV) for q in range(n)]
+    cfgs = [zs.adam_cfg(lr=1e-3 * (1.0 - 0.15 * k), weight_decay=0.01, decoupled=True,
+                        step=k + 1) for k in range(T)]
+    table = zs.adam_table_device(cfgs, DEV)
+    counter = torch.zeros(1, dtype=torch.int64, device=DEV)
+    G = list(_state(S, 9)) + [torch.zeros(P, dtype=torch.int16, device=DEV)]
+    E = [t.clone() for t in G]
+    gr = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+
+    def table_step(st):
+        zs.adam_step_table(L, 0, len(units), table, T, counter, st[0], st[1], st[2], st[3],
+                           grads=gr)
+        zs.gather_params(L, 0, len(units), peers, st[3])
+        zs.step_advance(counter)
+
+    # warm-up with the counter at 0: no entry, so nothing is written
+    W = [t.clone() for t in G]
+    zs.adam_step_table(L, 0, len(units), table, T, counter, W[0], W[1], W[2], W[3], grads=gr)
+    torch.cuda.synchronize()
+    for a, b in zip(W, G):
+        _same(a, b, "counter 0 must leave the state untouched")
+    counter.fill_(1)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        table_step(G)
+    for k in range(T):
+        zs.adam_step(L, 0, len(units), cfgs[k], E[0], E[1], E[2], E[3], grads=gr)
+        zs.gather_params(L, 0, len(units), peers, E[3])
+        graph.replay()
+        _noise()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(G, E)):
+            _same(a, b, f"step {k + 1}, output {i}")
+        assert int(counter.item()) == k + 2
+    before = [t.clone() for t in G]
+    graph.replay()                      # counter T + 1: past the table
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(G, before)):
+        _same(a, b, f"past the table, output {i}")
