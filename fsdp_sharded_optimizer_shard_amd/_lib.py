@@ -107,6 +107,9 @@ class _UnitIO(ctypes.Structure):
 _lib.zero_fsdp_sweep.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _I32,
                                  ctypes.POINTER(_UnitIO), _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_sweep.restype = _I32
+_lib.zero_fsdp_sweep_table.argtypes = [_P, _I32, _I32, _P, _I64, _P, _I32,
+                                       ctypes.POINTER(_UnitIO), _P, _P, _P, _I32, _P, _P]
+_lib.zero_fsdp_sweep_table.restype = _I32
 _lib.zero_gemm_bf16.argtypes = [_I64, _I64, _I64, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I32,
                                 _P]
 _lib.zero_gemm_bf16.restype = _I32
@@ -131,7 +134,8 @@ EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_
            "zero_layout_info", "zero_layout_query", "zero_reduce_shard",
            "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
            "zero_adam_table_fill", "zero_adam_step_table", "zero_step_advance", "zero_gather_params",
-           "zero_grad_accumulate", "zero_fsdp_sweep", "zero_gemm_bf16", "zero_gemm_bf16_nt",
+           "zero_grad_accumulate", "zero_fsdp_sweep", "zero_fsdp_sweep_table", "zero_gemm_bf16",
+           "zero_gemm_bf16_nt",
            "zero_transpose_bf16", "zero_fsdp_linear_forward", "zero_fsdp_linear_backward",
            "zero_status_str", "zero_last_error")
 
@@ -344,13 +348,7 @@ def _need_len(what: str, seq, n: int) -> None:
         raise ValueError(f"{what}: expected {n} entries, got {len(seq)}")
 
 
-def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, grad_dtype: int,
-               units, master, m, v, max_inflight: int = 2, step_stream=None,
-               gather_stream=None) -> None:
-    """units: one (rank_grads, peer_shards, unit_full) per unit of the range;
-    rank_grads are world_n buffers and peer_shards one per slice (world_n,
-    or 1 under DDP; None allowed).  gather_stream defaults to step_stream
-    (sequential)."""
+def _unit_ios(layout: Layout, unit_begin: int, unit_end: int, units):
     if 0 <= unit_begin <= unit_end:
         _need_len("units", units, unit_end - unit_begin)
         n, parts = layout.info()["world_n"], _parts(layout)
@@ -364,11 +362,36 @@ def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, gra
         p = (ctypes.c_void_p * max(1, len(peers)))(*[_addr(x) for x in peers])
         keep += [g, p]
         arr[i] = _UnitIO(g, p, _addr(full))
+    return arr, keep
+
+
+def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, grad_dtype: int,
+               units, master, m, v, max_inflight: int = 2, step_stream=None,
+               gather_stream=None) -> None:
+    """units: one (rank_grads, peer_shards, unit_full) per unit of the range;
+    rank_grads are world_n buffers and peer_shards one per slice (world_n,
+    or 1 under DDP; None allowed).  gather_stream defaults to step_stream
+    (sequential)."""
+    arr, keep = _unit_ios(layout, unit_begin, unit_end, units)
     ss = _stream(step_stream)
     gs = ss if gather_stream is None else _stream(gather_stream)
     _check(_lib.zero_fsdp_sweep(layout.handle, unit_begin, unit_end, ctypes.byref(cfg), grad_dtype,
                                 arr, _addr(master), _addr(m), _addr(v), max_inflight, ss, gs),
            "zero_fsdp_sweep")
+
+
+def fsdp_sweep_table(layout: Layout, unit_begin: int, unit_end: int, table, n_entries: int,
+                     step_counter, grad_dtype: int, units, master, m, v, max_inflight: int = 2,
+                     step_stream=None, gather_stream=None) -> None:
+    """fsdp_sweep with the step scalars of table[*step_counter - 1] (device
+    table and counter); advances the counter once, after the last unit."""
+    arr, keep = _unit_ios(layout, unit_begin, unit_end, units)
+    ss = _stream(step_stream)
+    gs = ss if gather_stream is None else _stream(gather_stream)
+    _check(_lib.zero_fsdp_sweep_table(layout.handle, unit_begin, unit_end, _addr(table),
+                                      n_entries, _addr(step_counter), grad_dtype, arr,
+                                      _addr(master), _addr(m), _addr(v), max_inflight, ss, gs),
+           "zero_fsdp_sweep_table")
 
 
 def gemm_bf16(M: int, N: int, K: int, A, lda: int, a_order: int, B, ldb: int, b_order: int, C,

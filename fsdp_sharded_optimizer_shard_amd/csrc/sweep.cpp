@@ -46,19 +46,22 @@ zero_status hip_check(hipError_t e, const char *what)
     return ZERO_OK;
 }
 
-}  // namespace
 
-extern "C" zero_status zero_fsdp_sweep(const zero_layout *L, int32_t ub, int32_t ue,
-                                       const zero_adam_cfg *cfg, int32_t grad_dtype,
-                                       const zero_unit_io *io, float *master, float *m, float *v,
-                                       int32_t max_inflight, void *step_stream,
-                                       void *gather_stream)
+// The schedule shared by both sweeps: validation of the per-unit buffers,
+// then per unit step_unit(u, grads, so, unit_full) on the step stream and
+// its gather on the gather stream.  `finish` runs on the step stream after
+// the last unit's step.
+template <typename StepUnit, typename Finish>
+zero_status sweep(const zero_layout *L, int32_t ub, int32_t ue, int32_t grad_dtype,
+                  const zero_unit_io *io, float *master, float *m, float *v,
+                  int32_t max_inflight, void *step_stream, void *gather_stream,
+                  StepUnit step_unit, Finish finish)
 {
     zero_status st = zs::check_range(L, ub, ue);
     if (st != ZERO_OK)
         return st;
-    if (!cfg || (!io && ue > ub))
-        return zs::fail(ZERO_ERR_INVALID_ARG, "cfg and io are required");
+    if (!io && ue > ub)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "io is required");
     if (max_inflight < 0)
         return zs::fail(ZERO_ERR_INVALID_ARG, "max_inflight must be >= 0");
     if (grad_dtype != ZERO_BF16 && grad_dtype != ZERO_FP32)
@@ -112,9 +115,7 @@ extern "C" zero_status zero_fsdp_sweep(const zero_layout *L, int32_t ub, int32_t
             return st;
         const zero_grads g{x.rank_grads, nullptr, n, grad_dtype, ZERO_INDEX_SHARD, 0};
         const int64_t so = L->shard_off[u] - L->shard_off[ub];
-        st = zero_adam_step(L, u, u + 1, cfg, nullptr, ZERO_INDEX_SHARD, nullptr, &g, master + so,
-                            m + so, v + so, x.unit_full, ZERO_INDEX_FULL, step_stream);
-        if (st != ZERO_OK)
+        if ((st = step_unit(u, g, so, x.unit_full)) != ZERO_OK)
             return st;
         if (two) {
             if ((st = hip_check(hipEventRecord(stepped.ev[k], ss), "hipEventRecord")) != ZERO_OK ||
@@ -128,7 +129,53 @@ extern "C" zero_status zero_fsdp_sweep(const zero_layout *L, int32_t ub, int32_t
         if (two && (st = hip_check(hipEventRecord(gathered.ev[k], gs), "hipEventRecord")) != ZERO_OK)
             return st;
     }
+    if ((st = finish()) != ZERO_OK)
+        return st;
     if (two && U > 0)
         return hip_check(hipStreamWaitEvent(ss, gathered.ev[U - 1], 0), "hipStreamWaitEvent");
     return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" zero_status zero_fsdp_sweep(const zero_layout *L, int32_t ub, int32_t ue,
+                                       const zero_adam_cfg *cfg, int32_t grad_dtype,
+                                       const zero_unit_io *io, float *master, float *m, float *v,
+                                       int32_t max_inflight, void *step_stream,
+                                       void *gather_stream)
+{
+    if (!cfg)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "cfg is required");
+    return sweep(L, ub, ue, grad_dtype, io, master, m, v, max_inflight, step_stream,
+                 gather_stream,
+                 [&](int32_t u, const zero_grads &g, int64_t so, uint16_t *full) {
+                     return zero_adam_step(L, u, u + 1, cfg, nullptr, ZERO_INDEX_SHARD, nullptr,
+                                           &g, master + so, m + so, v + so, full,
+                                           ZERO_INDEX_FULL, step_stream);
+                 },
+                 [] { return ZERO_OK; });
+}
+
+extern "C" zero_status zero_fsdp_sweep_table(const zero_layout *L, int32_t ub, int32_t ue,
+                                             const zero_adam_table_entry *table,
+                                             int64_t n_entries, int64_t *step_counter,
+                                             int32_t grad_dtype, const zero_unit_io *io,
+                                             float *master, float *m, float *v,
+                                             int32_t max_inflight, void *step_stream,
+                                             void *gather_stream)
+{
+    if (!table || !step_counter || n_entries < 1)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "table, step_counter and n_entries >= 1 are "
+                        "required");
+    if (reinterpret_cast<uintptr_t>(table) % 4 || reinterpret_cast<uintptr_t>(step_counter) % 8)
+        return zs::fail(ZERO_ERR_ALIGNMENT, "misaligned step table or counter");
+    return sweep(L, ub, ue, grad_dtype, io, master, m, v, max_inflight, step_stream,
+                 gather_stream,
+                 [&](int32_t u, const zero_grads &g, int64_t so, uint16_t *full) {
+                     return zero_adam_step_table(L, u, u + 1, table, n_entries, step_counter,
+                                                 nullptr, ZERO_INDEX_SHARD, nullptr, &g,
+                                                 master + so, m + so, v + so, full,
+                                                 ZERO_INDEX_FULL, step_stream);
+                 },
+                 [&] { return zero_step_advance(step_counter, step_stream); });
 }

@@ -351,6 +351,19 @@ zero_status zero_fsdp_sweep(const zero_layout *layout, int32_t unit_begin,
                             int32_t max_inflight, void *step_stream,
                             void *gather_stream);
 
+/* zero_fsdp_sweep with each unit's step as zero_adam_step_table (scalars of
+   table[*step_counter - 1], read on the device), then *step_counter += 1 on
+   step_stream after the last unit's step: a graph captured from one call
+   replays as the sweeps of steps 1, 2, 3, ... .  Arguments and errors
+   otherwise as zero_fsdp_sweep and zero_adam_step_table. */
+zero_status zero_fsdp_sweep_table(const zero_layout *layout, int32_t unit_begin,
+                                  int32_t unit_end, const zero_adam_table_entry *table,
+                                  int64_t n_entries, int64_t *step_counter,
+                                  int32_t grad_dtype, const zero_unit_io *io,
+                                  float *master, float *m, float *v,
+                                  int32_t max_inflight, void *step_stream,
+                                  void *gather_stream);
+
 /* ------------------------------------------------------- accumulation -- */
 
 /* Megatron-style fp32 main-gradient accumulation of one micro-batch:

@@ -415,3 +415,20 @@ def test_adam_table_validation():
     assert _err(step, table=FAKE + 2).status == zs.ERR_ALIGNMENT
     assert _err(zs.step_advance, None, stream=0).status == zs.ERR_INVALID_ARG
     assert _err(zs.step_advance, FAKE + 4, stream=0).status == zs.ERR_ALIGNMENT
+
+
+def test_fsdp_sweep_table_validation_launches_nothing():
+    L = zs.shard_init("fsdp", 4, 3, [4096, 100])
+    good = ([FAKE] * 4, [FAKE, FAKE, FAKE, None], FAKE)
+
+    def sweep(table=FAKE, n=4, counter=FAKE, units=(good, good)):
+        zs.fsdp_sweep_table(L, 0, 2, table, n, counter, zs.BF16, list(units), FAKE, FAKE, FAKE,
+                            2, 0, 0)
+
+    assert _err(sweep, table=None).status == zs.ERR_INVALID_ARG
+    assert _err(sweep, n=0).status == zs.ERR_INVALID_ARG
+    assert _err(sweep, counter=None).status == zs.ERR_INVALID_ARG
+    assert _err(sweep, counter=FAKE + 4).status == zs.ERR_ALIGNMENT
+    bad = ([FAKE, None, FAKE, FAKE], [FAKE, FAKE, FAKE, None], FAKE)
+    e = _err(sweep, units=(good, bad))
+    assert e.status == zs.ERR_INVALID_ARG and "unit 1" in str(e)
