@@ -50,8 +50,9 @@
 // tiles, walked 4 tile rows at a time, so the blocks that share an L2 share
 // A rows and B columns.
 //
-// Both operands K-inner (dY W^T): the same pipeline on 16x16x32 MFMAs
-// (gemm_tile16) with its own chunk swizzle, about 6 % faster there.
+// Both operands K-inner (dY W^T): 16x16x32 MFMAs and 64-k stage pairs
+// (gemm_tile_kp, below), so that every DMA instruction moves whole cache
+// lines.
 //
 // MFMA 32x32x16 bf16 lane layout (checked on the device against an exact
 // CPU product): lane l holds A row (l % 32), k = 8 (l / 32) .. +7, and B
@@ -96,15 +97,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// K-inner stage: byte offset of the 16-byte chunk c (of 4) of row r, under
-// the chunk swizzle of the MFMA shape that reads it: (r >> 2) & 3 for the
-// 32x32x16 fragments (SW = 0), (r >> 1) & 3 for the 16x16x32 ones (SW = 1).
-// Each is free of bank conflicts for its own reads and not for the other's
-// (rocprofv3: 44 M and 29 M conflict cycles per launch the wrong way round).
-template <int SW>
-__device__ __forceinline__ int ki_swz(int r) { return SW ? (r >> 1) & 3 : (r >> 2) & 3; }
-template <int SW = 0>
-__device__ __forceinline__ int ki_pos(int r, int c) { return r * 64 + ((c ^ ki_swz<SW>(r)) << 4); }
+// K-inner stage of the 32x32x16 tile: byte offset of the 16-byte chunk c
+// (of 4) of row r, swizzled by (r >> 2) & 3 so that the fragment reads are
+// free of bank conflicts.
+__device__ __forceinline__ int ki_swz(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int ki_pos(int r, int c) { return r * 64 + ((c ^ ki_swz(r)) << 4); }
 
 // Buffer descriptor over `bytes` bytes from `base` (clamped to 2^31 - 1;
 // the host bounds every offset below that).
@@ -168,12 +165,12 @@ __device__ __forceinline__ int unit_at(int pos, int kr)
     return x ^ ((x & 1) << 2);
 }
 
-template <int R, bool KOUTER, int SW = 0>
+template <int R, bool KOUTER>
 __device__ __forceinline__ uint32_t dma_offset(int64_t ld, int wave, int lane, int n)
 {
     const int I = wave + kNW * n;
     if (!KOUTER) {
-        const int r = 16 * I + (lane >> 2), c = (lane & 3) ^ ki_swz<SW>(r);
+        const int r = 16 * I + (lane >> 2), c = (lane & 3) ^ ki_swz(r);
         return (uint32_t)((r * ld + 8 * c) * 2);
     }
     constexpr int KPI = Op<R, true>::KPI, LPR = 64 / KPI;  // lanes per k row
@@ -183,11 +180,10 @@ __device__ __forceinline__ uint32_t dma_offset(int64_t ld, int wave, int lane, i
 }
 
 // The k offset within the stage of a K-inner lane's chunk (for the K tail).
-template <int SW = 0>
 __device__ __forceinline__ int dma_kofs(int wave, int lane, int n)
 {
     const int r = 16 * (wave + kNW * n) + (lane >> 2);
-    return 8 * ((lane & 3) ^ ki_swz<SW>(r));
+    return 8 * ((lane & 3) ^ ki_swz(r));
 }
 
 // First LDS read offset of the fragment of rows w0 .. w0 + 31 at k
@@ -435,41 +431,61 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K,
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// The K-inner x K-inner tile on v_mfma_f32_16x16x32_bf16 (lane l: row l % 16,
-// k 8 (l / 16) .. +7; accumulator v: row 4 (l / 16) + v, column l % 16).  Each
-// wave owns (BM / 2) x 64 as (BM / 32) x 4 tiles of 16 x 16, one 32-k substep
-// per stage.  The wait and the barrier sit at the start of each tile, so the
-// next tile's fragments are read under all of this tile's MFMAs.  Its K-inner
-// stages use the SW = 1 chunk swizzle.  Paired against the 32x32x16 tile on
-// dX (4096 x 4096 x 14336, random operands): +4.4 %, and +1.8 % more with
-// that swizzle; bit-identical.  With a K-outer operand the 16x16x32 form was no
-// faster (forward 0.98 x) or spilled registers inside the loop (dW 0.60 x),
-// so those orders keep gemm_tile.
-template <int BM, bool OUT_BF16>
-__device__ __forceinline__ void gemm_tile16(int64_t M, int64_t N, int64_t K,
-                                            const uint16_t *__restrict__ A, int64_t lda,
-                                            const uint16_t *__restrict__ B, int64_t ldb,
-                                            void *__restrict__ C, int64_t ldc, int64_t m0, int64_t n0,
-                                            ZS_LDS char *const (&As)[kStages],
-                                            ZS_LDS char *const (&Bs)[kStages])
+// Both operands K-inner (dY W^T) run on 16x16x32 MFMAs with K in 64-k stage
+// pairs: a K-inner row chunk of one 32-k tile is 64 bytes, half a cache line,
+// so one DMA instruction would touch 16 lines; a pair buffer holds 64 k per
+// row, and each DMA instruction moves 8 whole 128-byte rows.  Two pair
+// buffers per operand (128 KB).  The pair of tiles 2p, 2p + 1 is fetched at
+// the start of tile 2p - 3, once the reads of pair p - 2 are done, and first
+// read during tile 2p - 1: two tiles of lead, as with single stages.
+// Paired against single 32-k stages: dX +10.6 %, bit-identical.
+// Row r of a pair buffer holds k 0..63 of the pair as eight 16-byte chunks,
+// chunk c at slot c ^ ((r >> 1) & 7); one DMA instruction moves 8 whole
+// 128-byte rows.
+__device__ __forceinline__ int kp_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int kp_pos(int r, int c) { return r * 128 + ((c ^ kp_swz(r)) << 4); }
+__device__ __forceinline__ uint32_t kp_dma_offset(int64_t ld, int wave, int lane, int n)
 {
+    const int r = 8 * (wave + kNW * n) + (lane >> 3), c = (lane & 7) ^ kp_swz(r);
+    return (uint32_t)((r * ld + 8 * c) * 2);
+}
+__device__ __forceinline__ int kp_kofs(int wave, int lane, int n)
+{
+    const int r = 8 * (wave + kNW * n) + (lane >> 3);
+    return 8 * ((lane & 7) ^ kp_swz(r));
+}
+constexpr int kPair = kBM * 128;  // bytes of one operand's pair buffer
+
+template <int BM, bool OUT_BF16>
+__device__ __forceinline__ void gemm_tile_kp(int64_t M, int64_t N, int64_t K,
+                                             const uint16_t *__restrict__ A, int64_t lda,
+                                             const uint16_t *__restrict__ B, int64_t ldb,
+                                             void *__restrict__ C, int64_t ldc, int64_t m0, int64_t n0,
+                                             ZS_LDS char *A0, ZS_LDS char *A1, ZS_LDS char *B0,
+                                             ZS_LDS char *B1)
+{
+    auto Ab = [&](auto pb) -> ZS_LDS char * {
+        if constexpr (decltype(pb)::value == 0) return A0; else return A1;
+    };
+    auto Bb = [&](auto pb) -> ZS_LDS char * {
+        if constexpr (decltype(pb)::value == 0) return B0; else return B1;
+    };
     constexpr int TM = BM / 32, TN = 4;
     constexpr int NF = TM + TN, NMF = TM * TN;
-    constexpr int NIA = Op<BM, false>::NI, NIB = Op<kBN, false>::NI;
-    constexpr int D = NIA + NIB;
+    constexpr int NPA = BM / (8 * kNW), NPB = kBN / (8 * kNW);
+    constexpr int DP = NPA + NPB;  // DMA instructions per wave per pair
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wm = (wave >> 2) * (BM / 2), wn = (wave & 3) * (kBN / 4);
     const int r16 = lane & 15, g = lane >> 4;
 
     uint32_t va[4], vb[4];
-    int ka[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-        va[n] = n < NIA ? dma_offset<BM, false, 1>(lda, wave, lane, n) : 0u;
-        vb[n] = n < NIB ? dma_offset<kBN, false, 1>(ldb, wave, lane, n) : 0u;
-        ka[n] = dma_kofs<1>(wave, lane, n);
+        va[n] = n < NPA ? kp_dma_offset(lda, wave, lane, n) : 0u;
+        vb[n] = n < NPB ? kp_dma_offset(ldb, wave, lane, n) : 0u;
     }
-    const int fa_off = ki_pos<1>(wm + r16, g), fb_off = ki_pos<1>(wn + r16, g);
+    const int fa_off[2] = {kp_pos(wm + r16, g), kp_pos(wm + r16, 4 + g)};
+    const int fb_off[2] = {kp_pos(wn + r16, g), kp_pos(wn + r16, 4 + g)};
 
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -478,33 +494,35 @@ __device__ __forceinline__ void gemm_tile16(int64_t M, int64_t N, int64_t K,
         for (int j = 0; j < TN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t kt_n = (K + kBK - 1) / kBK, kt_full = K / kBK;
-    auto dma = [&](auto st, auto whole, int64_t kt) {
-        constexpr int S = decltype(st)::value;
+    const int64_t kt_n = (K + kBK - 1) / kBK;
+    const int64_t np_n = (kt_n + 1) / 2, np_full = K / (2 * kBK);
+    auto dma = [&](auto pb, auto whole, int64_t p) {
+        constexpr int P = decltype(pb)::value;
         constexpr bool WHOLE = decltype(whole)::value != 0;
-        const int64_t k0 = kt * kBK;
+        const int64_t k0 = p * 2 * kBK;
         const __amdgpu_buffer_rsrc_t ra = rsrc(A + m0 * lda + k0, ((M - 1 - m0) * lda + K - k0) * 2);
         const __amdgpu_buffer_rsrc_t rb = rsrc(B + n0 * ldb + k0, ((N - 1 - n0) * ldb + K - k0) * 2);
 #pragma unroll
-        for (int n = 0; n < NIA; ++n) {
-            const uint32_t o = !WHOLE && k0 + ka[n] >= K ? kOOB : va[n];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (ZS_LDS void *)(As[S] + (wave + kNW * n) * 1024), 16, o, 0, 0, 0);
+        for (int n = 0; n < NPA; ++n) {
+            const uint32_t o = !WHOLE && k0 + kp_kofs(wave, lane, n) >= K ? kOOB : va[n];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (ZS_LDS void *)(Ab(IC<P>{}) + (wave + kNW * n) * 1024), 16, o, 0, 0, 0);
         }
 #pragma unroll
-        for (int n = 0; n < NIB; ++n) {
-            const uint32_t o = !WHOLE && k0 + ka[n] >= K ? kOOB : vb[n];
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ZS_LDS void *)(Bs[S] + (wave + kNW * n) * 1024), 16, o, 0, 0, 0);
+        for (int n = 0; n < NPB; ++n) {
+            const uint32_t o = !WHOLE && k0 + kp_kofs(wave, lane, n) >= K ? kOOB : vb[n];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (ZS_LDS void *)(Bb(IC<P>{}) + (wave + kNW * n) * 1024), 16, o, 0, 0, 0);
         }
     };
     bf16x8 fa[2][TM], fb[2][TN];
-    auto frags = [&](auto st, auto set) {
-        constexpr int S = decltype(st)::value, F = decltype(set)::value;
+    // fragments of a tile held in pair buffer P, half H, into set F
+    auto frags = [&](auto pb, auto hb, auto set) {
+        constexpr int P = decltype(pb)::value, H = decltype(hb)::value, F = decltype(set)::value;
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            fb[F][j] = *reinterpret_cast<const ZS_LDS bf16x8 *>(Bs[S] + fb_off + j * 1024);
+            fb[F][j] = *reinterpret_cast<const ZS_LDS bf16x8 *>(Bb(IC<P>{}) + fb_off[H] + j * 2048);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            fa[F][i] = *reinterpret_cast<const ZS_LDS bf16x8 *>(As[S] + fa_off + i * 1024);
+            fa[F][i] = *reinterpret_cast<const ZS_LDS bf16x8 *>(Ab(IC<P>{}) + fa_off[H] + i * 2048);
     };
     auto mma = [&](auto set) {
         constexpr int F = decltype(set)::value;
@@ -512,55 +530,64 @@ __device__ __forceinline__ void gemm_tile16(int64_t M, int64_t N, int64_t K,
         for (int q = 0; q < NMF; ++q)
             acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[F][q / TN], fb[F][q % TN], acc[q / TN][q % TN], 0, 0, 0);
     };
-    auto tile = [&](auto st, auto set, auto steady, int64_t kt) {
-        constexpr int S = decltype(st)::value, F = decltype(set)::value;
+    // Tile kt (TI = kt mod 4): wait for tile kt + 1's pair (odd tiles) or only
+    // for the LDS reads (even tiles), barrier; odd tiles then DMA the pair
+    // two ahead into the buffer the previous pair released; read tile
+    // kt + 1's fragments under tile kt's MFMAs.
+    auto tile = [&](auto ti, auto steady, int64_t kt) {
+        constexpr int TI = decltype(ti)::value;
         constexpr bool STEADY = decltype(steady)::value != 0;
-        constexpr int SN = (S + kStages - 1) % kStages, S1 = (S + 1) % kStages;
+        constexpr bool ODD = TI & 1;
+        constexpr int F = TI & 1;
+        constexpr int T1 = (TI + 1) & 3;                 // tile kt + 1 mod 4
+        constexpr int P1 = (T1 >> 1) & 1, H1 = T1 & 1;   // its buffer and half
+        constexpr int PN = (((TI + 3) >> 1)) & 1;        // buffer of pair (kt + 3) / 2
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) {
-            wait_vm_lgkm0<D>();
-        } else {
-            if (kt + 2 < kt_n) wait_vm_lgkm0<D>();
-            else wait_vm_lgkm0<0>();
-        }
+        if constexpr (ODD)
+            wait_vm_lgkm0<0>();
+        else
+            wait_vm_lgkm0<DP>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY)
-            dma(IC<SN>{}, IC<1>{}, kt + kStages - 1);
-        else if (kt + kStages - 1 < kt_n)
-            dma(IC<SN>{}, IC<0>{}, kt + kStages - 1);
+        if constexpr (ODD) {
+            const int64_t p = (kt + 3) / 2;
+            if constexpr (STEADY)
+                dma(IC<PN>{}, IC<1>{}, p);
+            else if (p < np_n)
+                dma(IC<PN>{}, IC<0>{}, p);
+        }
         if (STEADY || kt + 1 < kt_n)
-            frags(IC<S1>{}, IC<F ^ 1>{});
+            frags(IC<P1>{}, IC<H1>{}, IC<F ^ 1>{});
         mma(IC<F>{});
-        if constexpr (STEADY)
-            seq<NF, NMF, NF, D>();
+        if constexpr (STEADY && ODD)
+            seq<NF, NMF, NF, DP>();
         else
             seq<NF, NMF, NF, 0>();
     };
     if (kt_n > 0) {
         dma(IC<0>{}, IC<0>{}, 0);
-        if (kt_n > 1) dma(IC<1>{}, IC<0>{}, 1);
-        if (kt_n > 2) dma(IC<2>{}, IC<0>{}, 2);
-        {
-            const int64_t after = kt_n - 1;
-            if (after >= 2) wait_vm_lgkm0<2 * D>();
-            else if (after == 1) wait_vm_lgkm0<D>();
-            else wait_vm_lgkm0<0>();
+        if (np_n > 1) {
+            dma(IC<1>{}, IC<0>{}, 1);
+            wait_vm_lgkm0<DP>();
+        } else {
+            wait_vm_lgkm0<0>();
         }
         __builtin_amdgcn_s_barrier();
-        frags(IC<0>{}, IC<0>{});
+        frags(IC<0>{}, IC<0>{}, IC<0>{});
         int64_t kt = 0;
-        for (; kt + 2 * kStages - 1 <= kt_full; kt += kStages) {
-            tile(IC<0>{}, IC<0>{}, IC<1>{}, kt);
-            tile(IC<1>{}, IC<1>{}, IC<1>{}, kt + 1);
-            tile(IC<2>{}, IC<0>{}, IC<1>{}, kt + 2);
-            tile(IC<3>{}, IC<1>{}, IC<1>{}, kt + 3);
+        // steady: the pairs this group issues, (kt + 4) / 2 and (kt + 6) / 2,
+        // lie inside K
+        for (; (kt + 6) / 2 < np_full; kt += 4) {
+            tile(IC<0>{}, IC<1>{}, kt);
+            tile(IC<1>{}, IC<1>{}, kt + 1);
+            tile(IC<2>{}, IC<1>{}, kt + 2);
+            tile(IC<3>{}, IC<1>{}, kt + 3);
         }
-        for (; kt < kt_n; kt += kStages) {
-            tile(IC<0>{}, IC<0>{}, IC<0>{}, kt);
-            if (kt + 1 < kt_n) tile(IC<1>{}, IC<1>{}, IC<0>{}, kt + 1);
-            if (kt + 2 < kt_n) tile(IC<2>{}, IC<0>{}, IC<0>{}, kt + 2);
-            if (kt + 3 < kt_n) tile(IC<3>{}, IC<1>{}, IC<0>{}, kt + 3);
+        for (; kt < kt_n; kt += 4) {
+            tile(IC<0>{}, IC<0>{}, kt);
+            if (kt + 1 < kt_n) tile(IC<1>{}, IC<0>{}, kt + 1);
+            if (kt + 2 < kt_n) tile(IC<2>{}, IC<0>{}, kt + 2);
+            if (kt + 3 < kt_n) tile(IC<3>{}, IC<0>{}, kt + 3);
         }
     }
 #pragma unroll
@@ -603,23 +630,43 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(int64_t M, int64_t N, int64_t
     int tm, tn;
     if (b < n_big) {
         grouped(xcd_order(b, n_big), tiles_m, tiles_n, tm, tn);
-        if constexpr (!A_KOUTER && !B_KOUTER)
-            gemm_tile16<kBM, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, (int64_t)tm * kBM,
-                                       (int64_t)tn * kBN, As, Bs);
-        else
-            gemm_tile<kBM, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc,
-                                                         (int64_t)tm * kBM, (int64_t)tn * kBN, As,
-                                                         Bs);
+        gemm_tile<kBM, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc,
+                                                     (int64_t)tm * kBM, (int64_t)tn * kBN, As,
+                                                     Bs);
     } else {
         const int h = xcd_order(b - n_big, (int)gridDim.x - n_big);
         grouped(n_big + h / 2, tiles_m, tiles_n, tm, tn);
         const int64_t hm0 = (int64_t)tm * kBM + (h & 1) * (kBM / 2);
-        if constexpr (!A_KOUTER && !B_KOUTER)
-            gemm_tile16<kBM / 2, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, hm0,
-                                           (int64_t)tn * kBN, As, Bs);
-        else
-            gemm_tile<kBM / 2, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, hm0,
-                                                             (int64_t)tn * kBN, As, Bs);
+        gemm_tile<kBM / 2, A_KOUTER, B_KOUTER, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, hm0,
+                                                         (int64_t)tn * kBN, As, Bs);
+    }
+}
+
+// The both-K-inner order: gemm_tile_kp with its pair buffers, whole tiles and
+// half tiles as in gemm_kernel.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kGT) void gemm_kernel_kp(int64_t M, int64_t N, int64_t K,
+                                                      const uint16_t *__restrict__ A, int64_t lda,
+                                                      const uint16_t *__restrict__ B, int64_t ldb,
+                                                      void *__restrict__ C, int64_t ldc, int tiles_m,
+                                                      int tiles_n, int n_big)
+{
+    __shared__ __attribute__((aligned(1024))) char pa0[kPair], pa1[kPair];
+    __shared__ __attribute__((aligned(1024))) char pb0[kPair], pb1[kPair];
+    const int b = blockIdx.x;
+    int tm, tn;
+    if (b < n_big) {
+        grouped(xcd_order(b, n_big), tiles_m, tiles_n, tm, tn);
+        gemm_tile_kp<kBM, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, (int64_t)tm * kBM,
+                                    (int64_t)tn * kBN, (ZS_LDS char *)pa0, (ZS_LDS char *)pa1,
+                                    (ZS_LDS char *)pb0, (ZS_LDS char *)pb1);
+    } else {
+        const int h = xcd_order(b - n_big, (int)gridDim.x - n_big);
+        grouped(n_big + h / 2, tiles_m, tiles_n, tm, tn);
+        const int64_t hm0 = (int64_t)tm * kBM + (h & 1) * (kBM / 2);
+        gemm_tile_kp<kBM / 2, OUT_BF16>(M, N, K, A, lda, B, ldb, C, ldc, hm0, (int64_t)tn * kBN,
+                                        (ZS_LDS char *)pa0, (ZS_LDS char *)pa1, (ZS_LDS char *)pb0,
+                                        (ZS_LDS char *)pb1);
     }
 }
 
@@ -765,11 +812,17 @@ zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, i
     hipLaunchKernelGGL((zs::gemm_kernel<AO, BO, BF>), grid, block, 0, s, M, N, K, A, lda, B, ldb, \
                        C, ldc, (int)tm, (int)tn, (int)n_big)
     switch (code) {
-    case 0: ZS_GEMM(false, false, false); break;
+    case 0:
+        hipLaunchKernelGGL((zs::gemm_kernel_kp<false>), grid, block, 0, s, M, N, K, A, lda, B, ldb,
+                           C, ldc, (int)tm, (int)tn, (int)n_big);
+        break;
+    case 4:
+        hipLaunchKernelGGL((zs::gemm_kernel_kp<true>), grid, block, 0, s, M, N, K, A, lda, B, ldb,
+                           C, ldc, (int)tm, (int)tn, (int)n_big);
+        break;
     case 1: ZS_GEMM(true, false, false); break;
     case 2: ZS_GEMM(false, true, false); break;
     case 3: ZS_GEMM(true, true, false); break;
-    case 4: ZS_GEMM(false, false, true); break;
     case 5: ZS_GEMM(true, false, true); break;
     case 6: ZS_GEMM(false, true, true); break;
     default: ZS_GEMM(true, true, true); break;
