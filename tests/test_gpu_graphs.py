@@ -114,6 +114,57 @@ def test_two_pass_clip_in_a_graph():
     assert float(E[6]) < 1.0
 
 
+def test_table_clip_steps_replayed_from_one_graph():
+    """The two-pass clip path captured once, [reduce with partials, clip
+    coefficient, zero_adam_step_table from the fp32 gradient, step advance],
+    replays as steps 1..T with a learning-rate schedule and new gradients
+    each step, bit-identical to the eager path with zero_adam_step."""
+    units, n, r, T = [25000, 9001], 4, 2, 4
+    L = zs.shard_init("zero2", n, r, units)
+    S, P = L.shard_len, L.flat_len
+    U = len(units)
+    w = small_workload(units, n, "zero2", cfg=12)
+    npart = zs.reduce_partials_count(L, 0, U)
+    cfgs = [zs.adam_cfg(lr=1e-3 * (1.0 - 0.2 * k), weight_decay=0.01, decoupled=True,
+                        step=k + 1) for k in range(T)]
+    table = zs.adam_table_device(cfgs, DEV)
+    counter = torch.ones(1, dtype=torch.int64, device=DEV)
+    grads = [torch.empty(P, dtype=torch.int16, device=DEV) for _ in range(n)]
+    gr = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
+
+    def buffers():
+        master, m, v = _state(S, 11)
+        return [master, m, v, torch.zeros(P, dtype=torch.int16, device=DEV),
+                torch.empty(S, device=DEV), torch.empty(npart, dtype=torch.float64, device=DEV),
+                torch.empty(1, device=DEV)]
+
+    def two_pass(b, adam):
+        master, m, v, out, gsh, part, coef = b
+        zs.reduce_shard(L, 0, U, gr, gsh, part, npart)
+        # a small max_norm, so that the coefficient is below 1 and applied
+        zs.clip_coef(part, npart, 1e-3, coef)
+        adam(master, m, v, out, gsh, coef)
+
+    G, E = buffers(), buffers()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        two_pass(G, lambda *a: zs.adam_step_table(L, 0, U, table, T, counter, *a[:4],
+                                                  grad_fp32=a[4], clip_coef=a[5]))
+        zs.step_advance(counter)
+    for k in range(T):
+        for q in range(n):
+            grads[q].copy_(grad_bits(w, k, q, P, device=DEV))
+        two_pass(E, lambda *a: zs.adam_step(L, 0, U, cfgs[k], *a[:4], grad_fp32=a[4],
+                                            clip_coef=a[5]))
+        graph.replay()
+        _noise()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(G, E)):
+            _same(a, b, f"step {k + 1}, output {i}")
+        assert float(E[6]) < 1.0
+        assert int(counter.item()) == k + 2
+
+
 @pytest.mark.parametrize("ao,bo", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_gemm_in_a_graph(ao, bo):
     M, N, K = 264, 520, 200
