@@ -5,10 +5,10 @@ The arithmetic is the plain definition: average the N ranks' gradients, take
 one Adam step on the fp32 master state, round to bf16, lay the result out in
 the flat buffer.  Sharding changes who computes an element and where it is
 stored, never its value:
-  * DDP: every GPU holds a full replica, gradients are all-reduced so every
-    replica holds the average, then every replica takes the same optimizer
-    step ("Data Parallel, ZeRO and FSDP", section "Plain data parallel
-    (DDP)"; "Behind the scenes...", section on DDP).
+  * DDP: a full replica per GPU; the mean of the rank gradients reaches
+    every replica and all of them apply the same optimizer step ("Data
+    Parallel, ZeRO and FSDP", section "Plain data parallel (DDP)"; "Behind
+    the scenes...", section on DDP).
   * all-reduce = reduce-scatter (sum, each GPU keeps its 1/N) + all-gather
     (concatenate the 1/N slices) ("dp-zero-fsdp", concepts; "Behind the
     scenes...", section "ZeRO: The Dial Between DDP and FSDP").

@@ -56,6 +56,12 @@ MUTANTS = [
     ("clip coefficient not clamped at 1", C, "return c < 1.0f ? c : 1.0f;", "return c;"),
     ("clip divides by the sum of squares", C, "double norm = sqrt(sumsq);",
      "double norm = sumsq;"),
+    ("clip scale divides by the coefficient", C, "g[i] = g[i] * c;", "g[i] = g[i] / c;"),
+    ("clip scale by the reciprocal of the coefficient", C, "g[i] = g[i] * c;",
+     "g[i] = g[i] * (1.0f / c);"),
+    ("clip scale skips the last element", C,
+     "for (int64_t i = 0; i < count; ++i)\n        g[i] = g[i] * c;",
+     "for (int64_t i = 0; i + 1 < count; ++i)\n        g[i] = g[i] * c;"),
     # ---- Adam step scalars
     ("decay without lr", C,
      "s.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);",
@@ -133,6 +139,8 @@ MUTANTS = [
      "full[b:b + n] = shard[s:s + n]", "full[b + 1:b + n] = shard[s:s + n - 1]"),
     ("clip norm over rank 0's shard only", "strategies.py",
      "c = _clip_coefficient(cfg, g_mean_full)", "c = _clip_coefficient(cfg, shards[0])"),
+    ("sharded strategies skip the clip scale", "strategies.py",
+     "        if c < 1.0:\n            _c.scale(g, c)\n", ""),
     # ---- linear layer
     ("linear gather keeps the last rows", "linear.py", "return full[:rows]",
      "return full[full.shape[0] - rows:]"),

@@ -108,3 +108,70 @@ def test_clip_coefficient_rounding():
     for s, mx in [(39.6 ** 2, 1.0), (2.0, 1.0), (1e-12, 1.0), (1e6, 0.5)]:
         want = min(1.0, float(np.float32(mx / (np.sqrt(s) + 1e-6))))
         assert _c.clip_coef(s, mx) == np.float32(want)
+
+
+@pytest.mark.parametrize("c", [np.float32(1.0 / 39.6), np.float32(0.5), np.float32(0.3),
+                               np.float32(1.0 / (8.0 + 1e-6)), np.nextafter(np.float32(1), np.float32(0))])
+def test_scale_is_the_correctly_rounded_product(c):
+    # g <- g * c rounds the exact product once to binary32 (ties to even),
+    # checked against exact rationals; magnitudes span normal gradients,
+    # outliers and the subnormal range, where a product by c < 1 loses bits
+    rng = np.random.default_rng(int(c.view(np.uint32)))
+    k = 3000
+    mags = 10.0 ** rng.uniform(-42, 2, k)
+    g = (mags * rng.choice([-1.0, 1.0], k)).astype(np.float32)
+    g[:4] = [0.0, -0.0, 2.0 ** -149, -(2.0 ** -126)]
+    want = [rn32(Fr(float(x)) * Fr(float(c))) for x in g]
+    got = g.copy()
+    _c.scale(got, float(c))
+    for i in range(k):
+        w, x = np.float32(want[i]), got[i]
+        # a zero product keeps the sign of g (c > 0)
+        if w == 0:
+            w = np.float32(np.copysign(0.0, g[i]))
+        assert x.view(np.uint32) == w.view(np.uint32), (i, g[i], x, w)
+
+
+def test_scale_keeps_inf_and_nan():
+    g = np.array([np.inf, -np.inf, np.nan], np.float32)
+    _c.scale(g, 0.25)
+    assert g[0] == np.inf and g[1] == -np.inf and np.isnan(g[2])
+
+
+@pytest.mark.parametrize("n,k_exp,max_norm", [(4, -3, 1.0), (8, -7, 0.01), (2, 1, 3.0)])
+def test_clipped_first_moment_is_the_scaled_constant_gradient(n, k_exp, max_norm):
+    # every rank holds the constant gradient k = 2^k_exp over psi = 4096
+    # elements, so the mean is k, the norm 64|k| exactly, and the clip
+    # coefficient c = max_norm / (64|k| + 1e-6) < 1.  After one step from
+    # zero state the first moment is (1 - b1) * (k * c): checked against
+    # exact rationals through the C per-rank chain and through every
+    # strategy of the simulation.  Dividing by c, or scaling by anything but
+    # c, moves m by a factor near 1/c^2.
+    from oracle import strategies
+    psi = 4096
+    k = 2.0 ** k_exp
+    cfg = strategies.AdamConfig(max_grad_norm=max_norm)
+    hp = cfg.hparams(1)
+    c = np.float32(max_norm / (64.0 * k + 1e-6))
+    assert c < 1
+    omb1 = np.float32(1.0 - float(np.float32(cfg.beta1)))
+    g_c = rn32(Fr(k) * Fr(float(c)))
+    m_want = rn32(Fr(float(omb1)) * Fr(float(g_c)))
+    exact = Fr(float(omb1)) * Fr(k) * Fr(float(c))
+    assert abs(Fr(float(m_want)) - exact) <= 2 * Fr(float(np.spacing(np.float32(m_want))))
+
+    ranks = [bf16(np.full(psi, k)) for _ in range(n)]
+    coef = _c.clip_coef(_c.sumsq(_c.average(ranks)), max_norm)
+    assert np.float32(coef) == c
+    p = np.full(psi, 0.01, np.float32)
+    m = np.zeros(psi, np.float32)
+    v = np.zeros(psi, np.float32)
+    out = np.empty(psi, np.uint16)
+    _c.rank_step(hp, ranks, coef, p, m, v, out)
+    assert np.all(m == m_want)
+
+    for s in ("ddp", "zero2", "zero3", "megatron_do"):
+        cl = strategies.make_cluster(s, [psi], n, np.full(psi, 0.01, np.float32))
+        g = [[r] for r in ranks] if s == "megatron_do" else ranks
+        strategies.step(cl, cfg, 1, g)
+        assert np.all(strategies.full_state(cl)["m"] == m_want), s
