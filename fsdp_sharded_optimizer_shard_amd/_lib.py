@@ -32,6 +32,7 @@ DDP, STAGE1, STAGE2, STAGE3, FSDP, MEGATRON_DO = range(6)
 BF16, FP32 = 0, 1
 INDEX_FULL, INDEX_SHARD = 0, 1
 K_INNER, K_OUTER = 0, 1
+MIX_STEP_STREAMS, MIX_READS, MIX_WRITES = 0, 1, 2
 MAX_RANKS_PER_CALL = 64
 
 STRATEGY = {"ddp": DDP, "zero1": STAGE1, "zero1_allreduce": STAGE1, "zero2": STAGE2,
@@ -123,6 +124,9 @@ _lib.zero_fsdp_linear_forward.restype = _I32
 _lib.zero_fsdp_linear_backward.argtypes = [_P, _I32, ctypes.POINTER(ctypes.c_void_p), _I64, _P,
                                            _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_linear_backward.restype = _I32
+_lib.zero_stream_mix.argtypes = [_I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P, _P, _P,
+                                 _I64, _P]
+_lib.zero_stream_mix.restype = _I32
 _lib.zero_grad_accumulate.argtypes = [_P, _P, _I64, _P]
 _lib.zero_grad_accumulate.restype = _I32
 _lib.zero_status_str.argtypes = [_I32]
@@ -134,7 +138,7 @@ EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_
            "zero_layout_info", "zero_layout_query", "zero_reduce_shard",
            "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
            "zero_adam_table_fill", "zero_adam_step_table", "zero_step_advance", "zero_gather_params",
-           "zero_grad_accumulate", "zero_fsdp_sweep", "zero_fsdp_sweep_table", "zero_gemm_bf16",
+           "zero_grad_accumulate", "zero_stream_mix", "zero_fsdp_sweep", "zero_fsdp_sweep_table", "zero_gemm_bf16",
            "zero_gemm_bf16_nt",
            "zero_transpose_bf16", "zero_fsdp_linear_forward", "zero_fsdp_linear_backward",
            "zero_status_str", "zero_last_error")
@@ -430,6 +434,14 @@ def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy,
                                           _addr(dy), _addr(w_full), _addr(dx), dx_dtype,
                                           _addr(dw_full), _stream(stream)),
            "zero_fsdp_linear_backward")
+
+
+def stream_mix(kind: int, grads, master, m, v, param, n: int, stream=None) -> None:
+    """zero_stream_mix: the fused step's memory traffic without its
+    arithmetic (kind MIX_STEP_STREAMS), its reads alone (MIX_READS) or its
+    writes alone (MIX_WRITES), over n elements."""
+    _check(_lib.zero_stream_mix(kind, _ptrs(grads), len(grads), _addr(master), _addr(m), _addr(v),
+                                _addr(param), n, _stream(stream)), "zero_stream_mix")
 
 
 def grad_accumulate(main_grad, micro_bf16, n: int, stream=None) -> None:

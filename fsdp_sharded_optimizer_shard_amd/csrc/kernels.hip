@@ -5,12 +5,16 @@
 // (12 bytes), and writes master, m, v (12) and the bf16 parameter (2), for
 // about N + 20 flops -- far below the machine balance, so there is no
 // contraction and no MFMA.  The design rules that matter are the memory ones:
-//   * 2048-element tiles; in the step kernel each lane owns one group of 4
-//     consecutive elements so that every load / store instruction of a wave
-//     covers one contiguous run (fp32 streams in 128-bit accesses, bf16
-//     streams in 64-bit ones) and whole lines are written by one
-//     instruction -- rocprof FETCH_SIZE / WRITE_SIZE equal the algorithmic
-//     bytes;
+//   * the step kernel walks 1024-element tiles in 256-thread blocks, each
+//     lane owning one group of 4 consecutive elements, so that every load /
+//     store instruction of a wave covers one contiguous run (fp32 streams in
+//     128-bit accesses, bf16 streams in 64-bit ones) and whole lines are
+//     written by one instruction -- rocprof FETCH_SIZE / WRITE_SIZE equal the
+//     algorithmic bytes; the gather and the accumulation walk 2048-element
+//     tiles;
+//   * the step kernel runs at most 5 blocks (20 waves) per CU: fewer
+//     requests in flight mix the read and write streams better (measured
+//     below, at launch_one);
 //   * one pass: the reduce over ranks, the Adam update and the bf16 cast are
 //     fused so each byte crosses HBM once;
 //   * one launch covers a tile space that concatenates the slices of many
@@ -41,11 +45,15 @@
 namespace zs {
 namespace {
 
-constexpr int kTile = 2048;                 // elements per tile
+constexpr int kTile = 2048;                 // elements per gather / accumulate tile
 constexpr int kVec = 8;                     // gather: bf16 elements per 16-byte chunk
 constexpr int kMaxSegs = 32;                // units per launch (kernarg table)
-constexpr int kStepThreads = 512;           // step kernel: one 4-element group per lane
-constexpr int kStepWaveElems = kTile / (kStepThreads / 64);  // 256
+constexpr int kStepTile = 1024;             // elements per step-kernel tile
+constexpr int kStepThreads = 256;           // step kernel: one 4-element group per lane
+constexpr int kStepBlocksPerCU = 5;         // step kernel occupancy cap (LDS reservation)
+constexpr int kAccThreads = 512;            // accumulate: one 4-element group per lane
+constexpr int kWaveElems = 256;             // elements one wave covers (64 lanes x 4)
+static_assert(kStepTile == kStepThreads * 4 && kTile == kAccThreads * 4, "one group per lane");
 constexpr int kClipThreads = 1024;          // one block sums the clip partials
 constexpr int kMaxRanks = ZERO_MAX_RANKS_PER_CALL;
 
@@ -76,7 +84,10 @@ static_assert(offsetof(AdamScalars, omb1) == offsetof(zero_adam_table_entry, one
                   offsetof(AdamScalars, decoupled) == offsetof(zero_adam_table_entry, decoupled),
               "table entry layout");
 
-enum Mode { kFused = 0, kReduce = 1, kApply = 2 };
+// kFused / kReduce / kApply are the optimizer step's passes.  The last
+// three measure HBM rates of the fused pass's exact streams, tile walk and
+// launch shape with the Adam arithmetic taken out (zero_stream_mix).
+enum Mode { kFused = 0, kReduce = 1, kApply = 2, kMix = 3, kReadOnly = 4, kWriteOnly = 5 };
 
 struct StepArgs {
     const void *grads[kMaxRanks];
@@ -99,7 +110,7 @@ struct StepArgs {
     double *partials;    // kReduce: one fp64 sum of squares per tile, or null
     uint16_t *pout;      // bf16 parameter output
     int32_t pout_full;   // 1: full-indexed, 0: shard-indexed
-    int32_t _pad;
+    float sink_key;      // kReadOnly: a value no element equals (NaN)
     AdamScalars sc;
     const AdamScalars *table;  // non-null: scalars from table[*step - 1] instead of sc
     const int64_t *step;
@@ -307,16 +318,17 @@ __device__ double block_sum(double x)
 
 // -------------------------------------------------------- step kernel --
 //
-// Element ownership in a 2048-element tile: the step kernel runs 512-thread
+// Element ownership in a 1024-element tile: the step kernel runs 256-thread
 // blocks; wave w covers [256w, 256w + 256) and lane l owns the 4-element
 // group at 256w + 4l.  Every load or store instruction of a wave therefore
 // covers one contiguous run -- 512 bytes of a bf16 stream, 1 KiB of an fp32
 // stream -- so caches and HBM see whole lines written by one instruction.
 // (With 8 contiguous elements per lane, each 16-byte fp32 store instruction
 // filled only every other 16 bytes of its span and lines were written back
-// in halves.)  One group per lane keeps the kernel at 55 VGPRs, 8 waves per
-// SIMD; paired runs on the 7B / N = 8 step measured 2-3 % over 256-thread
-// blocks with two groups per lane (91 VGPRs, 5 waves).
+// in halves; 8 elements per lane with 128-bit bf16 loads and a
+// v_permlane32_swap hand-off that keeps the fp32 instructions on whole lines
+// measured 1.6 % slower than this.)  One group per lane keeps the kernel near
+// 55 VGPRs; two groups per lane (91 VGPRs) measured 2-3 % slower.
 
 // The fused / reduce / apply work for G full groups of 4 elements.
 template <int MODE, int NR, bool BF16, int G>
@@ -331,6 +343,19 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
         fi[h] = sg.full_off + j[h];
     }
     float p[G][4], m[G][4], v[G][4], g[G][4];
+    if constexpr (MODE == kWriteOnly) {
+        // the fused pass's four write streams, with values from the index
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float x = (float)j[h];
+            st_nt(reinterpret_cast<f32x4 *>(a.master + si[h]), f32x4{x, x, x, x});
+            st_nt(reinterpret_cast<f32x4 *>(a.m + si[h]), f32x4{x, x, x, x});
+            st_nt(reinterpret_cast<f32x4 *>(a.v + si[h]), f32x4{x, x, x, x});
+            st_nt(reinterpret_cast<u32x2 *>(a.pout + (a.pout_full ? fi[h] : si[h])),
+                  u32x2{(uint32_t)j[h], (uint32_t)j[h]});
+        }
+        return;
+    }
     if (MODE != kReduce) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -361,7 +386,19 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
         for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                g[h][e] = mean_of(a, acc[h][e]);
+                g[h][e] = MODE >= kMix ? acc[h][e] : mean_of(a, acc[h][e]);
+    }
+    if constexpr (MODE == kReadOnly) {
+        // every loaded value feeds a comparison the host makes false
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x = ((g[h][e] + p[h][e]) + m[h][e]) + v[h][e];
+                if (x == a.sink_key)
+                    a.master[si[h] + e] = x;
+            }
+        return;
     }
     if (MODE == kReduce) {
 #pragma unroll
@@ -377,16 +414,29 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            adam1(sc, g[h][e], p[h][e], m[h][e], v[h][e]);
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (MODE == kMix) {
+                p[h][e] = p[h][e] + g[h][e];
+                m[h][e] = m[h][e] + g[h][e];
+                v[h][e] = v[h][e] + g[h][e];
+            } else {
+                adam1(sc, g[h][e], p[h][e], m[h][e], v[h][e]);
+            }
+        }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         st_nt(reinterpret_cast<f32x4 *>(a.master + si[h]), f32x4{p[h][0], p[h][1], p[h][2], p[h][3]});
         st_nt(reinterpret_cast<f32x4 *>(a.m + si[h]), f32x4{m[h][0], m[h][1], m[h][2], m[h][3]});
         st_nt(reinterpret_cast<f32x4 *>(a.v + si[h]), f32x4{v[h][0], v[h][1], v[h][2], v[h][3]});
         u32x2 w;
-        w.x = to_bf16(p[h][0]) | (to_bf16(p[h][1]) << 16);
-        w.y = to_bf16(p[h][2]) | (to_bf16(p[h][3]) << 16);
+        if constexpr (MODE == kMix) {
+            // the upper halves: a bf16 stream without the rounding
+            w.x = (__float_as_uint(p[h][0]) >> 16) | (__float_as_uint(p[h][1]) & 0xffff0000u);
+            w.y = (__float_as_uint(p[h][2]) >> 16) | (__float_as_uint(p[h][3]) & 0xffff0000u);
+        } else {
+            w.x = to_bf16(p[h][0]) | (to_bf16(p[h][1]) << 16);
+            w.y = to_bf16(p[h][2]) | (to_bf16(p[h][3]) << 16);
+        }
         st_nt(reinterpret_cast<u32x2 *>(a.pout + (a.pout_full ? fi[h] : si[h])), w);
     }
 }
@@ -397,6 +447,9 @@ __device__ __forceinline__ void step_scalar(const StepArgs &a, const AdamScalars
                                             const Seg &sg, int64_t j,
                                             int64_t cnt, float coef, double &sq)
 {
+    if constexpr (MODE >= kMix) {
+        return;  // zero_stream_mix accepts whole 16-byte aligned groups only
+    } else {
     const int64_t si = sg.shard_off + j;
     const int64_t fi = sg.full_off + j;
     const int64_t oi = a.pout_full ? fi : si;
@@ -418,6 +471,7 @@ __device__ __forceinline__ void step_scalar(const StepArgs &a, const AdamScalars
             a.pout[oi + e] = (uint16_t)to_bf16(p);
         }
     }
+    }
 }
 
 template <int MODE, int NR, bool BF16>
@@ -438,7 +492,7 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(const StepArgs a)
     const TileWalk tw = tile_walk(a.n_tiles, MODE != kApply);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         const Seg &sg = a.seg[find_seg(a.seg, a.n_segs, t)];
-        const int64_t j[1] = {(t - sg.tile0) * kTile + wave * kStepWaveElems + lane * 4};
+        const int64_t j[1] = {(t - sg.tile0) * kStepTile + wave * kWaveElems + lane * 4};
         const bool vec = sg.vec && a.vec_ptrs;
         double sq = 0.0;  // kReduce: this thread's sum of squares in this tile
         if (j[0] < sg.len) {
@@ -515,15 +569,15 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(const GatherArgs
 
 // ------------------------------------------------- accumulate kernel --
 
-// The step kernel's ownership: 512-thread blocks, lane l of wave w owns the
-// 4-element group at 256w + 4l of each 2048-element tile (paired runs on a
-// 4e9-element buffer: 1.2-2 % faster than 256 threads with two groups per
-// lane).
-__global__ __launch_bounds__(kStepThreads) void accumulate_kernel(float *acc,
+// 512-thread blocks, lane l of wave w owns the 4-element group at 256w + 4l
+// of each 2048-element tile (paired runs on a 4e9-element buffer: 1.2-2 %
+// faster than 256 threads with two groups per lane; capping its occupancy
+// as the step kernel does measured 3.5-7 % slower).
+__global__ __launch_bounds__(kAccThreads) void accumulate_kernel(float *acc,
                                                                   const uint16_t *micro,
                                                                   int64_t n, int32_t vec)
 {
-    const int64_t lane_off = (threadIdx.x >> 6) * kStepWaveElems + (threadIdx.x & 63) * 4;
+    const int64_t lane_off = (threadIdx.x >> 6) * kWaveElems + (threadIdx.x & 63) * 4;
     const TileWalk tw = tile_walk((n + kTile - 1) / kTile, true);
     for (int64_t t = tw.t; t < tw.end; t += tw.stride) {
         const int64_t i = t * kTile + lane_off;
@@ -604,7 +658,7 @@ int device_cus()
     return cus;
 }
 
-// Launch width.  Default: one block per 2048-element tile.  Measured on
+// Launch width.  Default: one block per tile.  Measured on
 // MI355X (7B / N = 8 step, paired runs over six buffer placements) this beat
 // a persistent grid sized to the resident occupancy by 6 % on the fused
 // kernel and 12 % on the gather: the dispatcher hands out blocks in tile
@@ -624,10 +678,10 @@ int blocks_per_cu_override()
 }
 
 template <typename Kernel>
-int resident_blocks(Kernel kernel, int threads)
+int resident_blocks(Kernel kernel, int threads, size_t lds = 0)
 {
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, threads, lds) != hipSuccess ||
         nb < 1)
         nb = 4;
     return nb;
@@ -653,6 +707,31 @@ int64_t stream_grid(int64_t n_tiles, int resident, int threads)
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t tiles_of(int64_t len) { return (len + kTile - 1) / kTile; }
+int64_t step_tiles_of(int64_t len) { return (len + kStepTile - 1) / kStepTile; }
+
+// LDS bytes reserved per step-kernel block so that at most kStepBlocksPerCU
+// blocks share a CU (the kernel itself uses no LDS beyond a few bytes for
+// the clip partials).  From the device's LDS per CU (160 KiB on gfx950: 32
+// KiB per block), cached per device.
+size_t step_lds_reserve()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 32 * 1024;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        int lds = 0;
+        if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+                hipSuccess ||
+            lds <= 0)
+            lds = 160 * 1024;
+        v = (lds / kStepBlocksPerCU) & ~1023;
+        v = v > 64 * 1024 ? 64 * 1024 : (v < 1024 ? 1024 : v);
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return (size_t)v;
+}
 
 // Splits a unit range into launches of at most kMaxSegs units each and
 // calls fn(first_unit, last_unit_exclusive).
@@ -685,7 +764,7 @@ int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg 
         s.full_off = L->flat_off[u] - L->flat_off[ub] + (int64_t)L->rank * len;
         s.tile0 = tiles;
         s.vec = (s.shard_off % 4 == 0 && s.full_off % 4 == 0) ? 1 : 0;
-        tiles += tiles_of(len);
+        tiles += step_tiles_of(len);
     }
     *n_segs = k;
     return tiles;
@@ -754,13 +833,24 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
     return s;
 }
 
+// Occupancy of the step kernel.  Its launches reserve LDS so that at most 5
+// of its 256-thread blocks (20 waves) run on a CU at once.  Paired runs over
+// ten buffer placements (the 7B / N = 8 fused step, the apply pass and the
+// N = 64 Llama-70B unit), against the former 512-thread / 2048-element tiles
+// at full occupancy: fused 0.964 x (0.947-0.982 per placement), apply
+// 0.955 x, N = 64 0.973 x; the same 256-thread tiles at full occupancy
+// 0.985 x, with a 16-wave cap 0.965 x, 8 or 12 waves 0.99 x.  With fewer
+// requests in flight the memory controllers mix the read and write streams
+// better; the kernel's time is that of its memory traffic (the same streams
+// without the arithmetic run no faster; zero_stream_mix).
 template <int MODE, int NR, bool BF16>
 void launch_one(const StepArgs &a, hipStream_t st)
 {
-    static const int resident = resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads);
+    const size_t lds = step_lds_reserve();
+    static const int resident = resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads, lds);
     const int64_t blocks = stream_grid(a.n_tiles, resident, kStepThreads);
     hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kStepThreads),
-                       0, st, a);
+                       lds, st, a);
 }
 
 template <int MODE, bool BF16>
@@ -778,6 +868,22 @@ void launch_step(const StepArgs &a, hipStream_t st)
         default: launch_one<MODE, 0, BF16>(a, st); break;
         }
     }
+}
+
+// The calibration modes take bf16 rank buffers; N = 8 (the 7B step) has the
+// fused kernel's specialisation, other counts the generic loop.
+template <int MODE>
+zero_status launch_mix(const StepArgs &a, hipStream_t st)
+{
+    (void)hipGetLastError();
+    if (a.n_ranks == 8)
+        launch_one<MODE, 8, true>(a, st);
+    else
+        launch_one<MODE, 0, true>(a, st);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(ZERO_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ZERO_OK;
 }
 
 template <int MODE>
@@ -1090,6 +1196,53 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
     return ZERO_OK;
 }
 
+zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t n_ranks,
+                            float *master, float *m, float *v, uint16_t *param, int64_t n,
+                            void *stream)
+{
+    if (kind != ZERO_MIX_STEP_STREAMS && kind != ZERO_MIX_READS && kind != ZERO_MIX_WRITES)
+        return fail(ZERO_ERR_INVALID_ARG, "unknown stream-mix kind %d", kind);
+    if (n_ranks < 1 || n_ranks > kMaxRanks)
+        return fail(ZERO_ERR_INVALID_ARG, "n_ranks must lie in [1, %d] (got %d)", kMaxRanks,
+                    n_ranks);
+    if (n < 0 || n % 4)
+        return fail(ZERO_ERR_INVALID_ARG, "n must be a non-negative multiple of 4 (got %lld)",
+                    (long long)n);
+    if (!grads || !master || !m || !v || !param)
+        return fail(ZERO_ERR_INVALID_ARG, "grads, master, m, v and param are required");
+    bool al = aligned16(master) && aligned16(m) && aligned16(v) && aligned16(param);
+    for (int q = 0; q < n_ranks; ++q) {
+        if (!grads[q])
+            return fail(ZERO_ERR_INVALID_ARG, "gradient buffer of rank %d is NULL", q);
+        al = al && aligned16(grads[q]);
+    }
+    if (!al)
+        return fail(ZERO_ERR_ALIGNMENT, "every buffer must be 16-byte aligned");
+    if (n == 0)
+        return ZERO_OK;
+    StepArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int q = 0; q < n_ranks; ++q)
+        a.grads[q] = grads[q];
+    a.n_ranks = n_ranks;
+    a.vec_ptrs = 1;
+    a.n_segs = 1;
+    a.seg[0].len = n;
+    a.seg[0].vec = 1;
+    a.n_tiles = step_tiles_of(n);
+    a.master = master;
+    a.m = m;
+    a.v = v;
+    a.pout = param;
+    a.sink_key = __builtin_nanf("");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kind == ZERO_MIX_STEP_STREAMS)
+        return launch_mix<kMix>(a, s);
+    if (kind == ZERO_MIX_READS)
+        return launch_mix<kReadOnly>(a, s);
+    return launch_mix<kWriteOnly>(a, s);
+}
+
 zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro, int64_t n, void *stream)
 {
     if (!main_grad || !micro || n < 0)
@@ -1099,11 +1252,11 @@ zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro, int64_
     if (n == 0)
         return ZERO_OK;
     const int64_t tiles = tiles_of(n);
-    static const int resident = resident_blocks(accumulate_kernel, kStepThreads);
-    const int64_t grid = stream_grid(tiles, resident, kStepThreads);
+    static const int resident = resident_blocks(accumulate_kernel, kAccThreads);
+    const int64_t grid = stream_grid(tiles, resident, kAccThreads);
     const int32_t vec = aligned16(main_grad) && aligned16(micro);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(accumulate_kernel, dim3((unsigned)grid), dim3(kStepThreads), 0,
+    hipLaunchKernelGGL(accumulate_kernel, dim3((unsigned)grid), dim3(kAccThreads), 0,
                        static_cast<hipStream_t>(stream), main_grad, micro, n, vec);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -195,7 +195,7 @@ zero_status zero_layout_rows(const zero_layout *layout, int32_t unit,
    N ranks' calls together then form the all-reduce).
    If `sumsq_partials` is non-NULL it receives exactly
    zero_reduce_partials_count(...) fp64 partial sums of out[i]^2 (each square
-   exact in fp64; one partial per 2048-element tile of a unit slice, summed
+   exact in fp64; one partial per 1024-element tile of a unit slice, summed
    in a fixed order), for the global-norm clip; `n_partials` is the capacity
    of that buffer. */
 zero_status zero_reduce_shard(const zero_layout *layout, int32_t unit_begin,
@@ -205,7 +205,7 @@ zero_status zero_reduce_shard(const zero_layout *layout, int32_t unit_begin,
                               int64_t n_partials, void *stream);
 
 /* Number of fp64 partials zero_reduce_shard writes for a range: one per
-   2048-element tile of every unit slice in the range (a fixed function of
+   1024-element tile of every unit slice in the range (a fixed function of
    the range, independent of the device and of the launch width). */
 int64_t zero_reduce_partials_count(const zero_layout *layout,
                                    int32_t unit_begin, int32_t unit_end);
@@ -370,6 +370,35 @@ zero_status zero_fsdp_sweep_table(const zero_layout *layout, int32_t unit_begin,
    main_grad[i] = main_grad[i] + float(micro_bf16[i]) for i < n. */
 zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro_bf16,
                                  int64_t n, void *stream);
+
+/* ---------------------------------------------- rate calibration -- */
+
+/* HBM rate of the fused step's memory traffic without its arithmetic, for
+   measuring the step kernel against the ceiling of its own access pattern
+   (a measurement aid, not part of the optimizer step).  Over elements
+   i < n, with the launch shape, tile walk and per-lane element ownership of
+   zero_adam_step's fused kernel, and every buffer indexed from 0:
+     ZERO_MIX_STEP_STREAMS  reads the n_ranks bf16 grads[q][i] and master[i],
+                            m[i], v[i]; writes master[i] + s, m[i] + s and
+                            v[i] + s (s = the fp32 sum of the rank values) and
+                            param[i] = the upper 16 bits of the new master[i];
+     ZERO_MIX_READS         the same reads, nothing written;
+     ZERO_MIX_WRITES        the same writes, nothing read (master, m, v and
+                            param receive values derived from i).
+   Per element the step streams are 2*n_ranks + 12 bytes read and 14 bytes
+   written, as in the fused step.  `grads` is a host array of n_ranks device
+   pointers; 1 <= n_ranks <= ZERO_MAX_RANKS_PER_CALL; n must be a multiple of
+   4 and every buffer 16-byte aligned (ZERO_ERR_INVALID_ARG /
+   ZERO_ERR_ALIGNMENT otherwise, nothing launched). */
+typedef enum {
+    ZERO_MIX_STEP_STREAMS = 0,
+    ZERO_MIX_READS = 1,
+    ZERO_MIX_WRITES = 2
+} zero_mix_kind;
+
+zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t n_ranks,
+                            float *master, float *m, float *v, uint16_t *param, int64_t n,
+                            void *stream);
 
 /* ----------------------------------------------- FSDP linear layer -- */
 

@@ -6,7 +6,8 @@ oracle.
 Every draw comes from its own torch.Generator seeded by
     seed = ((((cfg * 16 + kind) * 1024 + step) * 128 + rank) * 128 + unit)
 with kind 0 = gradient, 1 = master init, 2 = outlier mask, 3 = micro-batch
-gradient (the micro-batch index rides in `unit`).  CPU and GPU generators give
+gradient (the micro-batch index rides in `unit`), 4 = a peer's parameter
+shard for the gather.  CPU and GPU generators give
 different streams for one seed, so a test draws on one device and copies the
 bits to the other.
 
@@ -105,7 +106,7 @@ WORKLOADS = {
 
 # ---------------------------------------------------------------- draws --
 
-KIND_GRAD, KIND_MASTER, KIND_OUTLIER, KIND_MICRO = 0, 1, 2, 3
+KIND_GRAD, KIND_MASTER, KIND_OUTLIER, KIND_MICRO, KIND_PEER = 0, 1, 2, 3, 4
 
 
 def seed(cfg: int, kind: int, step: int, rank: int, unit: int = 0) -> int:
@@ -140,6 +141,14 @@ def grad_bits(w: Workload, step: int, rank: int, n: int, device="cpu",
                        device=device)
         x = torch.where(u < w.outlier_frac, x * w.outlier_scale, x)
     return to_bf16_bits(x)
+
+
+def peer_bits(w: Workload, rank: int, n: int, device="cpu", unit: int = 0) -> torch.Tensor:
+    """A peer rank's parameter shard for the gather: n uniformly random
+    16-bit patterns (int16 tensor; every bf16 pattern, NaNs and Infs
+    included, is equally likely), distinct per rank and unit."""
+    g = _gen(seed(w.cfg, KIND_PEER, 0, rank, unit), device)
+    return torch.randint(-32768, 32768, (n,), generator=g, device=device, dtype=torch.int16)
 
 
 def master_init(w: Workload, n: int, device="cpu", rank: int = 0, unit: int = 0) -> torch.Tensor:

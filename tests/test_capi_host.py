@@ -183,12 +183,12 @@ def test_reduce_validation():
 
 def test_partials_count_is_a_fixed_function_of_the_range():
     L = zs.shard_init("zero2", 8, 0, [25_000_000] * 4 + [24_439_808])
-    # one partial per 2048-element tile
+    # one partial per 1024-element tile
     per = [zs.reduce_partials_count(L, u, u + 1) for u in range(5)]
-    assert per == [-(-3_125_000 // 2048)] * 4 + [-(-3_054_976 // 2048)]
+    assert per == [-(-3_125_000 // 1024)] * 4 + [-(-3_054_976 // 1024)]
     assert zs.reduce_partials_count(L, 0, 5) == sum(per)
     L = zs.shard_init("fsdp", 64, 0, [64 * 4096] * 40)     # 40 units -> two launches
-    assert zs.reduce_partials_count(L, 0, 40) == 2 * 40
+    assert zs.reduce_partials_count(L, 0, 40) == 4 * 40
 
 
 def test_gather_and_accumulate_and_clip_validation():
@@ -432,3 +432,22 @@ def test_fsdp_sweep_table_validation_launches_nothing():
     bad = ([FAKE, None, FAKE, FAKE], [FAKE, FAKE, FAKE, None], FAKE)
     e = _err(sweep, units=(good, bad))
     assert e.status == zs.ERR_INVALID_ARG and "unit 1" in str(e)
+
+
+def test_stream_mix_validation_launches_nothing():
+    g8 = [FAKE] * 8
+    st = (FAKE, FAKE, FAKE, FAKE)
+    assert _err(zs.stream_mix, 3, g8, *st, 64, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.stream_mix, zs.MIX_READS, g8, *st, 66, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.stream_mix, zs.MIX_READS, g8, *st, -4, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.stream_mix, zs.MIX_READS, [], *st, 64, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.stream_mix, zs.MIX_READS, [FAKE] * 65, *st, 64, 0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.stream_mix, zs.MIX_WRITES, g8, FAKE, None, FAKE, FAKE, 64,
+                0).status == zs.ERR_INVALID_ARG
+    assert _err(zs.stream_mix, zs.MIX_WRITES, g8, FAKE + 8, FAKE, FAKE, FAKE, 64,
+                0).status == zs.ERR_ALIGNMENT
+    assert _err(zs.stream_mix, zs.MIX_STEP_STREAMS, [FAKE] * 7 + [FAKE + 4], *st, 64,
+                0).status == zs.ERR_ALIGNMENT
+    assert _err(zs.stream_mix, zs.MIX_STEP_STREAMS, [FAKE] * 7 + [None], *st, 64,
+                0).status == zs.ERR_INVALID_ARG
+    zs.stream_mix(zs.MIX_STEP_STREAMS, g8, *st, 0, 0)   # n = 0: nothing to launch

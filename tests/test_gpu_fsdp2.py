@@ -13,7 +13,8 @@ import torch
 
 from oracle import _c, strategies
 from oracle.layout import valid_rows
-from synthetic import grad_bits, master_init, mistral7b_shapes, small_workload
+from gather_check import assert_gathered
+from synthetic import grad_bits, master_init, mistral7b_shapes, peer_bits, small_workload
 
 pytestmark = pytest.mark.gpu
 zs = None
@@ -104,17 +105,12 @@ def test_fsdp2_mistral7b_full_size_sampled():
     assert np.array_equal(own[tidx].cpu().numpy().view(np.uint16), par_h)
     # gather the 7 peer shards into the full per-parameter buffer
     full = torch.empty(L.flat_len, dtype=torch.int16, device=DEV)
-    peers = [torch.full((S,), q + 1, dtype=torch.int16, device=DEV) for q in range(n - 1)]
+    peers = [peer_bits(w, q, S, device=DEV) for q in range(n - 1)]
     zs.gather_params(L, 0, len(shapes), peers + [own], full)
     torch.cuda.synchronize()
-    # spot-check every parameter's rank slots
-    for u in range(0, len(shapes), 7):
+    # every parameter, every rank slot: sampled positions and both slot edges
+    for u in range(len(shapes)):
         x = L.query(u)
-        s, F = x["shard_len"], x["flat_off"]
-        for q in (0, 3, n - 1):
-            got = full[F + q * s: F + q * s + min(s, 64)].cpu().numpy().view(np.uint16)
-            if q < n - 1:
-                assert np.all(got == q + 1), (u, q)
-            else:
-                want = own[x["shard_off"]: x["shard_off"] + min(s, 64)].cpu().numpy().view(np.uint16)
-                assert np.array_equal(got, want), u
+        s, F, R = x["shard_len"], x["flat_off"], x["shard_off"]
+        sidx = np.unique(rng.integers(0, s, 64)).astype(np.int64)
+        assert_gathered(full, F, s, [p[R:] for p in peers + [own]], sidx, f"FSDP2 parameter {u}")

@@ -24,7 +24,8 @@ import pytest
 import torch
 
 from oracle import _c, strategies
-from synthetic import KIND_MICRO, WORKLOADS, grad_bits, master_init
+from gather_check import assert_gathered
+from synthetic import KIND_MICRO, WORKLOADS, grad_bits, master_init, peer_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -178,7 +179,7 @@ def test_config3_megatron_full_size_sampled():
     index = [zs.INDEX_SHARD] * (n - 1) + [zs.INDEX_FULL]
     zs.adam_step(L, 0, 1, cfg_of(w, 1), master, m, v, replica, zs.INDEX_FULL,
                  grads=zs.Grads(ranks_fp32, zs.FP32, index))
-    peer_bf16 = [torch.full((S,), q + 3, dtype=torch.int16, device=DEV) for q in range(n - 1)]
+    peer_bf16 = [peer_bits(w, q, S, device=DEV) for q in range(n - 1)]
     zs.gather_params(L, 0, 1, peer_bf16 + [None], replica)
     torch.cuda.synchronize()
 
@@ -197,8 +198,7 @@ def test_config3_megatron_full_size_sampled():
     bitcmp(host_f32(m[tidx]), m_h, "config 3 m")
     bitcmp(host_f32(v[tidx]), v_h, "config 3 v")
     bitcmp(host_bf16(replica[off + tidx]), par_h, "config 3 own bf16 slice")
-    for q in range(n - 1):
-        assert np.all(host_bf16(replica[q * S + tidx]) == q + 3), f"gather slot {q}"
+    assert_gathered(replica, 0, S, peer_bf16 + [None], idx, "config 3 gather")
 
 
 # ------------------------------------------------------------ config 4 --
@@ -215,8 +215,7 @@ def test_config4_llama70b_fsdp_per_unit_sampled():
     m = torch.zeros(L.shard_len, device=DEV)
     v = torch.zeros(L.shard_len, device=DEV)
     full_unit = torch.empty(smax * n, dtype=torch.int16, device=DEV)
-    peers = [torch.full((smax,), (q * 7 + 1) & 0x7FFF, dtype=torch.int16, device=DEV)
-             for q in range(n - 1)]
+    peers = [peer_bits(w, q, smax, device=DEV) for q in range(n - 1)]
     rng = np.random.default_rng(4)
     cfg = cfg_of(w, 1)
     for u in range(len(units)):
@@ -240,6 +239,4 @@ def test_config4_llama70b_fsdp_per_unit_sampled():
         bitcmp(host_f32(m[so + tidx]), m_h, f"config 4 unit {u} m")
         bitcmp(host_f32(v[so + tidx]), v_h, f"config 4 unit {u} v")
         bitcmp(host_bf16(full_unit[r * su + tidx]), par_h, f"config 4 unit {u} own slice")
-        for k in (0, 1, n // 2, n - 2):
-            assert np.all(host_bf16(full_unit[k * su + tidx]) == ((k * 7 + 1) & 0x7FFF)), \
-                f"config 4 unit {u} gather slot {k}"
+        assert_gathered(full_unit, 0, su, peers + [None], idx, f"config 4 unit {u} gather")

@@ -21,7 +21,8 @@ import pytest
 import torch
 
 from oracle import _c, strategies
-from synthetic import WORKLOADS, grad_bits, master_init, small_workload
+from gather_check import assert_gathered
+from synthetic import WORKLOADS, grad_bits, master_init, peer_bits, small_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -399,16 +400,14 @@ def test_config2_full_size_sampled():
     assert_f32_close(host_f32(m[tidx]), m_h, "config 2 m")
     assert_f32_close(host_f32(v[tidx]), v_h, "config 2 v")
     assert_bf16_equal(host_bf16(own[tidx]), par_h, "config 2 bf16 shard")
-    # all-gather data movement into the full 7.24e9-element buffer
-    peers = [to_peer for to_peer in (torch.full((S,), q + 1, dtype=torch.int16, device=DEV)
-                                     for q in range(n - 1))] + [own]
+    # all-gather data movement into the full 7.24e9-element buffer: random
+    # peer shards, every slot at the sampled positions and its edges
+    peers = [peer_bits(w, q, S, device=DEV) for q in range(n - 1)] + [own]
     full = torch.empty(L.flat_len, dtype=torch.int16, device=DEV)
     zs.gather_params(L, 0, 1, peers, full)
     torch.cuda.synchronize()
-    for q in range(n):
-        got = host_bf16(full[q * S + tidx])
-        want = par_h if q == r else np.full(idx.size, q + 1, np.uint16)
-        assert np.array_equal(got, want), f"gather slot {q}"
+    assert np.array_equal(host_bf16(full[r * S + tidx]), par_h), "gather: own slot"
+    assert_gathered(full, 0, S, peers, idx, "config 2 gather")
 
 
 def test_config2_full_shard_every_element():

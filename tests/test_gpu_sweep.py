@@ -10,7 +10,8 @@ import pytest
 import torch
 
 from oracle import _c, strategies
-from synthetic import WORKLOADS, grad_bits, master_init, small_workload
+from gather_check import assert_gathered
+from synthetic import WORKLOADS, grad_bits, master_init, peer_bits, small_workload
 
 pytestmark = pytest.mark.gpu
 zs = None
@@ -97,7 +98,7 @@ def test_sweep_ring_of_two_buffers_full_llama70b():
     q = [L.query(u) for u in range(U)]
     smax = max(x["shard_len"] for x in q)
     grads = [grad_bits(w, 0, k, smax, device=DEV) for k in range(n)]
-    peers = [torch.full((smax,), k + 5, dtype=torch.int16, device=DEV) for k in range(n)]
+    peers = [peer_bits(w, k, smax, device=DEV) for k in range(n)]
     ring = [torch.zeros(n * smax, dtype=torch.int16, device=DEV) for _ in range(2)]
     master = torch.empty(L.shard_len, device=DEV)
     for u, x in enumerate(q):
@@ -136,5 +137,5 @@ def test_sweep_ring_of_two_buffers_full_llama70b():
             buf = ring[u % 2]
             own = h16(buf[r * s + torch.from_numpy(idx).to(DEV)])
             assert np.array_equal(own, par_h), u
-            for k in (0, 17, n - 2):
-                assert np.all(h16(buf[k * s + torch.from_numpy(idx).to(DEV)]) == k + 5), (u, k)
+            assert_gathered(buf, 0, s, [None if k == r else peers[k] for k in range(n)], idx,
+                            f"sweep unit {u} gather")
