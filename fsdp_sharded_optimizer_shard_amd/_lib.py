@@ -34,6 +34,7 @@ INDEX_FULL, INDEX_SHARD = 0, 1
 K_INNER, K_OUTER = 0, 1
 MIX_STEP_STREAMS, MIX_READS, MIX_WRITES = 0, 1, 2
 MAX_RANKS_PER_CALL = 64
+NOALLOC_MAX_PARTIALS = 524288
 
 STRATEGY = {"ddp": DDP, "zero1": STAGE1, "zero1_allreduce": STAGE1, "zero2": STAGE2,
             "zero3": STAGE3, "fsdp": FSDP, "fsdp2": FSDP, "megatron_do": MEGATRON_DO}
@@ -89,6 +90,10 @@ _lib.zero_clip_coef.restype = _I32
 _lib.zero_adam_step.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _P, _I32, _P,
                                 ctypes.POINTER(_Grads), _P, _P, _P, _P, _I32, _P]
 _lib.zero_adam_step.restype = _I32
+_lib.zero_adam_step_clip_noalloc.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg),
+                                             ctypes.c_float, ctypes.POINTER(_Grads), _P, _P, _P,
+                                             _P, _P, _I32, _P, _P]
+_lib.zero_adam_step_clip_noalloc.restype = _I32
 _lib.zero_adam_table_fill.argtypes = [ctypes.POINTER(AdamCfg), _I64, _P]
 _lib.zero_adam_table_fill.restype = _I32
 _lib.zero_adam_step_table.argtypes = [_P, _I32, _I32, _P, _I64, _P, _P, _I32, _P,
@@ -137,6 +142,7 @@ _lib.zero_last_error.restype = ctypes.c_char_p
 EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy",
            "zero_layout_info", "zero_layout_query", "zero_reduce_shard",
            "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
+           "zero_adam_step_clip_noalloc",
            "zero_adam_table_fill", "zero_adam_step_table", "zero_step_advance", "zero_gather_params",
            "zero_grad_accumulate", "zero_stream_mix", "zero_fsdp_sweep", "zero_fsdp_sweep_table", "zero_gemm_bf16",
            "zero_gemm_bf16_nt",
@@ -296,6 +302,19 @@ def adam_step(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, mast
                                grads.ref() if grads else None,
                                _addr(master), _addr(m), _addr(v), _addr(param_out), param_index,
                                _stream(stream)), "zero_adam_step")
+
+
+def adam_step_clip_noalloc(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg,
+                           max_norm: float, grads: Grads, grad_out, master, m, v, param_out,
+                           param_index: int = INDEX_FULL, norm_out=None, stream=None) -> None:
+    """The clipped two-pass step with the library's static scratch (no
+    device allocation): reduce with partials, clip coefficient, Adam."""
+    _check(_lib.zero_adam_step_clip_noalloc(layout.handle, unit_begin, unit_end,
+                                            ctypes.byref(cfg), max_norm,
+                                            grads.ref() if grads else None, _addr(grad_out),
+                                            _addr(master), _addr(m), _addr(v), _addr(param_out),
+                                            param_index, _addr(norm_out), _stream(stream)),
+           "zero_adam_step_clip_noalloc")
 
 
 def adam_table(cfgs):

@@ -973,6 +973,48 @@ zero_status adam_launch(const zero_layout *L, int32_t ub, int32_t ue, const Adam
 }  // namespace
 }  // namespace zs
 
+// Device memory for the one entry point that allocates nothing
+// (zero_adam_step_clip_noalloc): the fp64 sum-of-squares partials of the
+// reduce, then the clip coefficient (a float in the first 4 bytes of slot
+// kNoAllocPartials).  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never passes `scratch` itself to a kernel:
+// the host-side name is not a device address.  It uses the address
+// hipGetSymbolAddress returns for the current device (noalloc_scratch).
+constexpr int64_t kNoAllocPartials = ZERO_NOALLOC_MAX_PARTIALS;
+static __device__ __align__(256) double scratch[kNoAllocPartials + 32];
+
+namespace zs {
+namespace {
+
+// The device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept; several
+// host threads may race to look it up, and all store the same address.
+zero_status noalloc_scratch(double **out)
+{
+    static std::atomic<double *> cached[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(ZERO_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64)
+        return fail(ZERO_ERR_UNSUPPORTED, "device %d: at most 64 devices are supported", dev);
+    double *p = cached[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *addr = nullptr;
+        e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !addr)
+            return fail(ZERO_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        p = static_cast<double *>(addr);
+        cached[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return ZERO_OK;
+}
+
+}  // namespace
+}  // namespace zs
+
 using namespace zs;
 
 extern "C" {
@@ -1064,6 +1106,57 @@ zero_status zero_adam_step(const zero_layout *L, int32_t ub, int32_t ue,
         return st;
     return adam_launch(L, ub, ue, make_scalars(cfg), nullptr, 0, nullptr, grad_fp32, grad_index,
                        clip_coef, grads, master, m, v, param_out, param_index, stream);
+}
+
+zero_status zero_adam_step_clip_noalloc(const zero_layout *L, int32_t ub, int32_t ue,
+                                        const zero_adam_cfg *cfg, float max_norm,
+                                        const zero_grads *grads, float *grad_out, float *master,
+                                        float *m, float *v, uint16_t *param_out,
+                                        int32_t param_index, double *norm_out, void *stream)
+{
+    // every check on the host first: on error nothing is launched and no HIP
+    // call is made
+    zero_status st = check_range(L, ub, ue);
+    if (st != ZERO_OK)
+        return st;
+    if ((st = check_cfg(cfg)) != ZERO_OK)
+        return st;
+    if (!(max_norm > 0.0f) || !std::isfinite(max_norm))
+        return fail(ZERO_ERR_INVALID_ARG, "max_norm must be finite and > 0");
+    if (!grads || !grad_out)
+        return fail(ZERO_ERR_INVALID_ARG, "grads and grad_out are required");
+    if ((st = check_grads(L, grads)) != ZERO_OK)
+        return st;
+    if (!master || !m || !v || !param_out)
+        return fail(ZERO_ERR_INVALID_ARG, "master, m, v and param_out are required");
+    if (param_index != ZERO_INDEX_FULL && param_index != ZERO_INDEX_SHARD)
+        return fail(ZERO_ERR_INVALID_ARG, "unknown param_index %d", param_index);
+    if (reinterpret_cast<uintptr_t>(grad_out) % 4 || reinterpret_cast<uintptr_t>(master) % 4 ||
+        reinterpret_cast<uintptr_t>(m) % 4 || reinterpret_cast<uintptr_t>(v) % 4 ||
+        reinterpret_cast<uintptr_t>(param_out) % 2 || reinterpret_cast<uintptr_t>(norm_out) % 8)
+        return fail(ZERO_ERR_ALIGNMENT, "misaligned gradient, state, parameter or norm buffer");
+    const int64_t n = zero_reduce_partials_count(L, ub, ue);
+    if (n > kNoAllocPartials)
+        return fail(ZERO_ERR_UNSUPPORTED,
+                    "the range needs %lld sum-of-squares partials; the library's static buffer "
+                    "holds %lld (ranges up to %lld elements per rank)",
+                    (long long)n, (long long)kNoAllocPartials,
+                    (long long)kNoAllocPartials * kStepTile);
+    if (n == 0)
+        return ZERO_OK;  // every unit of the range is empty
+    double *sp = nullptr;
+    if ((st = noalloc_scratch(&sp)) != ZERO_OK)
+        return st;
+    float *coef = reinterpret_cast<float *>(sp + kNoAllocPartials);
+    // the three calls of the two-pass path, on the static buffer; their own
+    // checks pass, as every argument was checked above
+    if ((st = zero_reduce_shard(L, ub, ue, grads, grad_out, ZERO_INDEX_SHARD, sp, n, stream)) !=
+        ZERO_OK)
+        return st;
+    if ((st = zero_clip_coef(sp, n, max_norm, coef, norm_out, stream)) != ZERO_OK)
+        return st;
+    return zero_adam_step(L, ub, ue, cfg, grad_out, ZERO_INDEX_SHARD, coef, nullptr, master, m, v,
+                          param_out, param_index, stream);
 }
 
 zero_status zero_adam_table_fill(const zero_adam_cfg *cfgs, int64_t n,

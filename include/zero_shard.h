@@ -219,6 +219,38 @@ int64_t zero_reduce_partials_count(const zero_layout *layout,
 zero_status zero_clip_coef(const double *partials, int64_t n, float max_norm,
                            float *coef_out, double *norm_out, void *stream);
 
+/* ------------------------------------------------ no allocation -- */
+
+/* Capacity of the library's static device buffer of sum-of-squares partials
+   (4 MiB of fp64 per GPU, held until the process ends). */
+#define ZERO_NOALLOC_MAX_PARTIALS 524288
+
+/* For callers that cannot allocate device memory: code under HIP graph
+   capture, tight serving loops, harnesses that forbid hipMalloc.  The
+   two-pass clipped step of one range -- zero_reduce_shard into `grad_out`
+   (fp32, shard-indexed) with sum-of-squares partials, zero_clip_coef over
+   those partials (max_norm > 0), then zero_adam_step from `grad_out` scaled
+   by the coefficient -- with the partials and the coefficient kept in a
+   static device array of the library instead of caller buffers.  Results
+   are those of that three-call sequence, bit for bit.  The norm is the
+   norm of this call's range: the whole buffer under ZERO_DDP, this rank's
+   shard otherwise (a global norm over several ranks needs every rank's
+   partials: use the three calls).  `norm_out` (device double, may be NULL)
+   receives the norm.  The range may need at most ZERO_NOALLOC_MAX_PARTIALS
+   partials (zero_reduce_partials_count; 536,870,912 elements per rank),
+   else ZERO_ERR_UNSUPPORTED.  The call allocates nothing and calls no
+   allocating routine; every argument is checked on the host before the
+   first HIP call.  Calls on one GPU share its array, so calls that overlap
+   in time on one GPU (other streams, other host threads) race; calls in
+   one stream order are safe, each overwriting what it uses before reading
+   it. */
+zero_status zero_adam_step_clip_noalloc(const zero_layout *layout, int32_t unit_begin,
+                                        int32_t unit_end, const zero_adam_cfg *cfg,
+                                        float max_norm, const zero_grads *grads,
+                                        float *grad_out, float *master, float *m, float *v,
+                                        uint16_t *param_out, int32_t param_index,
+                                        double *norm_out, void *stream);
+
 /* --------------------------------------------------------- Adam step -- */
 
 /* Adam / AdamW on this rank's slices of units [unit_begin, unit_end), then

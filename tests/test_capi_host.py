@@ -451,3 +451,32 @@ def test_stream_mix_validation_launches_nothing():
     assert _err(zs.stream_mix, zs.MIX_STEP_STREAMS, [FAKE] * 7 + [None], *st, 64,
                 0).status == zs.ERR_INVALID_ARG
     zs.stream_mix(zs.MIX_STEP_STREAMS, g8, *st, 0, 0)   # n = 0: nothing to launch
+
+
+def test_noalloc_clip_step_validation_makes_no_hip_call():
+    # every error is found on the host: these calls hold fake device
+    # addresses, so any launch or HIP call would surface as a HIP error
+    L = zs.shard_init("ddp", 4, 0, [1000, 24])
+    g = zs.Grads([FAKE] * 4, zs.BF16, zs.INDEX_FULL)
+    cfg = zs.adam_cfg(step=1)
+    args = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    def f(*a, **kw):
+        return zs.adam_step_clip_noalloc(*a, stream=0, **kw)
+    assert _err(f, L, 0, 2, cfg, 0.0, g, *args).status == zs.ERR_INVALID_ARG
+    assert _err(f, L, 0, 2, cfg, float("inf"), g, *args).status == zs.ERR_INVALID_ARG
+    assert _err(f, L, 0, 3, cfg, 1.0, g, *args).status == zs.ERR_INVALID_ARG
+    assert _err(f, L, 0, 2, zs.adam_cfg(step=0), 1.0, g, *args).status == zs.ERR_INVALID_ARG
+    assert _err(f, L, 0, 2, cfg, 1.0, zs.Grads([FAKE] * 3, zs.BF16, zs.INDEX_FULL),
+                *args).status == zs.ERR_INVALID_ARG
+    assert _err(f, L, 0, 2, cfg, 1.0, g, None, FAKE, FAKE, FAKE, FAKE).status == zs.ERR_INVALID_ARG
+    assert _err(f, L, 0, 2, cfg, 1.0, g, FAKE + 2, FAKE, FAKE, FAKE,
+                FAKE).status == zs.ERR_ALIGNMENT
+    assert _err(f, L, 0, 2, cfg, 1.0, g, *args, param_index=7).status == zs.ERR_INVALID_ARG
+    assert _err(f, L, 0, 2, cfg, 1.0, g, *args, norm_out=FAKE + 4).status == zs.ERR_ALIGNMENT
+    # one partial per 1024-element tile: a DDP buffer one tile past the limit
+    big = zs.shard_init("ddp", 4, 0, [zs.NOALLOC_MAX_PARTIALS * 1024 + 1])
+    assert zs.reduce_partials_count(big, 0, 1) == zs.NOALLOC_MAX_PARTIALS + 1
+    e = _err(f, big, 0, 1, cfg, 1.0, g, *args)
+    assert e.status == zs.ERR_UNSUPPORTED and "static buffer" in str(e)
+    # an empty range needs no partials and launches nothing
+    f(L, 1, 1, cfg, 1.0, g, *args)
