@@ -2,8 +2,12 @@
 marshalling only: every step of the path runs in the HIP library.
 
 Buffers may be given as torch tensors (their data_ptr() is passed) or as raw
-integer device addresses.  `stream` defaults to torch's current stream on the
-current device.  Errors raise ZeroShardError with the library's message.
+integer device addresses.  A tensor is checked before the call: its dtype,
+that it is contiguous, and that it holds every element the call touches (from
+the layout's unit range), so that an undersized buffer raises ValueError here
+instead of being read or written past its end by a kernel.  Raw addresses are
+passed as they are.  `stream` defaults to torch's current stream on the
+current device.  Errors of the library raise ZeroShardError with its message.
 There is no fallback: if the library is missing this module fails to import.
 """
 import ctypes
@@ -176,6 +180,43 @@ def _addr(x) -> Optional[int]:
     return x.data_ptr()
 
 
+_DTYPES = {
+    "fp32": (torch.float32,),
+    "fp64": (torch.float64,),
+    "bf16": (torch.int16, torch.uint16, torch.bfloat16),   # bf16 bit patterns
+    "int64": (torch.int64,),
+}
+
+
+def _need(x, what: str, count: Optional[int], kind: str) -> None:
+    """A tensor argument must be of `kind`, contiguous, and hold at least
+    `count` elements (bytes for kind "bytes").  None, raw addresses and an
+    unknown count (an invalid range, reported by the library) pass."""
+    if x is None or x.__class__ is int or not hasattr(x, "numel"):
+        return
+    if x.is_cuda is False:
+        raise ValueError(f"{what}: buffers passed to libzeroshard must be GPU tensors (got one "
+                         f"on {x.device})")
+    if count is None:
+        return
+    if kind == "bytes":
+        have = x.numel() * x.element_size()
+    else:
+        if x.dtype not in _DTYPES[kind]:
+            raise ValueError(f"{what}: dtype {x.dtype}, expected one of "
+                             f"{', '.join(str(d) for d in _DTYPES[kind])}")
+        have = x.numel()
+    if have < count:
+        raise ValueError(f"{what} holds {have} {'bytes' if kind == 'bytes' else 'elements'}, "
+                         f"the call touches {count}")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _kind(dtype: int) -> str:
+    return "fp32" if dtype == FP32 else "bf16"
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -191,6 +232,33 @@ class Layout:
     def __init__(self, handle: int, units: Sequence[int]):
         self._h = handle
         self.units = list(units)
+        self._uq = None
+        self._lens = {}
+
+    def _unit_table(self):
+        """Every unit's query(), read once (a layout never changes)."""
+        if self._uq is None:
+            self._uq = [self.query(u) for u in range(self.info()["n_units"])]
+        return self._uq
+
+    def range_lens(self, unit_begin: int, unit_end: int):
+        """(shard-indexed, full-indexed) element counts of a unit range, or
+        (None, None) for a range the library will refuse."""
+        key = (unit_begin, unit_end)
+        r = self._lens.get(key)
+        if r is None:
+            r = self._lens[key] = self._range_lens(unit_begin, unit_end)
+        return r
+
+    def _range_lens(self, unit_begin, unit_end):
+        q = self._unit_table()
+        if not (0 <= unit_begin <= unit_end <= len(q)):
+            return None, None
+        if unit_begin == unit_end:
+            return 0, 0
+        a, b = q[unit_begin], q[unit_end - 1]
+        return (b["shard_off"] + b["shard_len"] - a["shard_off"],
+                b["flat_off"] + b["padded_len"] - a["flat_off"])
 
     @property
     def handle(self) -> int:
@@ -271,9 +339,24 @@ class Grads:
         else:
             self._index = (ctypes.c_uint8 * len(index))(*[int(i) for i in index])
         self.s = _Grads(self._ptrs, self._index, len(ptrs), dtype, idx_all, 0)
+        self._checked = None
 
     def ref(self):
         return ctypes.byref(self.s)
+
+    def check(self, lens) -> None:
+        """Each rank buffer holds its index mode's range (lens from
+        Layout.range_lens).  The buffers of a Grads never change, so a
+        range checked once is not checked again."""
+        if lens == self._checked:
+            return
+        shard, full = lens
+        for q, b in enumerate(self._keep):
+            mode = self.s.index_all if self._index is None else self._index[q]
+            _need(b, f"gradient buffer of rank {q}", full if mode == INDEX_FULL else shard,
+                  _kind(self.s.dtype))
+        if None not in lens:
+            self._checked = lens
 
 
 def reduce_partials_count(layout: Layout, unit_begin: int, unit_end: int) -> int:
@@ -283,6 +366,11 @@ def reduce_partials_count(layout: Layout, unit_begin: int, unit_end: int) -> int
 def reduce_shard(layout: Layout, unit_begin: int, unit_end: int, grads: Grads, out,
                  sumsq_partials=None, n_partials: int = 0, stream=None,
                  out_index: int = INDEX_SHARD) -> None:
+    shard, full = layout.range_lens(unit_begin, unit_end)
+    if grads is not None:
+        grads.check((shard, full))
+    _need(out, "out", full if out_index == INDEX_FULL else shard, "fp32")
+    _need(sumsq_partials, "sumsq_partials", n_partials, "fp64")
     _check(_lib.zero_reduce_shard(layout.handle, unit_begin, unit_end, grads.ref() if grads else None,
                                   _addr(out), out_index, _addr(sumsq_partials), n_partials,
                                   _stream(stream)),
@@ -290,13 +378,34 @@ def reduce_shard(layout: Layout, unit_begin: int, unit_end: int, grads: Grads, o
 
 
 def clip_coef(partials, n: int, max_norm: float, coef_out, norm_out=None, stream=None) -> None:
+    _need(partials, "partials", n, "fp64")
+    _need(coef_out, "coef_out", 1, "fp32")
+    _need(norm_out, "norm_out", 1, "fp64")
     _check(_lib.zero_clip_coef(_addr(partials), n, max_norm, _addr(coef_out), _addr(norm_out),
                                _stream(stream)), "zero_clip_coef")
+
+
+def _check_step(layout, unit_begin, unit_end, master, m, v, param_out, param_index,
+                grad_fp32=None, grad_index=INDEX_SHARD, clip_coef=None, grads=None):
+    lens = layout.range_lens(unit_begin, unit_end)
+    shard, full = lens
+    _need(master, "master", shard, "fp32")
+    _need(m, "m", shard, "fp32")
+    _need(v, "v", shard, "fp32")
+    _need(param_out, "param_out", full if param_index == INDEX_FULL else shard, "bf16")
+    if grad_fp32 is not None:
+        _need(grad_fp32, "grad_fp32", full if grad_index == INDEX_FULL else shard, "fp32")
+    if clip_coef is not None:
+        _need(clip_coef, "clip_coef", 1, "fp32")
+    if grads is not None:
+        grads.check(lens)
 
 
 def adam_step(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, master, m, v,
               param_out, param_index: int = INDEX_FULL, grad_fp32=None, clip_coef=None,
               grads: Optional[Grads] = None, stream=None, grad_index: int = INDEX_SHARD) -> None:
+    _check_step(layout, unit_begin, unit_end, master, m, v, param_out, param_index, grad_fp32,
+                grad_index, clip_coef, grads)
     _check(_lib.zero_adam_step(layout.handle, unit_begin, unit_end, ctypes.byref(cfg),
                                _addr(grad_fp32), grad_index, _addr(clip_coef),
                                grads.ref() if grads else None,
@@ -309,6 +418,9 @@ def adam_step_clip_noalloc(layout: Layout, unit_begin: int, unit_end: int, cfg: 
                            param_index: int = INDEX_FULL, norm_out=None, stream=None) -> None:
     """The clipped two-pass step with the library's static scratch (no
     device allocation): reduce with partials, clip coefficient, Adam."""
+    _check_step(layout, unit_begin, unit_end, master, m, v, param_out, param_index,
+                grad_fp32=grad_out, grads=grads)
+    _need(norm_out, "norm_out", 1, "fp64")
     _check(_lib.zero_adam_step_clip_noalloc(layout.handle, unit_begin, unit_end,
                                             ctypes.byref(cfg), max_norm,
                                             grads.ref() if grads else None, _addr(grad_out),
@@ -339,6 +451,10 @@ def adam_step_table(layout: Layout, unit_begin: int, unit_end: int, table, n_ent
                     step_counter, master, m, v, param_out, param_index: int = INDEX_FULL,
                     grad_fp32=None, clip_coef=None, grads: Optional[Grads] = None, stream=None,
                     grad_index: int = INDEX_SHARD) -> None:
+    _check_step(layout, unit_begin, unit_end, master, m, v, param_out, param_index, grad_fp32,
+                grad_index, clip_coef, grads)
+    _need(table, "table", n_entries * ctypes.sizeof(AdamTableEntry), "bytes")
+    _need(step_counter, "step_counter", 1, "int64")
     _check(_lib.zero_adam_step_table(layout.handle, unit_begin, unit_end, _addr(table), n_entries,
                                      _addr(step_counter), _addr(grad_fp32), grad_index,
                                      _addr(clip_coef), grads.ref() if grads else None,
@@ -347,11 +463,16 @@ def adam_step_table(layout: Layout, unit_begin: int, unit_end: int, table, n_ent
 
 
 def step_advance(step_counter, stream=None) -> None:
+    _need(step_counter, "step_counter", 1, "int64")
     _check(_lib.zero_step_advance(_addr(step_counter), _stream(stream)), "zero_step_advance")
 
 
 def gather_params(layout: Layout, unit_begin: int, unit_end: int, shards, param_full,
                   stream=None) -> None:
+    shard, full = layout.range_lens(unit_begin, unit_end)
+    for q, x in enumerate(shards):
+        _need(x, f"shard of rank {q}", shard, "bf16")
+    _need(param_full, "param_full", full, "bf16")
     ptrs = [_addr(s) for s in shards]
     arr = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
     _check(_lib.zero_gather_params(layout.handle, unit_begin, unit_end, arr, len(ptrs),
@@ -371,13 +492,22 @@ def _need_len(what: str, seq, n: int) -> None:
         raise ValueError(f"{what}: expected {n} entries, got {len(seq)}")
 
 
-def _unit_ios(layout: Layout, unit_begin: int, unit_end: int, units):
+def _unit_ios(layout: Layout, unit_begin: int, unit_end: int, units, grad_dtype=BF16):
     if 0 <= unit_begin <= unit_end:
         _need_len("units", units, unit_end - unit_begin)
         n, parts = layout.info()["world_n"], _parts(layout)
-        for grads, peers, _ in units:
+        table = layout._unit_table()
+        for i, (grads, peers, full) in enumerate(units):
             _need_len("rank_grads", grads, n)
             _need_len("peer_shards", peers, parts)
+            if unit_begin + i < len(table):
+                q = table[unit_begin + i]
+                for k, x in enumerate(grads):
+                    _need(x, f"unit {unit_begin + i} gradient of rank {k}", q["shard_len"],
+                          _kind(grad_dtype))
+                for k, x in enumerate(peers):
+                    _need(x, f"unit {unit_begin + i} shard of rank {k}", q["shard_len"], "bf16")
+                _need(full, f"unit {unit_begin + i} buffer", q["padded_len"], "bf16")
     keep = []
     arr = (_UnitIO * max(1, len(units)))()
     for i, (grads, peers, full) in enumerate(units):
@@ -395,7 +525,10 @@ def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, gra
     rank_grads are world_n buffers and peer_shards one per slice (world_n,
     or 1 under DDP; None allowed).  gather_stream defaults to step_stream
     (sequential)."""
-    arr, keep = _unit_ios(layout, unit_begin, unit_end, units)
+    arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype)
+    shard, _ = layout.range_lens(unit_begin, unit_end)
+    for name, x in (("master", master), ("m", m), ("v", v)):
+        _need(x, name, shard, "fp32")
     ss = _stream(step_stream)
     gs = ss if gather_stream is None else _stream(gather_stream)
     _check(_lib.zero_fsdp_sweep(layout.handle, unit_begin, unit_end, ctypes.byref(cfg), grad_dtype,
@@ -408,7 +541,12 @@ def fsdp_sweep_table(layout: Layout, unit_begin: int, unit_end: int, table, n_en
                      step_stream=None, gather_stream=None) -> None:
     """fsdp_sweep with the step scalars of table[*step_counter - 1] (device
     table and counter); advances the counter once, after the last unit."""
-    arr, keep = _unit_ios(layout, unit_begin, unit_end, units)
+    arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype)
+    shard, _ = layout.range_lens(unit_begin, unit_end)
+    for name, x in (("master", master), ("m", m), ("v", v)):
+        _need(x, name, shard, "fp32")
+    _need(table, "table", n_entries * ctypes.sizeof(AdamTableEntry), "bytes")
+    _need(step_counter, "step_counter", 1, "int64")
     ss = _stream(step_stream)
     gs = ss if gather_stream is None else _stream(gather_stream)
     _check(_lib.zero_fsdp_sweep_table(layout.handle, unit_begin, unit_end, _addr(table),
@@ -417,19 +555,37 @@ def fsdp_sweep_table(layout: Layout, unit_begin: int, unit_end: int, table, n_en
            "zero_fsdp_sweep_table")
 
 
+def _operand_extent(rows: int, K: int, ld: int, order: int) -> int:
+    """Elements from an operand's start to its last one read."""
+    if rows <= 0 or K <= 0:
+        return 0
+    return (rows - 1) * ld + K if order == K_INNER else (K - 1) * ld + rows
+
+
 def gemm_bf16(M: int, N: int, K: int, A, lda: int, a_order: int, B, ldb: int, b_order: int, C,
               ldc: int, c_dtype: int = FP32, stream=None) -> None:
+    if M > 0 and N > 0 and K >= 0:
+        _need(A, "A", _operand_extent(M, K, lda, a_order), "bf16")
+        _need(B, "B", _operand_extent(N, K, ldb, b_order), "bf16")
+        _need(C, "C", (M - 1) * ldc + N, _kind(c_dtype))
     _check(_lib.zero_gemm_bf16(M, N, K, _addr(A), lda, a_order, _addr(B), ldb, b_order, _addr(C),
                                ldc, c_dtype, _stream(stream)), "zero_gemm_bf16")
 
 
 def gemm_bf16_nt(M: int, N: int, K: int, A, lda: int, B, ldb: int, C, ldc: int,
                  c_dtype: int = FP32, stream=None) -> None:
+    if M > 0 and N > 0 and K >= 0:
+        _need(A, "A", _operand_extent(M, K, lda, K_INNER), "bf16")
+        _need(B, "B", _operand_extent(N, K, ldb, K_INNER), "bf16")
+        _need(C, "C", (M - 1) * ldc + N, _kind(c_dtype))
     _check(_lib.zero_gemm_bf16_nt(M, N, K, _addr(A), lda, _addr(B), ldb, _addr(C), ldc, c_dtype,
                                   _stream(stream)), "zero_gemm_bf16_nt")
 
 
 def transpose_bf16(rows: int, cols: int, src, lds: int, dst, ldd: int, stream=None) -> None:
+    if rows > 0 and cols > 0:
+        _need(src, "src", (rows - 1) * lds + cols, "bf16")
+        _need(dst, "dst", (cols - 1) * ldd + rows, "bf16")
     _check(_lib.zero_transpose_bf16(rows, cols, _addr(src), lds, _addr(dst), ldd, _stream(stream)),
            "zero_transpose_bf16")
 
@@ -438,9 +594,34 @@ def _ptrs(bufs):
     return (ctypes.c_void_p * max(1, len(bufs)))(*[_addr(b) for b in bufs])
 
 
+def _layer_dims(layout: Layout, unit: int):
+    """(in, out, shard, padded) of a linear layer's unit, or None if the unit
+    does not exist (the library reports that)."""
+    table = layout._unit_table()
+    if not 0 <= unit < len(table):
+        return None
+    q = table[unit]
+    cols = layout.rows(unit)["cols"]
+    return q["numel"] // cols, cols, q["shard_len"], q["padded_len"]
+
+
+def _check_layer(layout, unit, w_shards, w_full, batch):
+    d = _layer_dims(layout, unit)
+    if d is None or batch < 0:
+        return None
+    for q, x in enumerate(w_shards):
+        _need(x, f"W shard of rank {q}", d[2], "bf16")
+    _need(w_full, "w_full", d[3], "bf16")
+    return d
+
+
 def fsdp_linear_forward(layout: Layout, unit: int, w_shards, batch: int, x, w_full, y,
                         y_dtype: int = BF16, stream=None) -> None:
     _need_len("w_shards", w_shards, _parts(layout))
+    d = _check_layer(layout, unit, w_shards, w_full, batch)
+    if d is not None:
+        _need(x, "x", batch * d[0], "bf16")
+        _need(y, "y", batch * d[1], _kind(y_dtype))
     _check(_lib.zero_fsdp_linear_forward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
                                          _addr(w_full), _addr(y), y_dtype, _stream(stream)),
            "zero_fsdp_linear_forward")
@@ -449,6 +630,12 @@ def fsdp_linear_forward(layout: Layout, unit: int, w_shards, batch: int, x, w_fu
 def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy, w_full, dx,
                          dw_full, dx_dtype: int = BF16, stream=None) -> None:
     _need_len("w_shards", w_shards, _parts(layout))
+    d = _check_layer(layout, unit, w_shards, w_full, batch)
+    if d is not None:
+        _need(x, "x", batch * d[0], "bf16")
+        _need(dy, "dy", batch * d[1], "bf16")
+        _need(dx, "dx", batch * d[0], _kind(dx_dtype))
+        _need(dw_full, "dw_full", d[3], "fp32")
     _check(_lib.zero_fsdp_linear_backward(layout.handle, unit, _ptrs(w_shards), batch, _addr(x),
                                           _addr(dy), _addr(w_full), _addr(dx), dx_dtype,
                                           _addr(dw_full), _stream(stream)),
@@ -459,11 +646,18 @@ def stream_mix(kind: int, grads, master, m, v, param, n: int, stream=None) -> No
     """zero_stream_mix: the fused step's memory traffic without its
     arithmetic (kind MIX_STEP_STREAMS), its reads alone (MIX_READS) or its
     writes alone (MIX_WRITES), over n elements."""
+    for q, x in enumerate(grads):
+        _need(x, f"gradient buffer of rank {q}", n, "bf16")
+    for name, x in (("master", master), ("m", m), ("v", v)):
+        _need(x, name, n, "fp32")
+    _need(param, "param", n, "bf16")
     _check(_lib.zero_stream_mix(kind, _ptrs(grads), len(grads), _addr(master), _addr(m), _addr(v),
                                 _addr(param), n, _stream(stream)), "zero_stream_mix")
 
 
 def grad_accumulate(main_grad, micro_bf16, n: int, stream=None) -> None:
+    _need(main_grad, "main_grad", n, "fp32")
+    _need(micro_bf16, "micro_bf16", n, "bf16")
     _check(_lib.zero_grad_accumulate(_addr(main_grad), _addr(micro_bf16), n, _stream(stream)),
            "zero_grad_accumulate")
 

@@ -754,13 +754,15 @@ zero_status zero_rows_fill(float *p, int64_t ld, int64_t r0, int64_t r1, int64_t
 
 }  // namespace zs
 
-extern "C" {
+namespace zs {
 
-zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
-                           int32_t a_order, const uint16_t *B, int64_t ldb, int32_t b_order,
-                           void *C, int64_t ldc, int32_t c_dtype, void *stream)
+// Every argument check of zero_gemm_bf16, with nothing launched; composite
+// calls (the FSDP linear layer) run it for each of their GEMMs before their
+// first launch.
+zero_status gemm_check(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                       int32_t a_order, const uint16_t *B, int64_t ldb, int32_t b_order,
+                       const void *C, int64_t ldc, int32_t c_dtype)
 {
-    using zs::fail;
     if (M < 0 || N < 0 || K < 0)
         return fail(ZERO_ERR_INVALID_ARG, "negative GEMM size");
     if ((a_order != ZERO_K_INNER && a_order != ZERO_K_OUTER) ||
@@ -799,6 +801,23 @@ zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, i
         return fail(ZERO_ERR_ALIGNMENT, "A and B must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(C) % (c_dtype == ZERO_BF16 ? 2 : 4))
         return fail(ZERO_ERR_ALIGNMENT, "C is misaligned");
+    return ZERO_OK;
+}
+
+}  // namespace zs
+
+extern "C" {
+
+zero_status zero_gemm_bf16(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                           int32_t a_order, const uint16_t *B, int64_t ldb, int32_t b_order,
+                           void *C, int64_t ldc, int32_t c_dtype, void *stream)
+{
+    const zero_status st = zs::gemm_check(M, N, K, A, lda, a_order, B, ldb, b_order, C, ldc,
+                                          c_dtype);
+    if (st != ZERO_OK || M == 0 || N == 0)
+        return st;
+    const bool ao = a_order == ZERO_K_OUTER, bo = b_order == ZERO_K_OUTER;
+    const int64_t tm = (M + zs::kBM - 1) / zs::kBM, tn = (N + zs::kBN - 1) / zs::kBN;
     // One block per CU at a time (128 KB of LDS).  A last wave of at most
     // half the CUs runs as twice as many half tiles.
     const int64_t T = tm * tn, P = zs::cu_count();

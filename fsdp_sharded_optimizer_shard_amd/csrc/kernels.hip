@@ -612,23 +612,35 @@ __global__ __launch_bounds__(64) void step_advance_kernel(int64_t *step)
 // ------------------------------------------------------- clip kernel --
 
 // One block of 1024 threads: thread i sums partials i, i + 1024, ... into
-// four independent fp64 accumulators (element k goes to accumulator k mod 4,
-// so four loads are in flight), adds them in order, then a fixed-order block
+// kClipAcc independent fp64 accumulators (the k-th of its elements goes to
+// accumulator k mod kClipAcc, so that many loads are in flight: the kernel
+// is bound by load latency), adds them in order, then a fixed-order block
 // sum.  The order is fixed for a given n, so the result is deterministic.
+constexpr int kClipAcc = 16;
 __global__ __launch_bounds__(kClipThreads) void clip_kernel(const double *partials, int64_t n,
                                                             float max_norm, float *coef,
                                                             double *norm_out)
 {
-    double s[4] = {0.0, 0.0, 0.0, 0.0};
-    int64_t i = threadIdx.x;
-    for (; i + 3 * kClipThreads < n; i += 4 * kClipThreads) {
+    double s[kClipAcc];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+    for (int k = 0; k < kClipAcc; ++k)
+        s[k] = 0.0;
+    int64_t i = threadIdx.x;
+    for (; i + (kClipAcc - 1) * kClipThreads < n; i += kClipAcc * kClipThreads) {
+#pragma unroll
+        for (int k = 0; k < kClipAcc; ++k)
             s[k] = s[k] + partials[i + k * kClipThreads];
     }
-    for (int k = 0; i < n; i += kClipThreads, ++k)
-        s[k] = s[k] + partials[i];
-    const double total = block_sum<kClipThreads>(((s[0] + s[1]) + s[2]) + s[3]);
+    // fewer than kClipAcc elements of this thread remain
+#pragma unroll
+    for (int k = 0; k < kClipAcc; ++k)
+        if (i + (int64_t)k * kClipThreads < n)
+            s[k] = s[k] + partials[i + k * kClipThreads];
+    double t = 0.0;
+#pragma unroll
+    for (int k = 0; k < kClipAcc; ++k)
+        t = t + s[k];
+    const double total = block_sum<kClipThreads>(t);
     if (threadIdx.x == 0) {
         const double norm = sqrt(total);
         const float c = (float)((double)max_norm / (norm + 1e-6));

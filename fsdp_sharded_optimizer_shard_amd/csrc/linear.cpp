@@ -18,6 +18,9 @@
 namespace zs {
 zero_status zero_rows_fill(float *p, int64_t ld, int64_t r0, int64_t r1, int64_t cols,
                            hipStream_t s);
+zero_status gemm_check(int64_t M, int64_t N, int64_t K, const uint16_t *A, int64_t lda,
+                       int32_t a_order, const uint16_t *B, int64_t ldb, int32_t b_order,
+                       const void *C, int64_t ldc, int32_t c_dtype);
 }
 
 namespace {
@@ -38,6 +41,19 @@ zero_status layer_dims(const zero_layout *L, int32_t unit, Dims *d)
     return ZERO_OK;
 }
 
+// The shards the gather reads: every one present and 2-byte aligned (the
+// gather's own checks), so that a layer call fails before its first launch.
+zero_status check_shards(const zero_layout *L, const uint16_t *const *w_shards)
+{
+    for (int32_t q = 0; q < L->parts; ++q) {
+        if (!w_shards[q])
+            return zs::fail(ZERO_ERR_INVALID_ARG, "W shard of rank %d is NULL", q);
+        if (reinterpret_cast<uintptr_t>(w_shards[q]) % 2)
+            return zs::fail(ZERO_ERR_ALIGNMENT, "W shard of rank %d is misaligned", q);
+    }
+    return ZERO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -54,12 +70,15 @@ zero_status zero_fsdp_linear_forward(const zero_layout *L, int32_t unit,
     if (!w_shards || !x || !w_full || !y || batch < 0)
         return zs::fail(ZERO_ERR_INVALID_ARG, "w_shards, x, w_full, y and batch >= 0 are "
                         "required");
-    for (int32_t q = 0; q < L->parts; ++q)
-        if (!w_shards[q])
-            return zs::fail(ZERO_ERR_INVALID_ARG, "W shard of rank %d is NULL", q);
+    if ((st = check_shards(L, w_shards)) != ZERO_OK)
+        return st;
     if (d.in % 8 || d.out % 8)
         return zs::fail(ZERO_ERR_UNSUPPORTED, "in_features and out_features must be "
                         "multiples of 8");
+    // every check before the first launch: the GEMM's too
+    if ((st = zs::gemm_check(batch, d.out, d.in, x, d.in, ZERO_K_INNER, w_full, d.out,
+                             ZERO_K_OUTER, y, d.out, y_dtype)) != ZERO_OK)
+        return st;
     if ((st = zero_gather_params(L, unit, unit + 1, w_shards, L->parts, w_full, stream)) != ZERO_OK)
         return st;
     // Y = X W: a(i, k) = X[i][k], b(j, k) = W[k][j]
@@ -78,12 +97,17 @@ zero_status zero_fsdp_linear_backward(const zero_layout *L, int32_t unit,
         return st;
     if (!w_shards || !x || !dy || !w_full || !dx || !dw_full || batch < 0)
         return zs::fail(ZERO_ERR_INVALID_ARG, "every buffer and batch >= 0 are required");
-    for (int32_t q = 0; q < L->parts; ++q)
-        if (!w_shards[q])
-            return zs::fail(ZERO_ERR_INVALID_ARG, "W shard of rank %d is NULL", q);
+    if ((st = check_shards(L, w_shards)) != ZERO_OK)
+        return st;
     if (d.in % 8 || d.out % 8 || batch % 8)
         return zs::fail(ZERO_ERR_UNSUPPORTED, "in_features, out_features and batch must be "
                         "multiples of 8");
+    // every check before the first launch: both GEMMs' too
+    if ((st = zs::gemm_check(batch, d.in, d.out, dy, d.out, ZERO_K_INNER, w_full, d.out,
+                             ZERO_K_INNER, dx, d.in, dx_dtype)) != ZERO_OK ||
+        (st = zs::gemm_check(d.in, d.out, batch, x, d.in, ZERO_K_OUTER, dy, d.out, ZERO_K_OUTER,
+                             dw_full, d.out, ZERO_FP32)) != ZERO_OK)
+        return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // re-gather W (FSDP frees it after forward)
     if ((st = zero_gather_params(L, unit, unit + 1, w_shards, L->parts, w_full, stream)) != ZERO_OK)

@@ -480,3 +480,99 @@ def test_noalloc_clip_step_validation_makes_no_hip_call():
     assert e.status == zs.ERR_UNSUPPORTED and "static buffer" in str(e)
     # an empty range needs no partials and launches nothing
     f(L, 1, 1, cfg, 1.0, g, *args)
+
+
+def test_linear_layer_checks_every_gemm_before_the_gather():
+    # arguments that only a GEMM of the layer would refuse come back with
+    # that GEMM's error, not a HIP error from a gather launched first
+    # (these addresses are fake: any launch fails on the host)
+    L = zs.shard_init_rows("fsdp2", 4, 1, [(16, 16)])
+    fw = zs.fsdp_linear_forward
+    bw = zs.fsdp_linear_backward
+    assert _err(fw, L, 0, [FAKE] * 4, 8, FAKE + 8, FAKE, FAKE, stream=0).status == \
+        zs.ERR_ALIGNMENT                                   # X not 16-byte aligned
+    assert _err(fw, L, 0, [FAKE] * 4, 8, FAKE, FAKE, FAKE + 1, stream=0).status == \
+        zs.ERR_ALIGNMENT                                   # Y (bf16) misaligned
+    assert _err(fw, L, 0, [FAKE] * 4, 8, FAKE, FAKE, FAKE, y_dtype=5, stream=0).status == \
+        zs.ERR_INVALID_ARG
+    assert _err(fw, L, 0, [FAKE, FAKE + 1, FAKE, FAKE], 8, FAKE, FAKE, FAKE,
+                stream=0).status == zs.ERR_ALIGNMENT       # a W shard misaligned
+    assert _err(bw, L, 0, [FAKE] * 4, 8, FAKE, FAKE + 8, FAKE, FAKE, FAKE,
+                stream=0).status == zs.ERR_ALIGNMENT       # dY not 16-byte aligned
+    assert _err(bw, L, 0, [FAKE] * 4, 8, FAKE, FAKE, FAKE, FAKE, FAKE + 2,
+                stream=0).status == zs.ERR_ALIGNMENT       # dW (fp32) misaligned
+    assert _err(bw, L, 0, [FAKE] * 4, 8, FAKE + 8, FAKE, FAKE, FAKE, FAKE,
+                stream=0).status == zs.ERR_ALIGNMENT       # X (dW's A) misaligned
+
+
+def test_binding_checks_tensor_sizes_dtypes_and_contiguity():
+    # an undersized, mistyped or strided tensor is refused by the binding
+    # before the library is called.  Host tensors are refused first of all,
+    # so the cases use a stand-in that carries the attributes the checks
+    # read and reports itself as a GPU tensor.
+    import torch
+
+    class Dev:
+        """A device-tensor stand-in: the checks read dtype, numel,
+        element_size, is_contiguous and is_cuda; the library never sees it."""
+        def __init__(self, n, dtype=torch.float32, contiguous=True):
+            self.dtype, self._n, self._c = dtype, n, contiguous
+            self.is_cuda, self.device = True, "cuda:0"
+
+        def numel(self):
+            return self._n
+
+        def element_size(self):
+            return torch.empty(0, dtype=self.dtype).element_size()
+
+        def is_contiguous(self):
+            return self._c
+
+        def data_ptr(self):
+            return FAKE
+
+    L = zs.shard_init("zero3", 4, 1, [1000, 24])   # shard 250 + 6, flat 1000 + 24
+    shard, full = L.range_lens(0, 2)
+    assert (shard, full) == (256, 1024)
+    assert L.range_lens(1, 2) == (6, 24) and L.range_lens(0, 3) == (None, None)
+    cfg = zs.adam_cfg(step=1)
+    good = dict(master=Dev(shard), m=Dev(shard), v=Dev(shard))
+    G = zs.Grads([Dev(shard, torch.int16)] * 4, zs.BF16, zs.INDEX_SHARD)
+
+    def step(**kw):
+        a = dict(good, param_out=Dev(full, torch.int16), grads=G)
+        a.update(kw)
+        zs.adam_step(L, 0, 2, cfg, a.pop("master"), a.pop("m"), a.pop("v"), a.pop("param_out"),
+                     stream=0, **a)
+
+    with pytest.raises(ValueError, match="master holds 255 elements, the call touches 256"):
+        step(master=Dev(shard - 1))
+    with pytest.raises(ValueError, match="v: dtype"):
+        step(v=Dev(shard, torch.float64))
+    with pytest.raises(ValueError, match="m must be contiguous"):
+        step(m=Dev(shard, contiguous=False))
+    with pytest.raises(ValueError, match="param_out holds 1023"):
+        step(param_out=Dev(full - 1, torch.int16))
+    with pytest.raises(ValueError, match="gradient buffer of rank 2 holds"):
+        step(grads=zs.Grads([Dev(shard, torch.int16)] * 2 + [Dev(7, torch.int16)] +
+                            [Dev(shard, torch.int16)], zs.BF16, zs.INDEX_SHARD))
+    with pytest.raises(ValueError, match="gradient buffer of rank 0: dtype"):
+        step(grads=zs.Grads([Dev(shard)] * 4, zs.BF16, zs.INDEX_SHARD))
+    with pytest.raises(ValueError, match="shard of rank 3 holds"):
+        zs.gather_params(L, 0, 2, [Dev(shard, torch.int16)] * 3 + [Dev(9, torch.int16)],
+                         Dev(full, torch.int16), stream=0)
+    with pytest.raises(ValueError, match="param_full holds"):
+        zs.gather_params(L, 0, 2, [None] * 4, Dev(full - 8, torch.int16), stream=0)
+    with pytest.raises(ValueError, match="main_grad holds"):
+        zs.grad_accumulate(Dev(15), Dev(16, torch.int16), 16, stream=0)
+    with pytest.raises(ValueError, match="table holds"):
+        zs.adam_step_table(L, 0, 2, Dev(47, torch.uint8), 1, Dev(1, torch.int64), **good,
+                           param_out=Dev(full, torch.int16), grads=G, stream=0)
+    with pytest.raises(ValueError, match="sumsq_partials holds"):
+        zs.reduce_shard(L, 0, 2, G, Dev(shard), Dev(3, torch.float64), 4, stream=0)
+    with pytest.raises(ValueError, match="C holds"):
+        zs.gemm_bf16(16, 16, 16, Dev(256, torch.int16), 16, zs.K_INNER, Dev(256, torch.int16),
+                     16, zs.K_INNER, Dev(255), 16, stream=0)
+    with pytest.raises(ValueError, match="B holds"):
+        zs.gemm_bf16(16, 16, 32, Dev(512, torch.int16), 32, zs.K_INNER, Dev(511, torch.int16),
+                     16, zs.K_OUTER, Dev(256), 16, stream=0)
