@@ -855,11 +855,18 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
 // requests in flight the memory controllers mix the read and write streams
 // better; the kernel's time is that of its memory traffic (the same streams
 // without the arithmetic run no faster; zero_stream_mix).
+//
+// A launch whose tiles fit on the GPU at once under the cap (at most
+// kStepBlocksPerCU per CU) never has more in flight than the cap allows, so
+// it reserves nothing: small launches (a tiny shard, one bucket of a few
+// tiles) keep the plain dispatch.
 template <int MODE, int NR, bool BF16>
 void launch_one(const StepArgs &a, hipStream_t st)
 {
-    const size_t lds = step_lds_reserve();
-    static const int resident = resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads, lds);
+    const size_t lds =
+        a.n_tiles > (int64_t)device_cus() * kStepBlocksPerCU ? step_lds_reserve() : 0;
+    static const int resident =
+        resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads, step_lds_reserve());
     const int64_t blocks = stream_grid(a.n_tiles, resident, kStepThreads);
     hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kStepThreads),
                        lds, st, a);

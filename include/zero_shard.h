@@ -141,7 +141,15 @@ typedef struct zero_adam_cfg {
 /* Plan the layout of one rank: `n_units` units of unpadded sizes
    `unit_numel` (host array, each >= 0, at least one unit), `world_n` >= 1
    ranks, this rank `rank` in [0, world_n).  Host memory only; no HIP call.
-   *out receives a layout to free with zero_shard_destroy. */
+   *out receives a layout to free with zero_shard_destroy.
+   Source: "DP, ZeRO-1/2/3, FSDP" notes, concepts "ZeRO-1 / 2 / 3" (the
+   model states are cut into N parts by data-parallel rank; each rank keeps
+   and updates only its part) and "FSDP" (the model is split into units),
+   and the follow-up "FSDP2 vs FSDP1" (FSDP1 flattens and concatenates a
+   unit's parameters into one flat buffer and shards that); "Data Parallel,
+   ZeRO and FSDP", section "ZeRO and FSDP".  The padding of each unit to a
+   multiple of N is this layout's reading (the pages do not say how an
+   uneven unit is cut). */
 zero_status zero_shard_init(zero_layout **out, zero_strategy strategy,
                             int32_t world_n, int32_t rank, int32_t n_units,
                             const int64_t *unit_numel);
@@ -170,7 +178,10 @@ zero_status zero_layout_info(const zero_layout *layout, int64_t *flat_len,
                              int32_t *strategy);
 
 /* Per-unit numbers (see LAYOUT): n_u, L_u, F_u, s_u, R_u and the rank's
-   flat offset F_u + r*s_u.  Any output pointer may be NULL. */
+   flat offset F_u + r*s_u.  Any output pointer may be NULL.  These are the
+   offsets of the flat-buffer sharding that zero_shard_init plans (same
+   source): where unit u sits in the flat buffer, where its slice sits in a
+   rank's shard, and which flat elements this rank owns. */
 zero_status zero_layout_query(const zero_layout *layout, int32_t unit,
                               int64_t *numel, int64_t *padded_len,
                               int64_t *flat_off, int64_t *shard_len,
@@ -197,7 +208,14 @@ zero_status zero_layout_rows(const zero_layout *layout, int32_t unit,
    zero_reduce_partials_count(...) fp64 partial sums of out[i]^2 (each square
    exact in fp64; one partial per 1024-element tile of a unit slice, summed
    in a fixed order), for the global-norm clip; `n_partials` is the capacity
-   of that buffer. */
+   of that buffer.
+   Source: "DP, ZeRO-1/2/3, FSDP" notes, concepts "reduce-scatter and
+   all-gather" (a reduce-scatter sums the ranks' buffers and leaves each
+   rank 1/N of the result; with the all-gather it makes an all-reduce);
+   "Data Parallel, ZeRO and FSDP", section "Plain data parallel (DDP)"
+   (after the all-reduce every replica holds the mean gradient) and section
+   "ZeRO and FSDP" (gradients are reduce-scattered so that each GPU keeps
+   its shard).  Summing in ascending rank order is this library's reading. */
 zero_status zero_reduce_shard(const zero_layout *layout, int32_t unit_begin,
                               int32_t unit_end, const zero_grads *grads,
                               float *out, int32_t out_index,
@@ -210,8 +228,10 @@ zero_status zero_reduce_shard(const zero_layout *layout, int32_t unit_begin,
 int64_t zero_reduce_partials_count(const zero_layout *layout,
                                    int32_t unit_begin, int32_t unit_end);
 
-/* Global gradient-norm clip coefficient (not defined on the pages; PyTorch
-   clip_grad_norm_ semantics): norm = sqrt(sum of the n partials in fp64, in
+/* Global gradient-norm clip coefficient.  Not on the pages: the
+   GPT-2-small workload with a global-norm clip at 1.0 names it, and the
+   reading taken is PyTorch's clip_grad_norm_:
+   norm = sqrt(sum of the n partials in fp64, in
    a fixed order for a given n: strided per-thread sums, then a fixed tree),
    *coef_out = min(1, fp32(max_norm / (norm + 1e-6))).
    `partials`, `coef_out` (one float) and `norm_out` (one double, may be
@@ -255,6 +275,11 @@ zero_status zero_adam_step_clip_noalloc(const zero_layout *layout, int32_t unit_
 
 /* Adam / AdamW on this rank's slices of units [unit_begin, unit_end), then
    bf16 rounding of the new master into `param_out`.
+   Source: "DP, ZeRO-1/2/3, FSDP" notes, concepts "Model states" (bf16
+   parameter and gradient, fp32 master, m and v: 12 of the 16 bytes per
+   parameter) and "ZeRO-1 / 2 / 3" (each rank updates only its part); the
+   update itself is Kingma & Ba (2015) Algorithm 1 and, for AdamW,
+   Loshchilov & Hutter (2019), as the pages leave it to the optimizer.
    Gradient source, exactly one of:
      grad_fp32 != NULL: fp32 averaged gradient, indexed as `grad_index`
                         says: ZERO_INDEX_SHARD for a reduce-scatter result
@@ -327,7 +352,11 @@ zero_status zero_step_advance(int64_t *step_counter, void *stream);
 
 /* ------------------------------------------------------------ gather -- */
 
-/* All-gather data movement: for every rank q < n with shards[q] != NULL
+/* All-gather data movement (source: "DP, ZeRO-1/2/3, FSDP" notes, concepts
+   "reduce-scatter and all-gather": an all-gather puts the ranks' 1/N
+   slices back together into the whole; "Data Parallel, ZeRO and FSDP",
+   section "ZeRO and FSDP": a layer's parameter shards are all-gathered
+   before it runs): for every rank q < n with shards[q] != NULL
    and every element j of rank q's slice of unit u in the range,
        param_full[(F_u - F_begin) + q*s_u + j] = shards[q][(R_u - R_begin) + j]
    Bit copies.  `shards` is a host array of n = world_n device pointers
@@ -399,7 +428,11 @@ zero_status zero_fsdp_sweep_table(const zero_layout *layout, int32_t unit_begin,
 /* ------------------------------------------------------- accumulation -- */
 
 /* Megatron-style fp32 main-gradient accumulation of one micro-batch:
-   main_grad[i] = main_grad[i] + float(micro_bf16[i]) for i < n. */
+   main_grad[i] = main_grad[i] + float(micro_bf16[i]) for i < n.
+   Source: "DP, ZeRO-1/2/3, FSDP" notes, worked example "7B, N = 8", the
+   note under the Megatron distributed-optimizer row (the gradient is kept
+   and accumulated in fp32: 4 bytes per parameter, replicated); the bf16
+   micro-batch gradient is this library's reading (the model is bf16). */
 zero_status zero_grad_accumulate(float *main_grad, const uint16_t *micro_bf16,
                                  int64_t n, void *stream);
 
