@@ -84,6 +84,43 @@ def test_fused_step_and_gather_in_a_graph():
     _replay_and_compare(lambda: step(G), lambda: step(E), G, E)
 
 
+def test_launches_with_the_occupancy_reservation_in_a_graph():
+    # the step kernel reserves LDS (its occupancy cap) only for launches of
+    # more tiles than fit on the GPU at once, 5 per CU: a shard of about two
+    # million elements (1954 tiles of 1024) takes that path, under capture
+    units, n, r = [6_000_000, 2_000_003], 4, 1
+    L = zs.shard_init("zero3", n, r, units)
+    S, P = L.shard_len, L.flat_len
+    assert S > 256 * 5 * 1024
+    w = small_workload(units, n, "zero3", cfg=12)
+    grads = [grad_bits(w, 0, q, S, device=DEV) for q in range(n)]
+    peers = [None if q == r else grad_bits(w, 1, q, S, device=DEV) for q in range(n)]
+    cfg = zs.adam_cfg(lr=1e-3, step=4)
+    npart = zs.reduce_partials_count(L, 0, len(units))
+
+    def buffers():
+        master, m, v = _state(S, 7)
+        return [master, m, v, torch.zeros(P, dtype=torch.int16, device=DEV),
+                master.clone(), m.clone(), v.clone(), torch.zeros(P, dtype=torch.int16, device=DEV),
+                torch.empty(S, device=DEV), torch.empty(npart, dtype=torch.float64, device=DEV),
+                torch.empty(1, device=DEV)]
+
+    def step(b):
+        G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+        zs.adam_step(L, 0, len(units), cfg, b[0], b[1], b[2], b[3], grads=G)
+        zs.gather_params(L, 0, len(units), peers, b[3])
+        zs.reduce_shard(L, 0, len(units), G, b[8], b[9], npart)
+        zs.clip_coef(b[9], npart, 1e-3, b[10])
+        zs.adam_step(L, 0, len(units), cfg, b[4], b[5], b[6], b[7], grad_fp32=b[8],
+                     clip_coef=b[10])
+
+    G_, E_ = buffers(), buffers()
+    step(buffers())
+    torch.cuda.synchronize()
+    _replay_and_compare(lambda: step(G_), lambda: step(E_), G_, E_)
+    assert float(E_[10]) < 1.0
+
+
 def test_two_pass_clip_in_a_graph():
     units, n, r = [25000, 9001], 4, 2
     L = zs.shard_init("zero2", n, r, units)
