@@ -134,12 +134,16 @@ def phase(ph, name, fn):
         ph.run(name, fn)
 
 
-def roofline(name, bytes_per_launch, ms_per_launch, traffic=None):
+def roofline(name, bytes_per_launch, ms_per_launch, traffic=None, counters=COUNTERS):
     gbps = bytes_per_launch / (ms_per_launch * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": name, "achieved": gbps, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                             "copy-calibrated)",
+            "traffic_source": (f"the committed counter summary {os.path.relpath(counters, ROOT)}, "
+                               "taken on the kernel source whose sha256 it records; not measured "
+                               "in this run (null when the source has changed since or no "
+                               "summary covers this kernel)"),
             "algorithmic_bytes": bytes_per_launch}
 
 
