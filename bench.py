@@ -77,6 +77,10 @@ def parse():
                     help="instead of a step: the fused 7B step against zero_stream_mix (its "
                          "streams without the arithmetic, its reads, its writes) on this many "
                          "fresh placements")
+    ap.add_argument("--state-chunk", type=int, default=None, metavar="E",
+                    help="headline and --calibrate-mix: master, m and v as one buffer of "
+                         "E-element chunks (zero_layout_chunk_state); 0 keeps three arrays; "
+                         "default: the library's ZERO_STATE_CHUNK_DEFAULT")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
@@ -163,18 +167,53 @@ def add_rates(kernels, name, bytes_per_launch):
 
 # ------------------------------------------------------------ workloads --
 
+class State:
+    """One shard's fp32 master, m and v in the layout's state format: three
+    arrays, or one buffer of E-element chunks (master | m | v per chunk)."""
+
+    def __init__(self, torch, L, master0):
+        S, E = L.shard_len, L.state_chunk
+        self.E, self.buf = E, None
+        if E == 0:
+            self.views = (master0, torch.zeros(S, device=master0.device),
+                          torch.zeros(S, device=master0.device))
+            return
+        rows = -(-S // E)
+        self.buf = torch.zeros(L.state_len, device=master0.device)
+        col = torch.zeros(rows * E, device=master0.device)
+        col[:S] = master0
+        self.buf.view(rows, 3, E)[:, 0, :].copy_(col.view(rows, E))
+        del col
+        self.views = L.state_views(self.buf)
+
+    def master(self, off, n):
+        """The master values of shard elements [off, off + n) (a tensor)."""
+        if self.E == 0:
+            return self.views[0][off:off + n]
+        E = self.E
+        r0, r1 = off // E, -(-(off + n) // E)
+        return self.buf.view(-1, 3, E)[r0:r1, 0, :].reshape(-1)[off - r0 * E:off - r0 * E + n]
+
+
+def state_desc(E):
+    return ("three fp32 arrays (master, m, v)" if E == 0 else
+            f"one fp32 buffer of {E}-element chunks, master | m | v per chunk")
+
+
 def headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=True):
     """A fresh allocation of the headline step's buffers (one placement)."""
     from synthetic import grad_bits, master_init
     grads = [grad_bits(w, 0, q, S, device=dev) for q in range(N)]
-    master = master_init(w, S, device=dev, rank=r)
-    m = torch.zeros(S, device=dev)
-    v = torch.zeros(S, device=dev)
+    st = State(torch, L, master_init(w, S, device=dev, rank=r))
     full = torch.empty(L.flat_len, dtype=torch.int16, device=dev)
     peers = ([torch.full((S,), q + 1, dtype=torch.int16, device=dev) for q in range(N - 1)]
              if rank_peers else [])
     torch.cuda.synchronize()
-    return grads, master, m, v, full, peers
+    return grads, st, full, peers
+
+
+def state_chunk(args, zs):
+    return zs.STATE_CHUNK_DEFAULT if args.state_chunk is None else args.state_chunk
 
 
 def release(torch, *objs):
@@ -201,15 +240,18 @@ def run_headline(args, torch, zs, np):
         L = zs.shard_init_rows("fsdp2", N, r, mistral7b_shapes())
     else:
         L = zs.shard_init("zero3", N, r, list(w.units))
+    L = L.chunk_state(state_chunk(args, zs))
     S = L.shard_len
     U = L.info()["n_units"]
     print(f"# setup: {w.name}, rank {r}, shard {S} elements, {U} units, "
-          f"{args.placements} placements", file=sys.stderr, flush=True)
+          f"{args.placements} placements, state: {state_desc(L.state_chunk)}", file=sys.stderr,
+          flush=True)
     fused_b, gather_b = 42 * S, 4 * (N - 1) * S
     runs = []
     cpu = cmp = None
     for k in range(args.placements):
-        grads, master, m, v, full, peers = headline_buffers(torch, zs, w, L, S, N, r, dev)
+        grads, st, full, peers = headline_buffers(torch, zs, w, L, S, N, r, dev)
+        master, m, v = st.views
         shard_ptrs = peers + [None]                  # own slice is written by the step
         G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
         t = [0]
@@ -231,12 +273,12 @@ def run_headline(args, torch, zs, np):
               flush=True)
         if k == args.placements - 1:
             if args.cpu_baseline_seconds > 0:
-                cpu = cpu_baseline(w, grads, master, S, r, args.cpu_baseline_seconds)
+                cpu = cpu_baseline(w, grads, st.master, S, r, args.cpu_baseline_seconds)
             if args.vs_torch:
-                cmp = step_vs_torch(torch, zs, L, U, w, grads, master, m, v, full, G, r, S)
+                cmp = step_vs_torch(torch, zs, L, U, w, grads, st, full, G, r, S)
         del G, shard_ptrs
         release(torch, grads, peers)
-        del grads, master, m, v, full, peers
+        del grads, st, master, m, v, full, peers
         torch.cuda.empty_cache()
     order = sorted(range(len(runs)), key=lambda i: runs[i][0])
     ms, kern = runs[order[len(order) // 2]]
@@ -246,6 +288,7 @@ def run_headline(args, torch, zs, np):
                     "rank shard step: reduce 8 bf16 rank grads + Adam + "
                     "bf16 cast into the flat buffer + gather of 7 peer shards",
                     psi=L.flat_len, n_ranks=N, rank=r, shard_elems=S, units=U,
+                    state_layout=state_desc(L.state_chunk),
                     algorithmic_bytes_per_step=fused_b + gather_b)
     out["step_gbps"] = (fused_b + gather_b) / (ms * 1e-3) / 1e9
     out["state_gbps_16psi_over_n"] = 16 * S / (ms * 1e-3) / 1e9
@@ -268,7 +311,7 @@ def run_headline(args, torch, zs, np):
     return out
 
 
-def step_vs_torch(torch, zs, L, U, w, grads, master, m, v, full, G, r, S, rounds=5, iters=5):
+def step_vs_torch(torch, zs, L, U, w, grads, st, full, G, r, S, rounds=5, iters=5):
     """The rank's reduce + Adam + bf16 cast composed from PyTorch ops on the
     same inputs: the fp32 sum of the N bf16 gradients in rank order (in-place
     mixed-dtype adds), one division by N, torch.optim.Adam(fused=True) on an
@@ -276,9 +319,10 @@ def step_vs_torch(torch, zs, L, U, w, grads, master, m, v, full, G, r, S, rounds
     flat buffer.  Timed alternately with zero_adam_step (the fused kernel),
     `iters` steps per round, on the current stream with HIP events."""
     N = len(grads)
+    master, m, v = st.views
     gb = [g.view(torch.bfloat16) for g in grads]
     own = full.view(torch.bfloat16)[r * S:(r + 1) * S]
-    p = torch.nn.Parameter(master.detach().clone())
+    p = torch.nn.Parameter(st.master(0, S).detach().clone())
     acc = torch.empty(S, device=master.device)
     try:
         opt = torch.optim.Adam([p], lr=w.lr, betas=(w.beta1, w.beta2), eps=w.eps, fused=True)
@@ -669,7 +713,8 @@ def run_fsdp70b(args, torch, zs, np):
     if args.cpu_baseline_seconds > 0:
         # one layer unit x 64 ranks on the CPU, extrapolated to the 81 units
         s0 = q[0]["shard_len"]
-        out["cpu_baseline"] = cpu_baseline(w, grads, master, s0, r, args.cpu_baseline_seconds,
+        out["cpu_baseline"] = cpu_baseline(w, grads, lambda a, n: master[a:a + n], s0, r,
+                                           args.cpu_baseline_seconds,
                                            what="rank-{r} shard of layer unit 0", total=S)
     return out
 
@@ -830,15 +875,15 @@ def calibrate_mix(args, torch, zs, np, rounds=5):
     dev = torch.device("cuda:0")
     w = WORKLOADS[2]
     N, r = w.n_ranks, w.n_ranks - 1
-    L = zs.shard_init("zero3", N, r, list(w.units))
-    S = L.shard_len
+    L = zs.shard_init("zero3", N, r, list(w.units)).chunk_state(state_chunk(args, zs))
+    S, SE = L.shard_len, L.state_chunk
     kinds = {"fused_step": 42 * S, "step_streams_no_math": 42 * S, "reads_only": 28 * S,
              "writes_only": 14 * S}
     E = torch.cuda.Event
     per = {k: [] for k in kinds}
     for pl in range(args.calibrate_mix):
-        grads, master, m, v, full, _ = headline_buffers(torch, zs, w, L, S, N, r, dev,
-                                                        rank_peers=False)
+        grads, st, full, _ = headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=False)
+        master, m, v = st.views
         own = full[r * S:(r + 1) * S]
         G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
         t = [0]
@@ -850,9 +895,11 @@ def calibrate_mix(args, torch, zs, np, rounds=5):
 
         fns = {"fused_step": fused,
                "step_streams_no_math": lambda: zs.stream_mix(zs.MIX_STEP_STREAMS, grads, master,
-                                                             m, v, own, S),
-               "reads_only": lambda: zs.stream_mix(zs.MIX_READS, grads, master, m, v, own, S),
-               "writes_only": lambda: zs.stream_mix(zs.MIX_WRITES, grads, master, m, v, own, S)}
+                                                             m, v, own, S, state_chunk=SE),
+               "reads_only": lambda: zs.stream_mix(zs.MIX_READS, grads, master, m, v, own, S,
+                                                   state_chunk=SE),
+               "writes_only": lambda: zs.stream_mix(zs.MIX_WRITES, grads, master, m, v, own, S,
+                                                    state_chunk=SE)}
         got = {k: [] for k in kinds}
         names = list(kinds)
         for rd in range(rounds + 1):
@@ -871,11 +918,12 @@ def calibrate_mix(args, torch, zs, np, rounds=5):
               file=sys.stderr, flush=True)
         del G, own
         release(torch, grads)
-        del grads, master, m, v, full
+        del grads, st, master, m, v, full
         torch.cuda.empty_cache()
     med = {k: sorted(x)[len(x) // 2] for k, x in per.items()}
     return {"calibrate_mix": {
         "workload": "Mistral-7B ZeRO-3 rank shard, N=8, 905,000,000 elements",
+        "state_layout": state_desc(SE),
         "placements": args.calibrate_mix, "rounds_per_placement": rounds,
         "ms_per_placement": per,
         "ms_median": med,
@@ -915,7 +963,7 @@ def host_cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, grads, master, S, r, budget_s, what="rank-{r} shard", total=None):
+def cpu_baseline(w, grads, master_of, S, r, budget_s, what="rank-{r} shard", total=None):
     """The oracle, as it stands, on the first elements of the same shard:
     16M-element chunks are copied from the GPU and stepped (step 1) until the
     single-threaded oracle has run for `budget_s` seconds or the S elements
@@ -938,7 +986,7 @@ def cpu_baseline(w, grads, master, S, r, budget_s, what="rank-{r} shard", total=
     while spent < budget_s and done < S:
         n = min(chunk, S - done)
         g = [x[done:done + n].cpu().numpy().view(np.uint16) for x in grads]
-        p0 = master[done:done + n].cpu().numpy()
+        p0 = master_of(done, n).cpu().numpy()
         p, m, v = p0.copy(), np.zeros(n, np.float32), np.zeros(n, np.float32)
         out, tmp = np.empty(n, np.uint16), np.empty(n, np.float32)
         t0 = time.perf_counter()

@@ -39,6 +39,8 @@ K_INNER, K_OUTER = 0, 1
 MIX_STEP_STREAMS, MIX_READS, MIX_WRITES = 0, 1, 2
 MAX_RANKS_PER_CALL = 64
 NOALLOC_MAX_PARTIALS = 524288
+STATE_CHUNK_MIN, STATE_CHUNK_MAX = 4, 1 << 24     # zero_layout_chunk_state bounds
+STATE_CHUNK_DEFAULT = 8192                         # the measured best on MI355X
 
 STRATEGY = {"ddp": DDP, "zero1": STAGE1, "zero1_allreduce": STAGE1, "zero2": STAGE2,
             "zero3": STAGE3, "fsdp": FSDP, "fsdp2": FSDP, "megatron_do": MEGATRON_DO}
@@ -84,6 +86,10 @@ _lib.zero_layout_info.argtypes = [_P] + [ctypes.POINTER(_I64)] * 2 + [ctypes.POI
 _lib.zero_layout_info.restype = _I32
 _lib.zero_layout_query.argtypes = [_P, _I32] + [ctypes.POINTER(_I64)] * 6
 _lib.zero_layout_query.restype = _I32
+_lib.zero_layout_chunk_state.argtypes = [_P, _I64, ctypes.POINTER(_P)]
+_lib.zero_layout_chunk_state.restype = _I32
+_lib.zero_layout_state.argtypes = [_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+_lib.zero_layout_state.restype = _I32
 _lib.zero_reduce_shard.argtypes = [_P, _I32, _I32, ctypes.POINTER(_Grads), _P, _I32, _P, _I64,
                                    _P]
 _lib.zero_reduce_shard.restype = _I32
@@ -134,7 +140,7 @@ _lib.zero_fsdp_linear_backward.argtypes = [_P, _I32, ctypes.POINTER(ctypes.c_voi
                                            _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_linear_backward.restype = _I32
 _lib.zero_stream_mix.argtypes = [_I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P, _P, _P,
-                                 _I64, _P]
+                                 _I64, _I64, _P]
 _lib.zero_stream_mix.restype = _I32
 _lib.zero_grad_accumulate.argtypes = [_P, _P, _I64, _P]
 _lib.zero_grad_accumulate.restype = _I32
@@ -144,7 +150,8 @@ _lib.zero_last_error.argtypes = []
 _lib.zero_last_error.restype = ctypes.c_char_p
 
 EXPORTS = ("zero_shard_init", "zero_shard_init_rows", "zero_layout_rows", "zero_shard_destroy",
-           "zero_layout_info", "zero_layout_query", "zero_reduce_shard",
+           "zero_layout_info", "zero_layout_query", "zero_layout_chunk_state", "zero_layout_state",
+           "zero_reduce_shard",
            "zero_reduce_partials_count", "zero_clip_coef", "zero_adam_step",
            "zero_adam_step_clip_noalloc",
            "zero_adam_table_fill", "zero_adam_step_table", "zero_step_advance", "zero_gather_params",
@@ -234,6 +241,7 @@ class Layout:
         self.units = list(units)
         self._uq = None
         self._lens = {}
+        self._state = None
 
     def _unit_table(self):
         """Every unit's query(), read once (a layout never changes)."""
@@ -294,6 +302,54 @@ class Layout:
         _check(_lib.zero_layout_rows(self.handle, unit, *[ctypes.byref(x) for x in v]),
                "zero_layout_rows")
         return dict(zip(("cols", "first_row", "row_count"), (x.value for x in v)))
+
+    def chunk_state(self, chunk: int) -> "Layout":
+        """A copy of this layout whose master, m and v form one buffer in
+        chunks of `chunk` elements (0: three arrays); see state_views()."""
+        h = _P()
+        _check(_lib.zero_layout_chunk_state(self.handle, chunk, ctypes.byref(h)),
+               "zero_layout_chunk_state")
+        return Layout(h.value, self.units)
+
+    def _state_format(self):
+        if self._state is None:
+            e, n = _I64(), _I64()
+            _check(_lib.zero_layout_state(self.handle, ctypes.byref(e), ctypes.byref(n)),
+                   "zero_layout_state")
+            self._state = (e.value, n.value)
+        return self._state
+
+    @property
+    def state_chunk(self) -> int:
+        """0 for three state arrays, else the chunk E of the one state buffer."""
+        return self._state_format()[0]
+
+    @property
+    def state_len(self) -> int:
+        """Floats of the state: shard_len per array, or the chunked buffer's length."""
+        return self._state_format()[1]
+
+    def state_views(self, state):
+        """(master, m, v) for a chunked layout: views of one state tensor of
+        state_len floats starting at 0, E and 2E, as the library expects."""
+        E = self.state_chunk
+        if E == 0:
+            raise ValueError("this layout keeps master, m and v as three arrays")
+        if state.numel() != self.state_len:
+            raise ValueError(f"state: expected {self.state_len} floats, got {state.numel()}")
+        return state[0:], state[E:], state[2 * E:]
+
+    def state_count(self, unit_begin: int, unit_end: int):
+        """Floats each of master, m and v must hold from its pointer for a
+        call over [unit_begin, unit_end), or None for a range the library
+        will refuse."""
+        shard, _ = self.range_lens(unit_begin, unit_end)
+        E = self.state_chunk
+        if shard is None or E == 0 or shard == 0:
+            return shard
+        last = self._unit_table()[unit_end - 1]
+        i = last["shard_off"] + last["shard_len"] - 1     # highest shard index touched
+        return (i // E) * 3 * E + i % E + 1
 
     @property
     def flat_len(self) -> int:
@@ -389,9 +445,10 @@ def _check_step(layout, unit_begin, unit_end, master, m, v, param_out, param_ind
                 grad_fp32=None, grad_index=INDEX_SHARD, clip_coef=None, grads=None):
     lens = layout.range_lens(unit_begin, unit_end)
     shard, full = lens
-    _need(master, "master", shard, "fp32")
-    _need(m, "m", shard, "fp32")
-    _need(v, "v", shard, "fp32")
+    sc = layout.state_count(unit_begin, unit_end)
+    _need(master, "master", sc, "fp32")
+    _need(m, "m", sc, "fp32")
+    _need(v, "v", sc, "fp32")
     _need(param_out, "param_out", full if param_index == INDEX_FULL else shard, "bf16")
     if grad_fp32 is not None:
         _need(grad_fp32, "grad_fp32", full if grad_index == INDEX_FULL else shard, "fp32")
@@ -526,9 +583,9 @@ def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, gra
     or 1 under DDP; None allowed).  gather_stream defaults to step_stream
     (sequential)."""
     arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype)
-    shard, _ = layout.range_lens(unit_begin, unit_end)
+    sc = layout.state_count(unit_begin, unit_end)
     for name, x in (("master", master), ("m", m), ("v", v)):
-        _need(x, name, shard, "fp32")
+        _need(x, name, sc, "fp32")
     ss = _stream(step_stream)
     gs = ss if gather_stream is None else _stream(gather_stream)
     _check(_lib.zero_fsdp_sweep(layout.handle, unit_begin, unit_end, ctypes.byref(cfg), grad_dtype,
@@ -542,9 +599,9 @@ def fsdp_sweep_table(layout: Layout, unit_begin: int, unit_end: int, table, n_en
     """fsdp_sweep with the step scalars of table[*step_counter - 1] (device
     table and counter); advances the counter once, after the last unit."""
     arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype)
-    shard, _ = layout.range_lens(unit_begin, unit_end)
+    sc = layout.state_count(unit_begin, unit_end)
     for name, x in (("master", master), ("m", m), ("v", v)):
-        _need(x, name, shard, "fp32")
+        _need(x, name, sc, "fp32")
     _need(table, "table", n_entries * ctypes.sizeof(AdamTableEntry), "bytes")
     _need(step_counter, "step_counter", 1, "int64")
     ss = _stream(step_stream)
@@ -642,17 +699,21 @@ def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy,
            "zero_fsdp_linear_backward")
 
 
-def stream_mix(kind: int, grads, master, m, v, param, n: int, stream=None) -> None:
+def stream_mix(kind: int, grads, master, m, v, param, n: int, stream=None,
+               state_chunk: int = 0) -> None:
     """zero_stream_mix: the fused step's memory traffic without its
     arithmetic (kind MIX_STEP_STREAMS), its reads alone (MIX_READS) or its
-    writes alone (MIX_WRITES), over n elements."""
+    writes alone (MIX_WRITES), over n elements; state_chunk E > 0 takes
+    master, m, v in the chunked format (m = master + E, v = master + 2E)."""
     for q, x in enumerate(grads):
         _need(x, f"gradient buffer of rank {q}", n, "bf16")
+    E = state_chunk
+    sc = n if E <= 0 or n <= 0 else ((n - 1) // E) * 3 * E + (n - 1) % E + 1
     for name, x in (("master", master), ("m", m), ("v", v)):
-        _need(x, name, n, "fp32")
+        _need(x, name, sc, "fp32")
     _need(param, "param", n, "bf16")
     _check(_lib.zero_stream_mix(kind, _ptrs(grads), len(grads), _addr(master), _addr(m), _addr(v),
-                                _addr(param), n, _stream(stream)), "zero_stream_mix")
+                                _addr(param), n, state_chunk, _stream(stream)), "zero_stream_mix")
 
 
 def grad_accumulate(main_grad, micro_bf16, n: int, stream=None) -> None:

@@ -21,6 +21,10 @@ struct zero_layout {
     std::vector<int64_t> slice;      // s_u
     std::vector<int64_t> flat_off;   // F_u, F_{U} = flat length
     std::vector<int64_t> shard_off;  // R_u, R_{U} = shard length
+    // 0: master, m and v are three shard-indexed arrays.  Otherwise a power
+    // of two E: one buffer of chunks of E elements, each chunk holding E
+    // master, then E m, then E v values (zero_layout_chunk_state).
+    int64_t state_chunk = 0;
 };
 
 namespace zs {
@@ -32,5 +36,10 @@ void clear_error();
 
 // Validates a unit range of a layout.
 zero_status check_range(const zero_layout *L, int32_t unit_begin, int32_t unit_end);
+
+// Checks master, m and v against the layout's state format: under a chunked
+// state m and v must be master + E and master + 2E.
+zero_status check_state(const zero_layout *L, const float *master, const float *m,
+                        const float *v);
 
 }  // namespace zs

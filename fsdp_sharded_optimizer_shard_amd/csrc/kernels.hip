@@ -100,6 +100,9 @@ struct StepArgs {
     int32_t pow2;
     int32_t vec_ptrs;    // every base pointer is 16-byte aligned
     float *master, *m, *v;
+    int64_t st_base;     // chunked state: shard index of the range's first element
+    int32_t st_shift;    // 0: three state arrays; else log2 of the state chunk
+    int32_t _pad1;
     const float *gin;    // kApply: averaged gradient
     int32_t gin_full;    // kApply: 1 if gin is full-indexed, 0 if shard-indexed
     int32_t _pad2;
@@ -201,6 +204,20 @@ __device__ __forceinline__ void adam1(const AdamScalars &s, float g, float &p, f
 __device__ __forceinline__ float mean_of(const StepArgs &a, float sum)
 {
     return a.pow2 ? sum * a.inv_n : sum / a.n_f;
+}
+
+// Offset of shard element `si` (relative to the range) in master, m and v.
+// Three arrays: si itself.  Chunked state (chunk E = 2^st_shift): element
+// i = st_base + si sits at (i / E) 3E + i % E from master (m and v are
+// master + E and master + 2E).  A 4-aligned group of 4 never crosses a
+// chunk, so the vector path keeps one 16-byte access per lane and stream.
+__device__ __forceinline__ int64_t st_at(const StepArgs &a, int64_t si)
+{
+    if (a.st_shift == 0)
+        return si;
+    const int64_t i = a.st_base + si;
+    const int sh = a.st_shift;
+    return ((i >> sh) * 3 << sh) + (i & (((int64_t)1 << sh) - 1));
 }
 
 // Sum of the N rank gradients for G groups of 4 consecutive elements, group
@@ -336,11 +353,12 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
                                             const Seg &sg, const int64_t *j,
                                             float coef, double &sq)
 {
-    int64_t si[G], fi[G];
+    int64_t si[G], fi[G], xi[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
         si[h] = sg.shard_off + j[h];
         fi[h] = sg.full_off + j[h];
+        xi[h] = st_at(a, si[h]);
     }
     float p[G][4], m[G][4], v[G][4], g[G][4];
     if constexpr (MODE == kWriteOnly) {
@@ -348,9 +366,9 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float x = (float)j[h];
-            st_nt(reinterpret_cast<f32x4 *>(a.master + si[h]), f32x4{x, x, x, x});
-            st_nt(reinterpret_cast<f32x4 *>(a.m + si[h]), f32x4{x, x, x, x});
-            st_nt(reinterpret_cast<f32x4 *>(a.v + si[h]), f32x4{x, x, x, x});
+            st_nt(reinterpret_cast<f32x4 *>(a.master + xi[h]), f32x4{x, x, x, x});
+            st_nt(reinterpret_cast<f32x4 *>(a.m + xi[h]), f32x4{x, x, x, x});
+            st_nt(reinterpret_cast<f32x4 *>(a.v + xi[h]), f32x4{x, x, x, x});
             st_nt(reinterpret_cast<u32x2 *>(a.pout + (a.pout_full ? fi[h] : si[h])),
                   u32x2{(uint32_t)j[h], (uint32_t)j[h]});
         }
@@ -359,9 +377,9 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
     if (MODE != kReduce) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            const f32x4 pv = ld_nt(reinterpret_cast<const f32x4 *>(a.master + si[h]));
-            const f32x4 mv = ld_nt(reinterpret_cast<const f32x4 *>(a.m + si[h]));
-            const f32x4 vv = ld_nt(reinterpret_cast<const f32x4 *>(a.v + si[h]));
+            const f32x4 pv = ld_nt(reinterpret_cast<const f32x4 *>(a.master + xi[h]));
+            const f32x4 mv = ld_nt(reinterpret_cast<const f32x4 *>(a.m + xi[h]));
+            const f32x4 vv = ld_nt(reinterpret_cast<const f32x4 *>(a.v + xi[h]));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 p[h][e] = pv[e];
@@ -396,7 +414,7 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
             for (int e = 0; e < 4; ++e) {
                 const float x = ((g[h][e] + p[h][e]) + m[h][e]) + v[h][e];
                 if (x == a.sink_key)
-                    a.master[si[h] + e] = x;
+                    a.master[xi[h] + e] = x;
             }
         return;
     }
@@ -425,9 +443,9 @@ __device__ __forceinline__ void step_groups(const StepArgs &a, const AdamScalars
         }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        st_nt(reinterpret_cast<f32x4 *>(a.master + si[h]), f32x4{p[h][0], p[h][1], p[h][2], p[h][3]});
-        st_nt(reinterpret_cast<f32x4 *>(a.m + si[h]), f32x4{m[h][0], m[h][1], m[h][2], m[h][3]});
-        st_nt(reinterpret_cast<f32x4 *>(a.v + si[h]), f32x4{v[h][0], v[h][1], v[h][2], v[h][3]});
+        st_nt(reinterpret_cast<f32x4 *>(a.master + xi[h]), f32x4{p[h][0], p[h][1], p[h][2], p[h][3]});
+        st_nt(reinterpret_cast<f32x4 *>(a.m + xi[h]), f32x4{m[h][0], m[h][1], m[h][2], m[h][3]});
+        st_nt(reinterpret_cast<f32x4 *>(a.v + xi[h]), f32x4{v[h][0], v[h][1], v[h][2], v[h][3]});
         u32x2 w;
         if constexpr (MODE == kMix) {
             // the upper halves: a bf16 stream without the rounding
@@ -463,11 +481,12 @@ __device__ __forceinline__ void step_scalar(const StepArgs &a, const AdamScalars
             a.gout[(a.gout_full ? fi : si) + e] = g;
             sq = sq + (double)g * (double)g;
         } else {
-            float p = a.master[si + e], m = a.m[si + e], v = a.v[si + e];
+            const int64_t x = st_at(a, si + e);
+            float p = a.master[x], m = a.m[x], v = a.v[x];
             adam1(sc, g, p, m, v);
-            a.master[si + e] = p;
-            a.m[si + e] = m;
-            a.v[si + e] = v;
+            a.master[x] = p;
+            a.m[x] = m;
+            a.v[x] = v;
             a.pout[oi + e] = (uint16_t)to_bf16(p);
         }
     }
@@ -760,9 +779,11 @@ zero_status for_each_chunk(int32_t ub, int32_t ue, F fn)
 }
 
 // Fills the segment table for units [u0, u1) of a call whose range starts
-// at `ub`; returns the number of tiles.
+// at `ub`; returns the number of tiles.  `state_abs`: the launch addresses a
+// chunked state by absolute shard index, so a slice takes the vector path
+// only if its absolute shard offset is a multiple of 4 as well.
 int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg *seg,
-                  int32_t *n_segs)
+                  int32_t *n_segs, bool state_abs = false)
 {
     int64_t tiles = 0;
     int32_t k = 0;
@@ -775,7 +796,8 @@ int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg 
         s.shard_off = L->shard_off[u] - L->shard_off[ub];
         s.full_off = L->flat_off[u] - L->flat_off[ub] + (int64_t)L->rank * len;
         s.tile0 = tiles;
-        s.vec = (s.shard_off % 4 == 0 && s.full_off % 4 == 0) ? 1 : 0;
+        s.vec = (s.shard_off % 4 == 0 && s.full_off % 4 == 0 &&
+                 (!state_abs || L->shard_off[u] % 4 == 0)) ? 1 : 0;
         tiles += step_tiles_of(len);
     }
     *n_segs = k;
@@ -958,6 +980,9 @@ zero_status adam_launch(const zero_layout *L, int32_t ub, int32_t ue, const Adam
         return fail(ZERO_ERR_ALIGNMENT, "misaligned state / parameter buffer");
     if (grads && (st = check_grads(L, grads)) != ZERO_OK)
         return st;
+    if ((st = check_state(L, master, m, v)) != ZERO_OK)
+        return st;
+    const int64_t E = L->state_chunk;
     return for_each_chunk(ub, ue, [&](int32_t u0, int32_t u1) -> zero_status {
         StepArgs a;
         std::memset(&a, 0, sizeof a);
@@ -967,12 +992,16 @@ zero_status adam_launch(const zero_layout *L, int32_t ub, int32_t ue, const Adam
         else
             al = al && aligned16(grad_fp32);
         a.vec_ptrs = al;
-        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs);
+        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs, E > 0);
         if (a.n_tiles == 0)
             return ZERO_OK;
         a.master = master;
         a.m = m;
         a.v = v;
+        if (E > 0) {
+            a.st_base = L->shard_off[ub];
+            a.st_shift = __builtin_ctzll((unsigned long long)E);
+        }
         a.gin = grad_fp32;
         a.gin_full = grad_index == ZERO_INDEX_FULL;
         a.clip = clip_coef;
@@ -1154,6 +1183,8 @@ zero_status zero_adam_step_clip_noalloc(const zero_layout *L, int32_t ub, int32_
         reinterpret_cast<uintptr_t>(m) % 4 || reinterpret_cast<uintptr_t>(v) % 4 ||
         reinterpret_cast<uintptr_t>(param_out) % 2 || reinterpret_cast<uintptr_t>(norm_out) % 8)
         return fail(ZERO_ERR_ALIGNMENT, "misaligned gradient, state, parameter or norm buffer");
+    if ((st = check_state(L, master, m, v)) != ZERO_OK)
+        return st;
     const int64_t n = zero_reduce_partials_count(L, ub, ue);
     if (n > kNoAllocPartials)
         return fail(ZERO_ERR_UNSUPPORTED,
@@ -1310,7 +1341,7 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
 
 zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t n_ranks,
                             float *master, float *m, float *v, uint16_t *param, int64_t n,
-                            void *stream)
+                            int64_t state_chunk, void *stream)
 {
     if (kind != ZERO_MIX_STEP_STREAMS && kind != ZERO_MIX_READS && kind != ZERO_MIX_WRITES)
         return fail(ZERO_ERR_INVALID_ARG, "unknown stream-mix kind %d", kind);
@@ -1322,6 +1353,13 @@ zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t 
                     (long long)n);
     if (!grads || !master || !m || !v || !param)
         return fail(ZERO_ERR_INVALID_ARG, "grads, master, m, v and param are required");
+    const int64_t E = state_chunk;
+    if (E != 0 && (E < ZERO_STATE_CHUNK_MIN || E > ZERO_STATE_CHUNK_MAX || (E & (E - 1)) != 0))
+        return fail(ZERO_ERR_INVALID_ARG, "state_chunk must be 0 or a power of two in [%d, %d] "
+                    "(got %lld)", ZERO_STATE_CHUNK_MIN, ZERO_STATE_CHUNK_MAX, (long long)E);
+    if (E > 0 && (m != master + E || v != master + 2 * E))
+        return fail(ZERO_ERR_INVALID_ARG, "chunked state: m and v must be master + state_chunk "
+                    "and master + 2 state_chunk");
     bool al = aligned16(master) && aligned16(m) && aligned16(v) && aligned16(param);
     for (int q = 0; q < n_ranks; ++q) {
         if (!grads[q])
@@ -1345,6 +1383,8 @@ zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t 
     a.master = master;
     a.m = m;
     a.v = v;
+    if (E > 0)
+        a.st_shift = __builtin_ctzll((unsigned long long)E);
     a.pout = param;
     a.sink_key = __builtin_nanf("");
     const hipStream_t s = static_cast<hipStream_t>(stream);

@@ -42,6 +42,17 @@ zero_status check_range(const zero_layout *L, int32_t unit_begin, int32_t unit_e
     return ZERO_OK;
 }
 
+zero_status check_state(const zero_layout *L, const float *master, const float *m,
+                        const float *v)
+{
+    const int64_t E = L->state_chunk;
+    if (E > 0 && master && (m != master + E || v != master + 2 * E))
+        return fail(ZERO_ERR_INVALID_ARG, "chunked state (chunk %lld): m and v must be master + "
+                    "chunk and master + 2 chunk, master the start of the state buffer",
+                    (long long)E);
+    return ZERO_OK;
+}
+
 }  // namespace zs
 
 extern "C" {
@@ -132,6 +143,52 @@ zero_status zero_shard_init_rows(zero_layout **out, zero_strategy strategy, int3
 }
 
 void zero_shard_destroy(zero_layout *layout) { delete layout; }
+
+zero_status zero_layout_chunk_state(const zero_layout *L, int64_t chunk, zero_layout **out)
+{
+    using zs::fail;
+    if (!out)
+        return fail(ZERO_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!L)
+        return fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    if (chunk != 0 && (chunk < ZERO_STATE_CHUNK_MIN || chunk > ZERO_STATE_CHUNK_MAX ||
+                       (chunk & (chunk - 1)) != 0))
+        return fail(ZERO_ERR_INVALID_ARG, "state chunk must be 0 or a power of two in [%d, %d] "
+                    "(got %lld)", ZERO_STATE_CHUNK_MIN, ZERO_STATE_CHUNK_MAX, (long long)chunk);
+    zero_layout *C = nullptr;
+    try {
+        C = new zero_layout(*L);
+    } catch (const std::bad_alloc &) {
+        delete C;
+        return fail(ZERO_ERR_OOM, "host allocation of the layout copy failed");
+    }
+    C->state_chunk = chunk;
+    *out = C;
+    zs::clear_error();
+    return ZERO_OK;
+}
+
+zero_status zero_layout_state(const zero_layout *L, int64_t *chunk, int64_t *state_len)
+{
+    if (!L)
+        return zs::fail(ZERO_ERR_INVALID_ARG, "layout is NULL");
+    const int64_t E = L->state_chunk, S = L->shard_off[L->n_units];
+    if (chunk)
+        *chunk = E;
+    if (state_len) {
+        if (E == 0) {
+            *state_len = S;
+        } else {
+            const int64_t n_chunks = (S + E - 1) / E;
+            if (n_chunks > INT64_MAX / 4 / (3 * E))
+                return zs::fail(ZERO_ERR_INVALID_ARG, "state length overflows");
+            *state_len = n_chunks * 3 * E;
+        }
+    }
+    zs::clear_error();
+    return ZERO_OK;
+}
 
 zero_status zero_layout_info(const zero_layout *L, int64_t *flat_len, int64_t *shard_len,
                              int32_t *n_units, int32_t *world_n, int32_t *rank,

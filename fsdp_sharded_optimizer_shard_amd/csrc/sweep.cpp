@@ -71,6 +71,8 @@ zero_status sweep(const zero_layout *L, int32_t ub, int32_t ue, int32_t grad_dty
     if (reinterpret_cast<uintptr_t>(master) % 4 || reinterpret_cast<uintptr_t>(m) % 4 ||
         reinterpret_cast<uintptr_t>(v) % 4)
         return zs::fail(ZERO_ERR_ALIGNMENT, "misaligned state buffer");
+    if ((st = zs::check_state(L, master, m, v)) != ZERO_OK)
+        return st;
     if (L->world_n > ZERO_MAX_RANKS_PER_CALL)
         return zs::fail(ZERO_ERR_UNSUPPORTED, "at most %d rank buffers per call (got %d)",
                         ZERO_MAX_RANKS_PER_CALL, L->world_n);
@@ -114,7 +116,9 @@ zero_status sweep(const zero_layout *L, int32_t ub, int32_t ue, int32_t grad_dty
                             "hipStreamWaitEvent")) != ZERO_OK)
             return st;
         const zero_grads g{x.rank_grads, nullptr, n, grad_dtype, ZERO_INDEX_SHARD, 0};
-        const int64_t so = L->shard_off[u] - L->shard_off[ub];
+        // three state arrays: the unit's step gets them from the unit's
+        // first element; a chunked state is always passed from its start
+        const int64_t so = L->state_chunk ? 0 : L->shard_off[u] - L->shard_off[ub];
         if ((st = step_unit(u, g, so, x.unit_full)) != ZERO_OK)
             return st;
         if (two) {

@@ -7,6 +7,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -50,9 +52,35 @@ def test_cpu_baseline_all_cores_matches_single_thread():
     S = 70_001
     grads = [grad_bits(w, 0, q, S) for q in range(8)]
     master = master_init(w, S)
-    out = bench.cpu_baseline(w, grads, master, S, 7, budget_s=5.0)
+    out = bench.cpu_baseline(w, grads, lambda a, n: master[a:a + n], S, 7, budget_s=5.0)
     assert out["kind"] == "oracle" and out["cores"] == 1 and out["value"] > 0
     allc = out["all_cores"]
     assert allc["cores"] == len(os.sched_getaffinity(0)) and allc["value"] > 0
     assert f"first {S} of {S}" in out["sample"]
     assert isinstance(out["cpu_model"], str) and out["cpu_model"]
+
+
+@pytest.mark.parametrize("E", [0, 4, 1024, 8192])
+def test_bench_state_holds_the_master_in_the_layouts_format(E):
+    # the benchmark's state holder puts the initial master where the layout
+    # says (three arrays, or the master part of each chunk) and reads any
+    # range of it back
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    from fsdp_sharded_optimizer_shard_amd import zs
+    L = zs.shard_init("zero3", 8, 7, [80_000, 333]).chunk_state(E)
+    S = L.shard_len
+    master0 = torch.from_numpy(np.random.default_rng(E).standard_normal(S).astype(np.float32))
+    st = bench.State(torch, L, master0)
+    assert S == 10_042
+    for off, n in ((0, S), (0, 1), (S - 1, 1), (3, 4097), (E + 3 if E < S else 9, 17),
+                   (S - 5000, 5000)):
+        n = min(n, S - off)
+        assert torch.equal(st.master(off, n), master0[off:off + n]), (off, n)
+    if E:
+        b = st.buf.view(-1, 3, E)
+        assert not b[:, 1:, :].any(), "m and v start at zero"
+        assert st.views[1].data_ptr() == st.buf.data_ptr() + 4 * E
+        assert st.views[2].data_ptr() == st.buf.data_ptr() + 8 * E

@@ -576,3 +576,110 @@ def test_binding_checks_tensor_sizes_dtypes_and_contiguity():
     with pytest.raises(ValueError, match="B holds"):
         zs.gemm_bf16(16, 16, 32, Dev(512, torch.int16), 32, zs.K_INNER, Dev(511, torch.int16),
                      16, zs.K_OUTER, Dev(256), 16, stream=0)
+
+
+# ------------------------------------------------------- chunked state --
+
+def test_chunked_state_layout_and_length():
+    L = zs.shard_init("zero3", 8, 7, [1000, 24, 5000])
+    S = L.shard_len
+    assert (L.state_chunk, L.state_len) == (0, S)
+    for E in (4, 8, 1024, 8192, zs.STATE_CHUNK_MAX):
+        C = L.chunk_state(E)
+        assert C.state_chunk == E and C.state_len == -(-S // E) * 3 * E
+        # everything else is the source layout's
+        assert C.info() == L.info()
+        assert [C.query(u) for u in range(3)] == [L.query(u) for u in range(3)]
+        assert C.chunk_state(0).state_len == S
+    assert L.state_chunk == 0          # the source is not changed
+
+
+@pytest.mark.parametrize("E", [-4, 1, 2, 3, 6, 12, 1000, 2 * zs.STATE_CHUNK_MAX])
+def test_chunked_state_rejects_bad_chunks(E):
+    L = zs.shard_init("zero2", 4, 0, [4096])
+    assert _err(L.chunk_state, E).status == zs.ERR_INVALID_ARG
+
+
+def test_chunked_state_needs_m_and_v_beside_master():
+    # a chunked state is one buffer: m = master + E and v = master + 2E,
+    # master its start, for every range; anything else is refused on the host
+    E = 1024
+    L = _layout().chunk_state(E)
+    g = zs.Grads([FAKE] * 4, zs.BF16, zs.INDEX_FULL)
+    cfg = zs.adam_cfg(step=1)
+
+    def step(m, v, ub=0, ue=2):
+        zs.adam_step(L, ub, ue, cfg, FAKE, m, v, FAKE, grads=g, stream=0)
+
+    for m, v in ((FAKE, FAKE), (FAKE + 4 * E, FAKE + 4 * E), (FAKE + 8 * E, FAKE + 4 * E),
+                 (FAKE + 4 * E, FAKE + 4 * E + 4 * E + 16)):
+        e = _err(step, m, v)
+        assert e.status == zs.ERR_INVALID_ARG and "chunked state" in str(e)
+    assert _err(step, FAKE, FAKE, 1, 2).status == zs.ERR_INVALID_ARG
+    sweep_unit = ([FAKE] * 4, [FAKE, None, FAKE, FAKE], FAKE)
+    e = _err(zs.fsdp_sweep, L, 0, 2, cfg, zs.BF16, [sweep_unit] * 2, FAKE, FAKE + 16, FAKE, 2,
+             0, 0)
+    assert e.status == zs.ERR_INVALID_ARG and "chunked state" in str(e)
+    f = lambda *a: zs.adam_step_clip_noalloc(*a, stream=0)
+    e = _err(f, L, 0, 2, cfg, 1.0, g, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert e.status == zs.ERR_INVALID_ARG and "chunked state" in str(e)
+    # the same pointers pass the state check on the three-array layout: the
+    # call fails later, at the launch on the fake addresses' null stream
+    # (not run here: it would reach HIP)
+
+
+def test_chunked_state_counts_in_the_binding():
+    import torch
+
+    class Dev:
+        def __init__(self, n, off=0):
+            self._n, self._off = n, off
+            self.dtype, self.is_cuda, self.device = torch.float32, True, "cuda:0"
+
+        def numel(self):
+            return self._n
+
+        def element_size(self):
+            return 4
+
+        def is_contiguous(self):
+            return True
+
+        def data_ptr(self):
+            return FAKE + 4 * self._off
+
+    E = 8
+    L = zs.shard_init("zero3", 4, 1, [1000, 24]).chunk_state(E)   # shard 250 + 6
+    n = L.state_len
+    assert L.shard_len == 256 and n == 32 * 24
+    # the last shard index touched, 255, sits at (255 // 8) 24 + 7 = 751 from
+    # each pointer, whatever the range
+    assert L.state_count(0, 2) == 752 and L.state_count(1, 2) == 752
+    assert L.state_count(0, 1) == (249 // 8) * 24 + 249 % 8 + 1
+    assert L.state_count(1, 1) == 0 and L.state_count(0, 3) is None
+    master, m, v = Dev(n), Dev(n - E, E), Dev(n - 2 * E, 2 * E)
+    assert n - 2 * E >= 752          # the views of one whole buffer are large enough
+
+    def step(**kw):
+        a = dict(master=master, m=m, v=v)
+        a.update(kw)
+        zs.adam_step(L, 0, 2, zs.adam_cfg(step=1), a["master"], a["m"], a["v"],
+                     Dev(1024), grad_fp32=Dev(256), stream=0)
+
+    with pytest.raises(ValueError, match="v holds 751 elements, the call touches 752"):
+        step(v=Dev(751, 2 * E))
+    with pytest.raises(ValueError, match="master holds"):
+        step(master=Dev(700))
+
+
+def test_stream_mix_chunked_state_validation():
+    g8 = [FAKE] * 8
+    E = 1024
+    ok = (FAKE, FAKE + 4 * E, FAKE + 8 * E, FAKE)
+    for bad in (3, 2, 6, 2 * zs.STATE_CHUNK_MAX):
+        assert _err(zs.stream_mix, zs.MIX_READS, g8, *ok, 64, 0,
+                    state_chunk=bad).status == zs.ERR_INVALID_ARG
+    e = _err(zs.stream_mix, zs.MIX_READS, g8, FAKE, FAKE + 4 * E, FAKE + 4 * E, FAKE, 64, 0,
+             state_chunk=E)
+    assert e.status == zs.ERR_INVALID_ARG and "chunked state" in str(e)
+    zs.stream_mix(zs.MIX_READS, g8, *ok, 0, 0, state_chunk=E)   # n = 0: nothing to launch

@@ -9,6 +9,9 @@ partial one), so a rate measured with them is a rate of those streams.
   MIX_WRITES        master = m = v = the group index j (the first element of
                     the element's 4-element group), param = the low and high
                     halves of j, alternately.
+With a state chunk E the same holds at the chunked positions (element i of
+master at (i / E) 3E + i % E, m and v E and 2E further), and the rest of the
+buffer is left alone.
 """
 import numpy as np
 import pytest
@@ -63,3 +66,30 @@ def test_reads_change_nothing_and_writes_fill_the_index():
         assert np.array_equal(after.cpu().numpy(), j.astype(np.float32))
     half = np.where(np.arange(n) % 2 == 0, j & 0xffff, (j >> 16) & 0xffff).astype(np.uint16)
     assert np.array_equal(param.cpu().numpy().view(np.uint16), half)
+
+
+def test_step_streams_on_a_chunked_state():
+    n, E, n_ranks = 3 * 2048 + 4 * 37, 1024, 8
+    rng = np.random.default_rng(9)
+    dev = torch.device("cuda:0")
+    g = [rng.integers(0, 1 << 16, n, dtype=np.uint16) & 0xbfff for _ in range(n_ranks)]
+    rows = -(-n // E)
+    buf = rng.standard_normal(rows * 3 * E).astype(np.float32)
+    dbuf = torch.from_numpy(buf.copy()).to(dev)
+    dg = [torch.from_numpy(x.view(np.int16)).to(dev) for x in g]
+    param = torch.zeros(n, dtype=torch.int16, device=dev)
+    views = (dbuf[0:], dbuf[E:], dbuf[2 * E:])
+    zs.stream_mix(zs.MIX_STEP_STREAMS, dg, *views, param, n, state_chunk=E)
+    torch.cuda.synchronize()
+    acc = np.zeros(n, np.float32)
+    for x in g:
+        acc = acc + (x.astype(np.uint32) << 16).view(np.float32)
+    i = np.arange(n)
+    pos = (i // E) * 3 * E + i % E
+    want = buf.copy()
+    for k in range(3):
+        want[pos + k * E] = buf[pos + k * E] + acc
+    got = dbuf.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(param.cpu().numpy().view(np.uint16),
+                          (got[pos].view(np.uint32) >> 16).astype(np.uint16))

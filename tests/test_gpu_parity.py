@@ -60,6 +60,25 @@ def owned_index(lay):
     return np.concatenate([np.arange(b, b + k, dtype=np.int64) for b, _, k in lay.owned_runs()])
 
 
+def chunk_state(master, m, v, E):
+    """One chunked state buffer (chunks of E master, E m, E v values) holding
+    three shard-length arrays; the tail of the last chunk stays zero."""
+    S = master.size
+    n = -(-S // E)
+    buf = np.zeros((n, 3, E), np.float32)
+    for k, x in enumerate((master, m, v)):
+        col = np.zeros(n * E, np.float32)
+        col[:S] = x
+        buf[:, k, :] = col.reshape(n, E)
+    return buf.reshape(-1)
+
+
+def unchunk_state(buf, E, S):
+    """(master, m, v) of shard length S out of a chunked state buffer."""
+    b = np.asarray(buf).reshape(-1, 3, E)
+    return tuple(np.ascontiguousarray(b[:, k, :].reshape(-1)[:S]) for k in range(3))
+
+
 def assert_f32_close(got, want, what):
     """Bit-exact, and within the stated tolerance (reported together)."""
     diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
@@ -100,22 +119,39 @@ class GpuRanks:
     buffer (the all-gather is implicit) or, for ZeRO-3, into its own shard
     buffer followed by zero_gather_params."""
 
-    def __init__(self, w, master0, oracle_cluster):
+    def __init__(self, w, master0, oracle_cluster, state_chunk=0):
         self.w = w
         self.n = w.n_ranks
         self.oc = oracle_cluster
+        self.E = state_chunk
         self.lays = [zs.shard_init(w.strategy, self.n, r, list(w.units)) for r in range(self.n)]
+        if state_chunk:
+            self.lays = [L.chunk_state(state_chunk) for L in self.lays]
         self.U = len(w.units)
         lay0 = oracle_cluster.layouts[0]
         mfull = strategies.pad(lay0, master0)
         self.P = lay0.flat_len
         self.full = dev_bf16(_c.f32_to_bf16(mfull))
         self.state = []
+        self.bufs = []
         for r in range(self.n):
             idx = owned_index(oracle_cluster.layouts[r])
-            S = self.lays[r].shard_len
-            self.state.append([dev_f32(mfull[idx]), torch.zeros(S, device=DEV),
-                               torch.zeros(S, device=DEV)])
+            L = self.lays[r]
+            S = L.shard_len
+            if state_chunk:
+                z = np.zeros(S, np.float32)
+                buf = dev_f32(chunk_state(mfull[idx], z, z, state_chunk))
+                self.bufs.append(buf)
+                self.state.append(list(L.state_views(buf)))
+            else:
+                self.state.append([dev_f32(mfull[idx]), torch.zeros(S, device=DEV),
+                                   torch.zeros(S, device=DEV)])
+
+    def host_state(self, r):
+        """(master, m, v) of rank r as shard-length host arrays."""
+        if self.E:
+            return unchunk_state(host_f32(self.bufs[r]), self.E, self.lays[r].shard_len)
+        return tuple(host_f32(x) for x in self.state[r])
 
     def rank_grads(self, grads_t, r, index_modes, dtype):
         lay0 = self.oc.layouts[0]
@@ -145,7 +181,9 @@ class GpuRanks:
                 ptrs = [b[so:] if index_modes[k] == zs.INDEX_SHARD else b[fo:]
                         for k, b in enumerate(bufs)]
                 G = zs.Grads(ptrs, dtype, list(index_modes))
-                st = [x[so:] for x in self.state[r]]
+                # three arrays move with the unit; a chunked state is always
+                # passed from its start
+                st = self.state[r] if self.E else [x[so:] for x in self.state[r]]
                 zs.adam_step(L, u, u + 1, c, *st, self.full[fo:], zs.INDEX_FULL, grads=G)
 
     def step_two_pass(self, t, grads_t, max_norm):
@@ -177,8 +215,9 @@ class GpuRanks:
         st = strategies.full_state(self.oc, padded=True)
         for r in range(self.n):
             idx = owned_index(self.oc.layouts[r])
+            got = self.host_state(r)
             for k, name in enumerate(("master", "m", "v")):
-                assert_f32_close(host_f32(self.state[r][k]), st[name][idx], f"{what}: rank {r} {name}")
+                assert_f32_close(got[k], st[name][idx], f"{what}: rank {r} {name}")
 
 
 # ------------------------------------------------------------ cases --
@@ -250,6 +289,82 @@ def test_per_unit_calls_equal_whole_range():
         strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
         g.step_fused(t + 1, grads[t], _modes("mixed", n), per_unit=True)
         g.check(f"per-unit step {t + 1}")
+
+
+CHUNK_CASES = [
+    # units, N, strategy, decay, index modes, state chunk
+    ([5000, 333, 20000], 4, "zero2", "adamw", "full", 8192),
+    ([4097, 1, 0, 7], 3, "zero2", "l2", "shard", 4),
+    ([2048 * 3 + 5], 5, "zero3", "none", "mixed", 1024),
+    ([640, 6400, 64000], 8, "fsdp", "adamw", "shard", 8),
+    ([129 * 64, 64, 1], 64, "fsdp", "none", "shard", 16384),
+]
+
+
+@pytest.mark.parametrize("units,n,strategy,decay,modes,E", CHUNK_CASES)
+def test_fused_step_chunked_state(units, n, strategy, decay, modes, E):
+    """The fused step with master, m and v in one chunked buffer: results
+    equal the oracle's bit for bit.  Chunks of 4 and 8 put every 4-element
+    group at a chunk edge; units with shard offsets that are not multiples
+    of 4 run the scalar path across chunk edges."""
+    w = _w(units, n, strategy, decay)
+    master0, grads = draw(w, w.steps)
+    oc = strategies.make_cluster(strategy, units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=E)
+    for t in range(w.steps):
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        g.step_fused(t + 1, grads[t], _modes(modes, n))
+        g.check(f"{units} N={n} E={E} step {t + 1}")
+
+
+@pytest.mark.parametrize("E", [4, 64, 4096])
+def test_per_unit_calls_on_chunked_state(E):
+    """One call per unit on a chunked state (each passed from the buffer's
+    start) equals the oracle, with unit shard offsets 1024, 25, 2048+..."""
+    units, n = [4096, 100, 8192 + 3, 8], 4
+    w = _w(units, n, "fsdp", "adamw")
+    master0, grads = draw(w, 2)
+    oc = strategies.make_cluster("fsdp", units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=E)
+    for t in range(2):
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        g.step_fused(t + 1, grads[t], _modes("mixed", n), per_unit=True)
+        g.check(f"per-unit chunked E={E} step {t + 1}")
+
+
+def test_two_pass_clip_on_chunked_state():
+    """reduce -> clip coefficient -> Adam from fp32 on a chunked state."""
+    units, n, max_norm = [25000, 25000, 24439], 8, 1e-4
+    w = small_workload(units, n, "zero2", steps=2, cfg=11, weight_decay=0.01, decoupled=True,
+                       max_grad_norm=max_norm, outlier_frac=0.01)
+    master0, grads = draw(w, w.steps)
+    oc = strategies.make_cluster("zero2", units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=2048)
+    for t in range(w.steps):
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        g.step_two_pass(t + 1, grads[t], max_norm)
+        g.check(f"chunked clip step {t + 1}")
+
+
+def test_table_step_on_chunked_state():
+    """zero_adam_step_table (scalars read on the device from a step table)
+    on a chunked state, three steps with the counter advanced on the device."""
+    units, n, E = [5000, 777, 64], 4, 64
+    w = _w(units, n, "zero3", "adamw")
+    master0, grads = draw(w, w.steps)
+    oc = strategies.make_cluster("zero3", units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=E)
+    table = zs.adam_table_device([cfg_of(w, t + 1) for t in range(w.steps)], DEV)
+    counter = torch.ones(1, dtype=torch.int64, device=DEV)
+    modes = _modes("mixed", n)
+    for t in range(w.steps):
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        for r, L in enumerate(g.lays):
+            G = zs.Grads(g.rank_grads(grads[t], r, modes, zs.BF16), zs.BF16, modes)
+            zs.adam_step_table(L, 0, g.U, table, w.steps, counter, *g.state[r], g.full,
+                               zs.INDEX_FULL, grads=G)
+        zs.step_advance(counter)
+        g.check(f"table on chunked state, step {t + 1}")
 
 
 def test_fp32_gradients_megatron():
@@ -415,16 +530,27 @@ def test_config2_full_shard_every_element():
     3 fused Adam steps), compared element by element over the whole shard:
     the oracle steps every element from the same gradients, streamed from
     the GPU in 32M-element chunks, and master, m, v and the bf16 shard must
-    be bit-identical everywhere."""
+    be bit-identical everywhere -- for three state arrays and for the
+    chunked state the benchmark times, side by side."""
     w = WORKLOADS[2]
     n, r = w.n_ranks, w.n_ranks - 1
     L = zs.shard_init("zero3", n, r, list(w.units))
     S = L.shard_len
     CH = 1 << 25
+    E = zs.STATE_CHUNK_DEFAULT
+    assert CH % E == 0
+    LC = L.chunk_state(E)
     master = master_init(w, S, device=DEV, rank=r)
     m = torch.zeros(S, device=DEV)
     v = torch.zeros(S, device=DEV)
     own = torch.empty(S, dtype=torch.int16, device=DEV)
+    rows = -(-S // E)
+    st_c = torch.zeros(LC.state_len, device=DEV)
+    col = torch.zeros(rows * E, device=DEV)
+    col[:S] = master
+    st_c.view(rows, 3, E)[:, 0, :].copy_(col.view(rows, E))
+    del col
+    own_c = torch.empty(S, dtype=torch.int16, device=DEV)
     p_h = master.cpu().numpy()
     m_h = np.zeros(S, np.float32)
     v_h = np.zeros(S, np.float32)
@@ -432,15 +558,17 @@ def test_config2_full_shard_every_element():
     tmp = np.empty(CH, np.float32)
     for t in range(w.steps):
         grads = [grad_bits(w, t, q, S, device=DEV) for q in range(n)]
-        zs.adam_step(L, 0, 1, cfg_of(w, t + 1), master, m, v, own, zs.INDEX_SHARD,
-                     grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
+        G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+        zs.adam_step(L, 0, 1, cfg_of(w, t + 1), master, m, v, own, zs.INDEX_SHARD, grads=G)
+        zs.adam_step(LC, 0, 1, cfg_of(w, t + 1), *LC.state_views(st_c), own_c, zs.INDEX_SHARD,
+                     grads=G)
         hp = oracle_cfg(w).hparams(t + 1)
         for off in range(0, S, CH):
             k = min(CH, S - off)
             g = [host_bf16(gq[off:off + k]) for gq in grads]
             _c.rank_step(hp, g, 1.0, p_h[off:off + k], m_h[off:off + k], v_h[off:off + k],
                          par_h[off:off + k], tmp[:k])
-        del grads
+        del grads, G
     torch.cuda.synchronize()
     bad = {}
     for name, dev_t, want in (("master", master, p_h), ("m", m, m_h), ("v", v, v_h)):
@@ -450,8 +578,17 @@ def test_config2_full_shard_every_element():
             nbad += int(np.count_nonzero(got.view(np.uint32) !=
                                          want[off:off + CH].view(np.uint32)))
         bad[name] = nbad
-    nbad = 0
+    nbad = {"master": 0, "m": 0, "v": 0}
     for off in range(0, S, CH):
-        nbad += int(np.count_nonzero(host_bf16(own[off:off + CH]) != par_h[off:off + CH]))
-    bad["bf16 shard"] = nbad
+        k = min(CH, S - off)
+        got = unchunk_state(host_f32(st_c[off // E * 3 * E:(off + k + E - 1) // E * 3 * E]), E, k)
+        for name, x, want in zip(("master", "m", "v"), got, (p_h, m_h, v_h)):
+            nbad[name] += int(np.count_nonzero(x.view(np.uint32) !=
+                                               want[off:off + k].view(np.uint32)))
+    bad.update({f"chunked {k}": x for k, x in nbad.items()})
+    for name, o in (("bf16 shard", own), ("chunked-state bf16 shard", own_c)):
+        nb = 0
+        for off in range(0, S, CH):
+            nb += int(np.count_nonzero(host_bf16(o[off:off + CH]) != par_h[off:off + CH]))
+        bad[name] = nb
     assert not any(bad.values()), f"elements differing from the oracle: {bad}"

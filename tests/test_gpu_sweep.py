@@ -32,8 +32,10 @@ def h32(t):
     return t.cpu().numpy()
 
 
-@pytest.mark.parametrize("cap,two", [(0, True), (1, True), (2, True), (3, True), (2, False)])
-def test_sweep_small_ragged_matches_oracle(cap, two):
+@pytest.mark.parametrize("cap,two,E", [(0, True, 0), (1, True, 0), (2, True, 0), (3, True, 0),
+                                       (2, False, 0), (2, True, 16), (0, True, 2048)])
+def test_sweep_small_ragged_matches_oracle(cap, two, E):
+    """E > 0: master, m and v in one chunked buffer of E-element chunks."""
     units, n, r = [4096, 100, 8192 + 3, 8, 0, 64 * 33, 5000, 2048 * 3], 8, 5
     w = small_workload(units, n, "fsdp", steps=2, cfg=10, weight_decay=0.01, decoupled=True)
     psi = sum(units)
@@ -44,9 +46,20 @@ def test_sweep_small_ragged_matches_oracle(cap, two):
     U = len(units)
     idx = np.concatenate([np.arange(b, b + k) for b, _, k in olay.owned_runs()])
     mfull = strategies.pad(olay, master0)
-    master = torch.from_numpy(mfull[idx].copy()).to(DEV)
-    m = torch.zeros(L.shard_len, device=DEV)
-    v = torch.zeros(L.shard_len, device=DEV)
+    S = L.shard_len
+    if E:
+        L = L.chunk_state(E)
+        rows = -(-S // E)
+        col = np.zeros(rows * E, np.float32)
+        col[:S] = mfull[idx]
+        buf_h = np.zeros((rows, 3, E), np.float32)
+        buf_h[:, 0, :] = col.reshape(rows, E)
+        buf = torch.from_numpy(buf_h.reshape(-1)).to(DEV)
+        master, m, v = L.state_views(buf)
+    else:
+        master = torch.from_numpy(mfull[idx].copy()).to(DEV)
+        m = torch.zeros(S, device=DEV)
+        v = torch.zeros(S, device=DEV)
     rng = np.random.default_rng(cap)
     q = [L.query(u) for u in range(U)]
     peers_h = [[rng.integers(0, 1 << 16, x["shard_len"], dtype=np.uint16) for _ in range(n)]
@@ -69,8 +82,13 @@ def test_sweep_small_ragged_matches_oracle(cap, two):
                       zs.BF16, ios, master, m, v, cap, gather_stream=gs)
         torch.cuda.synchronize()
     st = strategies.full_state(oc, padded=True)
-    for k, (name, dev_t) in enumerate((("master", master), ("m", m), ("v", v))):
-        assert np.array_equal(h32(dev_t).view(np.uint32), st[name][idx].view(np.uint32)), name
+    if E:
+        b = h32(buf).reshape(-1, 3, E)
+        got = [b[:, k, :].reshape(-1)[:S] for k in range(3)]
+    else:
+        got = [h32(master), h32(m), h32(v)]
+    for name, x in zip(("master", "m", "v"), got):
+        assert np.array_equal(x.view(np.uint32), st[name][idx].view(np.uint32)), name
     want_params = strategies.full_params(oc, padded=True)
     for u, x in enumerate(q):
         if x["padded_len"] == 0:

@@ -32,14 +32,30 @@ def _bits(t):
     return x.view({4: np.uint32, 8: np.uint64, 2: np.uint16}[x.itemsize])
 
 
-def _both_paths(strategy, units, n, r, cfg_id, max_norm, steps):
+def _state(L, master0, E):
+    """master, m, v: three arrays, or views of one chunked buffer (E > 0)
+    holding master0 and zeros."""
+    S = L.shard_len
+    if not E:
+        return [master0.clone(), torch.zeros(S, device=DEV), torch.zeros(S, device=DEV)]
+    rows = -(-S // E)
+    buf = torch.zeros(L.state_len, device=DEV)
+    col = torch.zeros(rows * E, device=DEV)
+    col[:S] = master0
+    buf.view(rows, 3, E)[:, 0, :].copy_(col.view(rows, E))
+    return list(L.state_views(buf)) + [buf]
+
+
+def _both_paths(strategy, units, n, r, cfg_id, max_norm, steps, state_chunk=0):
     from fsdp_sharded_optimizer_shard_amd import zs
     w, L, grads, master0 = _case(strategy, units, n, r, cfg_id)
+    if state_chunk:
+        L = L.chunk_state(state_chunk)
     U, P, S = len(units), L.flat_len, L.shard_len
     G = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
     out = {}
     for path in ("three_calls", "noalloc"):
-        st = [master0.clone(), torch.zeros(S, device=DEV), torch.zeros(S, device=DEV)]
+        st = _state(L, master0, state_chunk)
         full = torch.zeros(P, dtype=torch.int16, device=DEV)
         gout = torch.empty(S, device=DEV)
         norm = torch.empty(1, dtype=torch.float64, device=DEV)
@@ -51,15 +67,16 @@ def _both_paths(strategy, units, n, r, cfg_id, max_norm, steps):
                 coef = torch.empty(1, device=DEV)
                 zs.reduce_shard(L, 0, U, G, gout, partials, count)
                 zs.clip_coef(partials, count, max_norm, coef, norm)
-                zs.adam_step(L, 0, U, cfg, *st, full, zs.INDEX_FULL, grad_fp32=gout,
+                zs.adam_step(L, 0, U, cfg, *st[:3], full, zs.INDEX_FULL, grad_fp32=gout,
                              clip_coef=coef)
                 out["coef"] = float(coef.item())
             else:
-                zs.adam_step_clip_noalloc(L, 0, U, cfg, max_norm, G, gout, *st, full,
+                zs.adam_step_clip_noalloc(L, 0, U, cfg, max_norm, G, gout, *st[:3], full,
                                           zs.INDEX_FULL, norm_out=norm)
         torch.cuda.synchronize()
-        out[path] = {"master": _bits(st[0]), "m": _bits(st[1]), "v": _bits(st[2]),
-                     "params": _bits(full), "grad": _bits(gout), "norm": _bits(norm)}
+        state = {"state": _bits(st[3])} if state_chunk else {
+            "master": _bits(st[0]), "m": _bits(st[1]), "v": _bits(st[2])}
+        out[path] = dict(state, params=_bits(full), grad=_bits(gout), norm=_bits(norm))
     return out
 
 
@@ -74,3 +91,15 @@ def test_two_calls_in_a_row_match_the_three_call_path():
             got = res["noalloc"][k]
             nbad = int(np.count_nonzero(got != want))
             assert nbad == 0, f"{name}: {k}: {nbad} of {want.size} differ"
+
+
+def test_chunked_state_call_matches_the_three_call_path():
+    # the same entry point on a layout whose master, m and v form one
+    # chunked buffer, after the calls above have left the static buffer
+    # holding their partials
+    res = _both_paths("zero3", [20_000, 333, 4099], 8, 3, 23, 0.005, steps=2, state_chunk=1024)
+    assert res["coef"] < 1.0
+    for k, want in res["three_calls"].items():
+        got = res["noalloc"][k]
+        nbad = int(np.count_nonzero(got != want))
+        assert nbad == 0, f"chunked state: {k}: {nbad} of {want.size} differ"
