@@ -78,9 +78,9 @@ def parse():
                          "streams without the arithmetic, its reads, its writes) on this many "
                          "fresh placements")
     ap.add_argument("--state-chunk", type=int, default=None, metavar="E",
-                    help="headline and --calibrate-mix: master, m and v as one buffer of "
-                         "E-element chunks (zero_layout_chunk_state); 0 keeps three arrays; "
-                         "default: the library's ZERO_STATE_CHUNK_DEFAULT")
+                    help="master, m and v of every workload as one buffer of E-element "
+                         "chunks (zero_layout_chunk_state); 0 keeps three arrays; default: "
+                         "the library's ZERO_STATE_CHUNK_DEFAULT")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
@@ -374,13 +374,13 @@ def run_tiny(args, torch, zs, np):
     dev = torch.device("cuda:0")
     w = WORKLOADS[0]
     N = w.n_ranks
-    lays = [zs.shard_init("zero2", N, r, list(w.units)) for r in range(N)]
+    lays = [zs.shard_init("zero2", N, r, list(w.units)).chunk_state(state_chunk(args, zs))
+            for r in range(N)]
     S, P = lays[0].shard_len, lays[0].flat_len
     grads = [grad_bits(w, 0, q, P, device=dev) for q in range(N)]
     G = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
     full = torch.empty(P, dtype=torch.int16, device=dev)
-    st = [[master_init(w, S, device=dev, rank=r), torch.zeros(S, device=dev),
-           torch.zeros(S, device=dev)] for r in range(N)]
+    st = [State(torch, lays[r], master_init(w, S, device=dev, rank=r)).views for r in range(N)]
     t = [0]
 
     def step(ph):
@@ -397,7 +397,8 @@ def run_tiny(args, torch, zs, np):
     out = base_line(args, "tiny ZeRO-2 step params/sec (Psi=2^20, N=4, all ranks)",
                     P / (ms * 1e-3), "params/s", ms,
                     "tiny ZeRO-2 step: 4 ranks x fused reduce + Adam + bf16 into one buffer",
-                    psi=w.psi, n_ranks=N, shard_elems=S)
+                    psi=w.psi, n_ranks=N, shard_elems=S,
+                    state_layout=state_desc(lays[0].state_chunk))
     out["kernels"] = kern
     out["roofline"] = roofline("step_kernel<fused, N=4, bf16> (cache-resident; not a roofline "
                                "point)", b, kern["fused_reduce_adam_cast"]["ms_per_launch_mean"])
@@ -438,14 +439,14 @@ def run_gpt2_clip(args, torch, zs, np):
     dev = torch.device("cuda:0")
     w = WORKLOADS[1]
     N, U = w.n_ranks, len(w.units)
-    lays = [zs.shard_init("zero2", N, r, list(w.units)) for r in range(N)]
+    lays = [zs.shard_init("zero2", N, r, list(w.units)).chunk_state(state_chunk(args, zs))
+            for r in range(N)]
     S, P = lays[0].shard_len, lays[0].flat_len
     grads = [grad_bits(w, 0, q, P, device=dev) for q in range(N)]
     G = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
     full = torch.empty(P, dtype=torch.int16, device=dev)
-    st = [[master_init(w, lays[r].shard_len, device=dev, rank=r),
-           torch.zeros(lays[r].shard_len, device=dev), torch.zeros(lays[r].shard_len, device=dev)]
-          for r in range(N)]
+    st = [State(torch, L, master_init(w, L.shard_len, device=dev, rank=r)).views
+          for r, L in enumerate(lays)]
     gsh = [torch.empty(L.shard_len, device=dev) for L in lays]
     counts = [zs.reduce_partials_count(L, 0, U) for L in lays]
     offs = [sum(counts[:r]) for r in range(N)]
@@ -479,7 +480,8 @@ def run_gpt2_clip(args, torch, zs, np):
                     P / (ms * 1e-3), "params/s", ms,
                     "GPT-2-small flat buffer, 5 x 25M buckets, N=8: reduce + global-norm clip "
                     "+ AdamW + bf16 for all 8 ranks",
-                    psi=w.psi, n_ranks=N, shard_elems=S, buckets=list(w.units))
+                    psi=w.psi, n_ranks=N, shard_elems=S, buckets=list(w.units),
+                    state_layout=state_desc(lays[0].state_chunk))
     out["step_gbps"] = N * (rb + ab) / (ms * 1e-3) / 1e9
     out["kernels"] = kern
     out["roofline"] = roofline(dom[0], dom[1], kern[dom[0]]["ms_per_launch_mean"])
@@ -532,7 +534,7 @@ def run_gpt2_ddp_buckets(args, torch, zs, np):
     dev = torch.device("cuda:0")
     w = WORKLOADS[1]
     N, U = w.n_ranks, len(w.units)
-    L = zs.shard_init("ddp", N, 0, list(w.units))
+    L = zs.shard_init("ddp", N, 0, list(w.units)).chunk_state(state_chunk(args, zs))
     P = L.flat_len
     grads = [grad_bits(w, 0, q, P, device=dev) for q in range(N)]
     fo = [L.query(u)["flat_off"] for u in range(U)]
@@ -542,9 +544,7 @@ def run_gpt2_ddp_buckets(args, torch, zs, np):
     partials = torch.empty(sum(tiles), dtype=torch.float64, device=dev)
     g = torch.empty(P, device=dev)
     coef = torch.empty(1, device=dev)
-    p = master_init(w, P, device=dev)
-    m = torch.zeros(P, device=dev)
-    v = torch.zeros(P, device=dev)
+    p, m, v = State(torch, L, master_init(w, P, device=dev)).views
     out = torch.empty(P, dtype=torch.int16, device=dev)
     t = [0]
 
@@ -570,7 +570,8 @@ def run_gpt2_ddp_buckets(args, torch, zs, np):
                          P / (ms * 1e-3), "params/s", ms,
                          "GPT-2-small DDP replica, N=8: per-bucket reduce launches (last bucket "
                          "first) + global clip + one AdamW",
-                         psi=w.psi, n_ranks=N, buckets=list(w.units))
+                         psi=w.psi, n_ranks=N, buckets=list(w.units),
+                         state_layout=state_desc(L.state_chunk))
     out_line["kernels"] = kern
     out_line["roofline"] = roofline("adamw_apply_cast", 30 * P,
                                     kern["adamw_apply_cast"]["ms_per_launch_mean"])
@@ -587,15 +588,13 @@ def run_megatron(args, torch, zs, np):
     dev = torch.device("cuda:0")
     w = WORKLOADS[3]
     N, r = w.n_ranks, w.n_ranks - 1
-    L = zs.shard_init("megatron_do", N, r, list(w.units))
+    L = zs.shard_init("megatron_do", N, r, list(w.units)).chunk_state(state_chunk(args, zs))
     S, P = L.shard_len, L.flat_len
     main = torch.zeros(P, device=dev)
     micro = grad_bits(w, 0, r, P, device=dev, kind=KIND_MICRO)
     peers32 = [torch.empty(S, device=dev).normal_(0, 1e-3) for _ in range(N - 1)]
     G = zs.Grads(peers32 + [main], zs.FP32, [zs.INDEX_SHARD] * (N - 1) + [zs.INDEX_FULL])
-    master = master_init(w, S, device=dev, rank=r)
-    m = torch.zeros(S, device=dev)
-    v = torch.zeros(S, device=dev)
+    master, m, v = State(torch, L, master_init(w, S, device=dev, rank=r)).views
     replica = torch.empty(P, dtype=torch.int16, device=dev)
     peers16 = [torch.full((S,), q + 1, dtype=torch.int16, device=dev) for q in range(N - 1)]
     torch.cuda.synchronize()
@@ -623,7 +622,8 @@ def run_megatron(args, torch, zs, np):
                     "Megatron DO, Psi=7.24e9, N=8, rank 7: 4 micro-batch fp32 accumulations "
                     "over the whole buffer + fp32 reduce + Adam + bf16 + gather of 7 peers "
                     "(the step also zeroes main_grad with torch, untimed per phase)",
-                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S, micro_batches=w.micro_batches)
+                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S, micro_batches=w.micro_batches,
+                    state_layout=state_desc(L.state_chunk))
     out["optimizer_only_shard_params_per_s"] = S / (opt_ms * 1e-3)
     out["kernels"] = kern
     dom = max(("accumulate_fp32", acc_b), ("fused_fp32_reduce_adam_cast", fb),
@@ -643,15 +643,14 @@ def run_fsdp70b(args, torch, zs, np):
     w = WORKLOADS[4]
     N, r = w.n_ranks, w.n_ranks - 1
     units = list(w.units)
-    L = zs.shard_init("fsdp", N, r, units)
-    S = L.shard_len
+    L = zs.shard_init("fsdp", N, r, units).chunk_state(state_chunk(args, zs))
+    S, SE = L.shard_len, L.state_chunk
     q = [L.query(u) for u in range(len(units))]
     smax = max(x["shard_len"] for x in q)
     grads = [grad_bits(w, 0, k, smax, device=dev) for k in range(N)]
     G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
-    master = torch.empty(S, device=dev).normal_(0, 0.02)
-    m = torch.zeros(S, device=dev)
-    v = torch.zeros(S, device=dev)
+    st = State(torch, L, torch.empty(S, device=dev).normal_(0, 0.02))
+    master, m, v = st.views
     full_unit = torch.empty(N * smax, dtype=torch.int16, device=dev)
     peers = [torch.full((smax,), k + 1, dtype=torch.int16, device=dev) for k in range(N - 1)]
     torch.cuda.synchronize()
@@ -661,7 +660,9 @@ def run_fsdp70b(args, torch, zs, np):
         t[0] += 1
         cfg = zs.adam_cfg(step=t[0])
         for u, x in enumerate(q):
-            so = x["shard_off"]
+            # three arrays are passed from the unit's first element, a
+            # chunked state from its start
+            so = 0 if SE else x["shard_off"]
             phase(ph, "fused_reduce64_adam_cast",
                   lambda u=u, so=so: zs.adam_step(L, u, u + 1, cfg, master[so:], m[so:], v[so:],
                                                   full_unit, zs.INDEX_FULL, grads=G))
@@ -702,7 +703,8 @@ def run_fsdp70b(args, torch, zs, np):
                     "Llama-70B FSDP full shard, N=64, rank 63: 81 units x (fused reduce of 64 "
                     "rank grads + Adam + bf16 into the unit buffer, gather of 63 peers); value "
                     "is the faster zero_fsdp_sweep variant",
-                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S, units=len(units))
+                    psi=w.psi, n_ranks=N, rank=r, shard_elems=S, units=len(units),
+                    state_layout=state_desc(SE))
     out["per_unit_calls_ms_per_step"] = ms
     out["sweeps"] = sweeps
     out["kernels"] = kern
@@ -713,7 +715,7 @@ def run_fsdp70b(args, torch, zs, np):
     if args.cpu_baseline_seconds > 0:
         # one layer unit x 64 ranks on the CPU, extrapolated to the 81 units
         s0 = q[0]["shard_len"]
-        out["cpu_baseline"] = cpu_baseline(w, grads, lambda a, n: master[a:a + n], s0, r,
+        out["cpu_baseline"] = cpu_baseline(w, grads, st.master, s0, r,
                                            args.cpu_baseline_seconds,
                                            what="rank-{r} shard of layer unit 0", total=S)
     return out

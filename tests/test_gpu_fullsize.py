@@ -16,6 +16,11 @@ benchmark uses (default launch width, whole-range or per-unit calls).
     64 rank gradients + Adam + cast into the unit's full buffer, then gather
     the 63 peer shards; sampled elements of every unit against the oracle.
 
+Every workload keeps its fp32 master, m and v in the chunked state format
+the benchmark times (one buffer of ZERO_STATE_CHUNK_DEFAULT-element chunks,
+master | m | v per chunk); the values are compared at their chunked
+positions.
+
 Bar: bit-exact (see test_gpu_parity.py); the clip coefficient must equal the
 oracle's.
 """
@@ -67,6 +72,28 @@ def hp_of(w, t):
     return _c.hparams(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, t, w.decoupled)
 
 
+def chunk_pos(E, i):
+    """Offset of shard element i's master in a chunked state (m: + E, v: + 2E)."""
+    return (i // E) * (3 * E) + i % E
+
+
+def chunked_state(L, master):
+    """A chunked state buffer of layout L holding `master` (device fp32,
+    shard length) and zero m and v, with its (master, m, v) views."""
+    E, S = L.state_chunk, L.shard_len
+    rows = -(-S // E)
+    buf = torch.zeros(L.state_len, device=DEV)
+    col = torch.zeros(rows * E, device=DEV)
+    col[:S] = master
+    buf.view(rows, 3, E)[:, 0, :].copy_(col.view(rows, E))
+    return buf, list(L.state_views(buf))
+
+
+def unchunk(buf, E, S):
+    b = host_f32(buf).reshape(-1, 3, E)
+    return [np.ascontiguousarray(b[:, k, :].reshape(-1)[:S]) for k in range(3)]
+
+
 def sample(rng, n, k, edge=2048):
     idx = rng.integers(0, n, k)
     edges = np.concatenate([np.arange(0, min(edge, n)), np.arange(max(0, n - edge), n)])
@@ -83,17 +110,18 @@ def test_config1_gpt2_small_clip_all_ranks():
     oc = strategies.make_cluster("zero2", units, n, master0)
     ocfg = strategies.AdamConfig(w.lr, w.beta1, w.beta2, w.eps, w.weight_decay, w.decoupled,
                                  w.max_grad_norm)
-    lays = [zs.shard_init("zero2", n, r, units) for r in range(n)]
+    E = zs.STATE_CHUNK_DEFAULT
+    lays = [zs.shard_init("zero2", n, r, units).chunk_state(E) for r in range(n)]
     P = lays[0].flat_len
     assert P == psi                                     # buckets are multiples of 8
     full = torch.from_numpy(_c.f32_to_bf16(master0).view(np.int16)).to(DEV)
-    state = []
+    state, bufs = [], []
     for r in range(n):
         lay = oc.layouts[r]
         idx = np.concatenate([np.arange(b, b + k) for b, _, k in lay.owned_runs()])
-        S = lays[r].shard_len
-        state.append([torch.from_numpy(master0[idx]).to(DEV),
-                      torch.zeros(S, device=DEV), torch.zeros(S, device=DEV)])
+        buf, views = chunked_state(lays[r], torch.from_numpy(master0[idx]).to(DEV))
+        bufs.append(buf)
+        state.append(views)
     counts = [zs.reduce_partials_count(L, 0, len(units)) for L in lays]
     partials = torch.empty(sum(counts), dtype=torch.float64, device=DEV)
     gshard = [torch.empty(L.shard_len, device=DEV) for L in lays]
@@ -123,8 +151,9 @@ def test_config1_gpt2_small_clip_all_ranks():
     for r in range(n):
         lay = oc.layouts[r]
         idx = np.concatenate([np.arange(b, b + k) for b, _, k in lay.owned_runs()])
+        got = unchunk(bufs[r], E, lays[r].shard_len)
         for k, name in enumerate(("master", "m", "v")):
-            bitcmp(host_f32(state[r][k]), st[name][idx], f"config 1 rank {r} {name}")
+            bitcmp(got[k], st[name][idx], f"config 1 rank {r} {name}")
 
 
 # ------------------------------------------------------------ config 3 --
@@ -132,7 +161,8 @@ def test_config1_gpt2_small_clip_all_ranks():
 def test_config3_megatron_full_size_sampled():
     w = WORKLOADS[3]
     n, r = w.n_ranks, w.n_ranks - 1
-    L = zs.shard_init("megatron_do", n, r, list(w.units))
+    E = zs.STATE_CHUNK_DEFAULT
+    L = zs.shard_init("megatron_do", n, r, list(w.units)).chunk_state(E)
     S, P = L.shard_len, L.flat_len
     off = L.query(0)["rank_flat_off"]
     assert (S, P, off) == (905_000_000, 7_240_000_000, 6_335_000_000)
@@ -170,11 +200,10 @@ def test_config3_megatron_full_size_sampled():
         _c.accumulate_bf16(want_main, micro_full[k])
     bitcmp(host_f32(main[tfidx]), want_main, "config 3 main_grad accumulation")
 
-    master = master_init(w, S, device=DEV, rank=r)
-    m = torch.zeros(S, device=DEV)
-    v = torch.zeros(S, device=DEV)
+    buf, (master, m, v) = chunked_state(L, master_init(w, S, device=DEV, rank=r))
+    pos = torch.from_numpy(chunk_pos(E, idx)).to(DEV)
     replica = torch.zeros(P, dtype=torch.int16, device=DEV)
-    p_h = host_f32(master[tidx]).copy()
+    p_h = host_f32(buf[pos]).copy()
     ranks_fp32 = peers + [main]
     index = [zs.INDEX_SHARD] * (n - 1) + [zs.INDEX_FULL]
     zs.adam_step(L, 0, 1, cfg_of(w, 1), master, m, v, replica, zs.INDEX_FULL,
@@ -194,9 +223,9 @@ def test_config3_megatron_full_size_sampled():
     v_h = np.zeros(idx.size, np.float32)
     par_h = np.empty(idx.size, np.uint16)
     _c.rank_step(hp_of(w, 1), tot, 1.0, p_h, m_h, v_h, par_h)
-    bitcmp(host_f32(master[tidx]), p_h, "config 3 master")
-    bitcmp(host_f32(m[tidx]), m_h, "config 3 m")
-    bitcmp(host_f32(v[tidx]), v_h, "config 3 v")
+    bitcmp(host_f32(buf[pos]), p_h, "config 3 master")
+    bitcmp(host_f32(buf[pos + E]), m_h, "config 3 m")
+    bitcmp(host_f32(buf[pos + 2 * E]), v_h, "config 3 v")
     bitcmp(host_bf16(replica[off + tidx]), par_h, "config 3 own bf16 slice")
     assert_gathered(replica, 0, S, peer_bf16 + [None], idx, "config 3 gather")
 
@@ -207,13 +236,18 @@ def test_config4_llama70b_fsdp_per_unit_sampled():
     w = WORKLOADS[4]
     n, r = w.n_ranks, w.n_ranks - 1
     units = list(w.units)
-    L = zs.shard_init("fsdp", n, r, units)
+    E = zs.STATE_CHUNK_DEFAULT
+    L = zs.shard_init("fsdp", n, r, units).chunk_state(E)
     assert L.shard_len == 1_102_401_664
     smax = max(L.query(u)["shard_len"] for u in range(len(units)))
-    # whole-shard state, per-unit working buffers reused across units
-    master = torch.empty(L.shard_len, device=DEV)
-    m = torch.zeros(L.shard_len, device=DEV)
-    v = torch.zeros(L.shard_len, device=DEV)
+    # whole-shard chunked state, per-unit working buffers reused across units
+    master0 = torch.empty(L.shard_len, device=DEV)
+    for u in range(len(units)):
+        q = L.query(u)
+        master0[q["shard_off"]:q["shard_off"] + q["shard_len"]] = master_init(
+            w, q["shard_len"], device=DEV, rank=r, unit=u)
+    buf, st = chunked_state(L, master0)
+    del master0
     full_unit = torch.empty(smax * n, dtype=torch.int16, device=DEV)
     peers = [peer_bits(w, q, smax, device=DEV) for q in range(n - 1)]
     rng = np.random.default_rng(4)
@@ -221,13 +255,14 @@ def test_config4_llama70b_fsdp_per_unit_sampled():
     for u in range(len(units)):
         q = L.query(u)
         su, so = q["shard_len"], q["shard_off"]
-        master[so:so + su] = master_init(w, su, device=DEV, rank=r, unit=u)
         grads = [grad_bits(w, 0, k, su, device=DEV, unit=u) for k in range(n)]
         idx = sample(rng, su, 4096, edge=64)
         tidx = torch.from_numpy(idx).to(DEV)
+        pos = torch.from_numpy(chunk_pos(E, so + idx)).to(DEV)
         samp = [host_bf16(g[tidx]) for g in grads]
-        p_h = host_f32(master[so + tidx]).copy()
-        zs.adam_step(L, u, u + 1, cfg, master[so:], m[so:], v[so:], full_unit, zs.INDEX_FULL,
+        p_h = host_f32(buf[pos]).copy()
+        # a chunked state is passed from its start for every unit
+        zs.adam_step(L, u, u + 1, cfg, *st, full_unit, zs.INDEX_FULL,
                      grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
         zs.gather_params(L, u, u + 1, peers + [None], full_unit)
         del grads
@@ -235,8 +270,8 @@ def test_config4_llama70b_fsdp_per_unit_sampled():
         v_h = np.zeros(idx.size, np.float32)
         par_h = np.empty(idx.size, np.uint16)
         _c.rank_step(hp_of(w, 1), samp, 1.0, p_h, m_h, v_h, par_h)
-        bitcmp(host_f32(master[so + tidx]), p_h, f"config 4 unit {u} master")
-        bitcmp(host_f32(m[so + tidx]), m_h, f"config 4 unit {u} m")
-        bitcmp(host_f32(v[so + tidx]), v_h, f"config 4 unit {u} v")
+        bitcmp(host_f32(buf[pos]), p_h, f"config 4 unit {u} master")
+        bitcmp(host_f32(buf[pos + E]), m_h, f"config 4 unit {u} m")
+        bitcmp(host_f32(buf[pos + 2 * E]), v_h, f"config 4 unit {u} v")
         bitcmp(host_bf16(full_unit[r * su + tidx]), par_h, f"config 4 unit {u} own slice")
         assert_gathered(full_unit, 0, su, peers + [None], idx, f"config 4 unit {u} gather")

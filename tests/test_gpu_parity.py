@@ -367,13 +367,15 @@ def test_table_step_on_chunked_state():
         g.check(f"table on chunked state, step {t + 1}")
 
 
-def test_fp32_gradients_megatron():
-    """fp32 rank gradients (the Megatron main_grad) through the fused path."""
+@pytest.mark.parametrize("E", [0, 1024])
+def test_fp32_gradients_megatron(E):
+    """fp32 rank gradients (the Megatron main_grad) through the fused path,
+    with three state arrays and with a chunked state."""
     units, n = [8192 * 3 + 17], 8
     w = _w(units, n, "megatron_do", "none")
     master0, grads = draw(w, 2)
     oc = strategies.make_cluster("megatron_do", units, n, master0)
-    g = GpuRanks(w, master0, oc)
+    g = GpuRanks(w, master0, oc, state_chunk=E)
     for t in range(2):
         strategies.step(oc, oracle_cfg(w), t + 1, [[x] for x in grads[t]])
         g.step_fused(t + 1, grads[t], _modes("mixed", n), dtype=zs.FP32)
