@@ -52,7 +52,8 @@
 //
 // Both operands K-inner (dY W^T): 16x16x32 MFMAs and 64-k stage pairs
 // (gemm_tile_kp, below), so that every DMA instruction moves whole cache
-// lines.
+// lines; a pair lands every second tile, so only those tiles need a
+// barrier.
 //
 // MFMA 32x32x16 bf16 lane layout (checked on the device against an exact
 // CPU product): lane l holds A row (l % 32), k = 8 (l / 32) .. +7, and B
@@ -530,10 +531,14 @@ __device__ __forceinline__ void gemm_tile_kp(int64_t M, int64_t N, int64_t K,
         for (int q = 0; q < NMF; ++q)
             acc[q / TN][q % TN] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[F][q / TN], fb[F][q % TN], acc[q / TN][q % TN], 0, 0, 0);
     };
-    // Tile kt (TI = kt mod 4): wait for tile kt + 1's pair (odd tiles) or only
-    // for the LDS reads (even tiles), barrier; odd tiles then DMA the pair
-    // two ahead into the buffer the previous pair released; read tile
-    // kt + 1's fragments under tile kt's MFMAs.
+    // Tile kt (TI = kt mod 4): odd tiles wait for tile kt + 1's pair and
+    // their own fragment reads, then a barrier: after it every wave's part of
+    // that pair has landed and no wave still reads the buffer the pair
+    // before it used, so the DMA of the pair two ahead goes there.  Even
+    // tiles only wait for their own reads: tile kt + 1 is the other half of
+    // the pair already in place, and no DMA is issued, so they need no
+    // barrier (paired on the dX shape: 1.022 x faster, bit-identical).
+    // Read tile kt + 1's fragments under tile kt's MFMAs.
     auto tile = [&](auto ti, auto steady, int64_t kt) {
         constexpr int TI = decltype(ti)::value;
         constexpr bool STEADY = decltype(steady)::value != 0;
@@ -543,11 +548,12 @@ __device__ __forceinline__ void gemm_tile_kp(int64_t M, int64_t N, int64_t K,
         constexpr int P1 = (T1 >> 1) & 1, H1 = T1 & 1;   // its buffer and half
         constexpr int PN = (((TI + 3) >> 1)) & 1;        // buffer of pair (kt + 3) / 2
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ODD)
+        if constexpr (ODD) {
             wait_vm_lgkm0<0>();
-        else
+            __builtin_amdgcn_s_barrier();
+        } else {
             wait_vm_lgkm0<DP>();
-        __builtin_amdgcn_s_barrier();
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ODD) {
             const int64_t p = (kt + 3) / 2;
