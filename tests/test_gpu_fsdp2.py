@@ -27,7 +27,9 @@ def setup_module(module):
     zs = _zs
 
 
-def test_fsdp2_uneven_rows_all_ranks():
+@pytest.mark.parametrize("E", [0, 64])
+def test_fsdp2_uneven_rows_all_ranks(E):
+    """E > 0: every rank's master, m and v in one buffer of E-element chunks."""
     shapes = [(250, 64), (9, 512), (64, 1), (1, 4096), (17, 8), (2048, 3)]
     n = 8
     psi = sum(r * c for r, c in shapes)
@@ -35,17 +37,29 @@ def test_fsdp2_uneven_rows_all_ranks():
     master0 = master_init(w, psi).numpy()
     oc = strategies.make_cluster("fsdp2", shapes, n, master0)
     lays = [zs.shard_init_rows("fsdp2", n, r, shapes) for r in range(n)]
+    if E:
+        lays = [L.chunk_state(E) for L in lays]
     U = len(shapes)
     lay0 = oc.layouts[0]
     full = torch.zeros(lay0.flat_len, dtype=torch.int16, device=DEV)
     mfull = strategies.pad(lay0, master0)
     st = []
     idxs = []
+    bufs = []
     for r in range(n):
         idx = np.concatenate([np.arange(b, b + k) for b, _, k in oc.layouts[r].owned_runs()])
         idxs.append(idx)
-        st.append([torch.from_numpy(mfull[idx].copy()).to(DEV),
-                   torch.zeros(idx.size, device=DEV), torch.zeros(idx.size, device=DEV)])
+        if E:
+            rows = -(-idx.size // E)
+            b = np.zeros((rows, 3, E), np.float32)
+            col = np.zeros(rows * E, np.float32)
+            col[:idx.size] = mfull[idx]
+            b[:, 0, :] = col.reshape(rows, E)
+            bufs.append(torch.from_numpy(b.reshape(-1)).to(DEV))
+            st.append(list(lays[r].state_views(bufs[-1])))
+        else:
+            st.append([torch.from_numpy(mfull[idx].copy()).to(DEV),
+                       torch.zeros(idx.size, device=DEV), torch.zeros(idx.size, device=DEV)])
     cfg = strategies.AdamConfig(weight_decay=0.01, decoupled=True)
     for t in range(w.steps):
         grads = [grad_bits(w, t, q, psi).numpy().view(np.uint16) for q in range(n)]
@@ -60,9 +74,13 @@ def test_fsdp2_uneven_rows_all_ranks():
                               strategies.full_params(oc, padded=True)), t
     S = strategies.full_state(oc, padded=True)
     for r in range(n):
+        if E:
+            b = bufs[r].cpu().numpy().reshape(-1, 3, E)
+            got = [b[:, k, :].reshape(-1)[:idxs[r].size] for k in range(3)]
+        else:
+            got = [x.cpu().numpy() for x in st[r]]
         for k, name in enumerate(("master", "m", "v")):
-            assert np.array_equal(st[r][k].cpu().numpy().view(np.uint32),
-                                  S[name][idxs[r]].view(np.uint32)), (r, name)
+            assert np.array_equal(got[k].view(np.uint32), S[name][idxs[r]].view(np.uint32)), (r, name)
         # the library's valid rows agree with the oracle's (state dict export)
         for u in range(U):
             first, cnt = valid_rows(oc.layouts[r], u)

@@ -84,6 +84,40 @@ def test_fused_step_and_gather_in_a_graph():
     _replay_and_compare(lambda: step(G), lambda: step(E), G, E)
 
 
+def test_chunked_state_steps_in_a_graph():
+    # master, m and v in one chunked buffer: the fused step with its gather,
+    # then the apply pass of the two-pass path, captured and replayed
+    units, n, r, E = [5000, 3000, 777], 4, 1, 1024
+    L = zs.shard_init("zero3", n, r, units).chunk_state(E)
+    S, P = L.shard_len, L.flat_len
+    w = small_workload(units, n, "zero3", cfg=12)
+    grads = [grad_bits(w, 0, q, S, device=DEV) for q in range(n)]
+    peers = [None if q == r else grad_bits(w, 1, q, S, device=DEV) for q in range(n)]
+    cfg = zs.adam_cfg(lr=1e-3, weight_decay=0.01, decoupled=True, step=3)
+    npart = zs.reduce_partials_count(L, 0, len(units))
+
+    def buffers():
+        g = torch.Generator(device="cpu")
+        g.manual_seed(11)
+        st = (torch.randn(L.state_len, generator=g) * 1e-3).abs().to(DEV)
+        return [st, torch.zeros(P, dtype=torch.int16, device=DEV), torch.empty(S, device=DEV),
+                torch.empty(npart, dtype=torch.float64, device=DEV), torch.empty(1, device=DEV)]
+
+    def step(b):
+        G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+        zs.adam_step(L, 0, len(units), cfg, *L.state_views(b[0]), b[1], grads=G)
+        zs.gather_params(L, 0, len(units), peers, b[1])
+        zs.reduce_shard(L, 0, len(units), G, b[2], b[3], npart)
+        zs.clip_coef(b[3], npart, 1e-3, b[4])
+        zs.adam_step(L, 0, len(units), cfg, *L.state_views(b[0]), b[1], grad_fp32=b[2],
+                     clip_coef=b[4])
+
+    G_, E_ = buffers(), buffers()
+    step(buffers())
+    torch.cuda.synchronize()
+    _replay_and_compare(lambda: step(G_), lambda: step(E_), G_, E_)
+
+
 def test_launches_with_the_occupancy_reservation_in_a_graph():
     # the step kernel reserves LDS (its occupancy cap) only for launches of
     # more tiles than fit on the GPU at once, 5 per CU: a shard of about two
