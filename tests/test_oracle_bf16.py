@@ -52,3 +52,16 @@ def test_special_values():
     expect = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x3F80, 0x3F80, 0x3F82,
                        0x7F80, 0x0000], dtype=np.uint16)
     assert np.array_equal(_c.f32_to_bf16(x), expect)
+
+
+def test_rne_matches_torch_on_every_fp32_pattern():
+    # all 2^32 bit patterns, in chunks of 2^26
+    step = 1 << 26
+    base = np.arange(step, dtype=np.uint32)
+    for start in range(0, 1 << 32, step):
+        x = (base + np.uint32(start)).view(np.float32)
+        ours = _c.f32_to_bf16(x)
+        ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        nan = np.isnan(x)
+        assert np.array_equal(ours[~nan], ref[~nan]), hex(start)
+        assert np.all(ours[nan] == 0x7FC0), hex(start)
