@@ -12,9 +12,10 @@
 //     written by one instruction -- rocprof FETCH_SIZE / WRITE_SIZE equal the
 //     algorithmic bytes; the gather and the accumulation walk 2048-element
 //     tiles;
-//   * the step kernel runs at most 5 blocks (20 waves) per CU: fewer
-//     requests in flight mix the read and write streams better (measured
-//     below, at launch_one);
+//   * the step kernel runs at most 5 blocks (20 waves) per CU and the
+//     gather at most 13 (26 waves): fewer requests in flight mix the read
+//     and write streams better (measured below, at launch_one and at the
+//     gather launch);
 //   * one pass: the reduce over ranks, the Adam update and the bf16 cast are
 //     fused so each byte crosses HBM once;
 //   * one launch covers a tile space that concatenates the slices of many
@@ -51,6 +52,7 @@ constexpr int kMaxSegs = 32;                // units per launch (kernarg table)
 constexpr int kStepTile = 1024;             // elements per step-kernel tile
 constexpr int kStepThreads = 256;           // step kernel: one 4-element group per lane
 constexpr int kStepBlocksPerCU = 5;         // step kernel occupancy cap (LDS reservation)
+constexpr int kGatherBlocksPerCU = 13;      // gather occupancy cap (LDS reservation)
 constexpr int kAccThreads = 512;            // accumulate: one 4-element group per lane
 constexpr int kWaveElems = 256;             // elements one wave covers (64 lanes x 4)
 static_assert(kStepTile == kStepThreads * 4 && kTile == kAccThreads * 4, "one group per lane");
@@ -740,16 +742,17 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t tiles_of(int64_t len) { return (len + kTile - 1) / kTile; }
 int64_t step_tiles_of(int64_t len) { return (len + kStepTile - 1) / kStepTile; }
 
-// LDS bytes reserved per step-kernel block so that at most kStepBlocksPerCU
-// blocks share a CU (the kernel itself uses no LDS beyond a few bytes for
-// the clip partials).  From the device's LDS per CU (160 KiB on gfx950: 32
-// KiB per block), cached per device.
-size_t step_lds_reserve()
+// LDS bytes reserved per block so that at most CAP blocks share a CU (the
+// kernels themselves use no LDS beyond a few bytes for the clip partials).
+// From the device's LDS per CU (160 KiB on gfx950: 32 KiB per step block,
+// 12 KiB per gather block), cached per device.
+template <int CAP>
+size_t lds_reserve()
 {
     static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-        return 32 * 1024;
+        return (size_t)(((160 * 1024) / CAP) & ~1023);
     int v = cached[dev].load(std::memory_order_relaxed);
     if (v <= 0) {
         int lds = 0;
@@ -757,12 +760,14 @@ size_t step_lds_reserve()
                 hipSuccess ||
             lds <= 0)
             lds = 160 * 1024;
-        v = (lds / kStepBlocksPerCU) & ~1023;
+        v = (lds / CAP) & ~1023;
         v = v > 64 * 1024 ? 64 * 1024 : (v < 1024 ? 1024 : v);
         cached[dev].store(v, std::memory_order_relaxed);
     }
     return (size_t)v;
 }
+
+size_t step_lds_reserve() { return lds_reserve<kStepBlocksPerCU>(); }
 
 // Splits a unit range into launches of at most kMaxSegs units each and
 // calls fn(first_unit, last_unit_exclusive).
@@ -1319,15 +1324,26 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
             // default: one block per (tile, source) -- paired runs on the 7-
             // and 63-source shapes measured 6.2-6.3 TB/s against 5.4-5.6 with
             // each block walking n_src tiles; a persistent override spreads
-            // its width over the sources
-            static const int resident = resident_blocks(gather_kernel, kGatherThreads);
+            // its width over the sources.  A launch of more blocks than fit
+            // at once reserves LDS so that at most kGatherBlocksPerCU of them
+            // (26 waves) share a CU: paired over ten buffer placements on
+            // two boxes, 0.989 x (0.975-0.997) for 7 sources of the 7B
+            // shard and 0.990 x (0.981-0.996) for 63 sources of a
+            // Llama-70B layer unit, against full occupancy (32 waves);
+            // 14 and 12 blocks were within 0.3 % of it, 10 blocks 2.8 %
+            // slower.
+            const size_t lds = tiles * a.n_src > (int64_t)device_cus() * kGatherBlocksPerCU
+                                   ? lds_reserve<kGatherBlocksPerCU>()
+                                   : 0;
+            static const int resident = resident_blocks(gather_kernel, kGatherThreads,
+                                                        lds_reserve<kGatherBlocksPerCU>());
             int64_t gx = blocks_per_cu_override() == 0
                              ? stream_grid(tiles, resident, kGatherThreads)
                              : stream_grid(tiles, resident, kGatherThreads) / a.n_src;
             gx = gx < 1 ? 1 : gx;
             (void)hipGetLastError();
             hipLaunchKernelGGL(gather_kernel, dim3((unsigned)gx, (unsigned)a.n_src),
-                               dim3(kGatherThreads), 0, s, a);
+                               dim3(kGatherThreads), lds, s, a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return fail(ZERO_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e));

@@ -119,13 +119,17 @@ def test_chunked_state_steps_in_a_graph():
 
 
 def test_launches_with_the_occupancy_reservation_in_a_graph():
-    # the step kernel reserves LDS (its occupancy cap) only for launches of
-    # more tiles than fit on the GPU at once, 5 per CU: a shard of about two
-    # million elements (1954 tiles of 1024) takes that path, under capture
-    units, n, r = [6_000_000, 2_000_003], 4, 1
+    # the step kernel and the gather reserve LDS (their occupancy caps) only
+    # for launches of more blocks than fit on the GPU at once, 5 and 13 per
+    # CU: a shard of 2.5 million elements (2442 step tiles of 1024; 1222
+    # gather tiles of 2048 for each of 3 sources) takes both paths, under
+    # capture
+    units, n, r = [8_000_000, 2_000_003], 4, 1
     L = zs.shard_init("zero3", n, r, units)
     S, P = L.shard_len, L.flat_len
     assert S > 256 * 5 * 1024
+    gather_tiles = sum(-(-L.query(u)["shard_len"] // 2048) for u in range(len(units)))
+    assert gather_tiles * (n - 1) > 256 * 13
     w = small_workload(units, n, "zero3", cfg=12)
     grads = [grad_bits(w, 0, q, S, device=DEV) for q in range(n)]
     peers = [None if q == r else grad_bits(w, 1, q, S, device=DEV) for q in range(n)]
