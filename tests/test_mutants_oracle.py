@@ -166,10 +166,17 @@ def _build_c(dst: str) -> None:
                    capture_output=True, timeout=120)
 
 
+# The pass over all 2^32 cast patterns takes half a minute; the selected
+# million patterns of the same file catch every planted cast mistake, so
+# the mutant runs leave the exhaustive pass out.
+SLOW_PINS = ["tests/test_oracle_bf16.py::test_rne_matches_torch_on_every_fp32_pattern"]
+
+
 def _run_pins(root: str) -> subprocess.CompletedProcess:
     env = dict(os.environ, ZS_ORACLE_MUTANT_ROOT=root, PYTHONDONTWRITEBYTECODE="1")
+    deselect = [a for p in SLOW_PINS for a in ("--deselect", p)]
     return subprocess.run([sys.executable, "-m", "pytest", *PINS, "-x", "-q",
-                           "-p", "no:cacheprovider", "-m", "not gpu"],
+                           "-p", "no:cacheprovider", "-m", "not gpu", *deselect],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
