@@ -8,7 +8,10 @@
 // DDP nothing is sharded ("Data Parallel, ZeRO and FSDP", plain DDP).
 // zero_shard_init_rows pads and slices in whole dim-0 rows instead: FSDP2
 // shards each parameter on its own along dim 0 (same notes, "FSDP2 vs
-// FSDP1"), with torch.chunk row counts.
+// FSDP1"), with torch.chunk row counts.  zero_layout_chunk_state copies a
+// layout and records a chunked format for its fp32 master, m and v (one
+// buffer, chunks of E master, E m, E v values): a memory layout the notes
+// leave open ("Model states" fixes only what is kept per parameter).
 #include <cstdarg>
 #include <cstdio>
 #include <new>
