@@ -76,8 +76,39 @@ int main()
         CHECK(st == ZERO_OK && L);
         if (L) {
             check_layout(L, n, num, cols);
+            // a chunked-state copy: the same layout, its state length
+            const int64_t E = (int64_t)1 << (2 + (int)(rng() % 23));   // 4 .. 2^24
+            zero_layout *C = nullptr;
+            CHECK(zero_layout_chunk_state(L, E, &C) == ZERO_OK && C);
+            if (C) {
+                check_layout(C, n, num, cols);
+                int64_t e = -1, len = -1, S = -1;
+                CHECK(zero_layout_info(L, nullptr, &S, nullptr, nullptr, nullptr, nullptr) == ZERO_OK);
+                CHECK(zero_layout_state(C, &e, &len) == ZERO_OK);
+                CHECK(e == E && len == (S + E - 1) / E * 3 * E);
+                CHECK(zero_layout_state(L, &e, &len) == ZERO_OK && e == 0 && len == S);
+                zero_shard_destroy(C);
+            }
+            zero_layout *B = (zero_layout *)&rng;  // refused: *out becomes NULL
+            CHECK(zero_layout_chunk_state(L, E + 1 + (E == 4 ? 1 : 0), &B) == ZERO_ERR_INVALID_ARG && !B);
             zero_shard_destroy(L);
         }
+    }
+    {
+        zero_layout *C = (zero_layout *)&rng;
+        CHECK(zero_layout_chunk_state(nullptr, 8, &C) == ZERO_ERR_INVALID_ARG && !C);
+        CHECK(zero_layout_chunk_state(nullptr, 8, nullptr) == ZERO_ERR_INVALID_ARG);
+        CHECK(zero_layout_state(nullptr, nullptr, nullptr) == ZERO_ERR_INVALID_ARG);
+        // a state length past the representable byte range is refused
+        const int64_t big = (int64_t)1 << 60;
+        zero_layout *L = nullptr, *D = nullptr;
+        CHECK(zero_shard_init(&L, ZERO_DDP, 1, 0, 1, &big) == ZERO_OK && L);
+        CHECK(zero_layout_chunk_state(L, (int64_t)1 << 24, &D) == ZERO_OK && D);
+        int64_t len = 0;
+        CHECK(zero_layout_state(D, nullptr, &len) == ZERO_ERR_INVALID_ARG);
+        CHECK(zero_layout_state(L, nullptr, &len) == ZERO_OK && len == big);
+        zero_shard_destroy(D);
+        zero_shard_destroy(L);
     }
     // adversarial sizes: every one is refused, and *out is left NULL
     const int64_t huge[] = {INT64_MAX, INT64_MAX / 2, (int64_t)1 << 62};
