@@ -81,6 +81,10 @@ def parse():
                     help="master, m and v of every workload as one buffer of E-element "
                          "chunks (zero_layout_chunk_state); 0 keeps three arrays; default: "
                          "the library's ZERO_STATE_CHUNK_DEFAULT")
+    ap.add_argument("--grad-chunk", type=int, default=None, metavar="E",
+                    help="the headline's 8 shard-indexed rank gradients as one buffer of rows "
+                         "of E elements per rank (zero_grads.chunk); 0 keeps 8 buffers; "
+                         "default: the library's ZERO_GRAD_CHUNK_DEFAULT")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
@@ -200,10 +204,74 @@ def state_desc(E):
             f"one fp32 buffer of {E}-element chunks, master | m | v per chunk")
 
 
-def headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=True):
+class RankGrads:
+    """The N ranks' shard-indexed bf16 gradients for one shard: N buffers, or
+    one buffer of rows of E elements per rank (rank q's element i at
+    (i // E) N E + q E + i % E), the chunked format zero_grads.chunk names."""
+
+    def __init__(self, torch, zs, L, draws, E):
+        self.zs, self.E, self.N, self.S = zs, E, len(draws), L.shard_len
+        self._grads = None
+        if E == 0:
+            self.bufs, self.buf = list(draws), None
+            return
+        rows, dev = -(-self.S // E), draws[0].device
+        self.bufs = None
+        self.buf = torch.zeros(L.grad_len(E), dtype=torch.int16, device=dev)
+        cells = self.buf.view(rows, self.N, E)
+        col = torch.zeros(rows * E, dtype=torch.int16, device=dev)
+        for q, d in enumerate(draws):
+            col[:self.S] = d
+            cells[:, q, :].copy_(col.view(rows, E))
+        del col
+
+    @property
+    def grads(self):
+        """The zs.Grads the library takes (made on first use)."""
+        if self._grads is None:
+            zs = self.zs
+            self._grads = (zs.Grads(self.bufs, zs.BF16, zs.INDEX_SHARD) if self.E == 0 else
+                           zs.Grads.chunked(self.buf, self.N, self.E))
+        return self._grads
+
+    @property
+    def ptrs(self):
+        """Rank q's pointer for each q, as the library takes them."""
+        return self.bufs if self.E == 0 else [self.buf[q * self.E:] for q in range(self.N)]
+
+    def rank(self, q, off, n):
+        """Rank q's gradient for shard elements [off, off + n) (a tensor)."""
+        if self.E == 0:
+            return self.bufs[q][off:off + n]
+        E = self.E
+        r0, r1 = off // E, -(-(off + n) // E)
+        return self.buf.view(-1, self.N, E)[r0:r1, q, :].reshape(-1)[off - r0 * E:off - r0 * E + n]
+
+    def ranks(self):
+        """One sliceable per rank: ranks()[q][a:b] is rank q's [a, b)."""
+        me = self
+
+        class _Rank:
+            def __init__(self, q):
+                self.q = q
+
+            def __getitem__(self, sl):
+                return me.rank(self.q, sl.start, sl.stop - sl.start)
+
+        return [_Rank(q) for q in range(self.N)]
+
+
+def grad_desc(E, N):
+    return (f"{N} bf16 buffers, one per rank" if E == 0 else
+            f"one bf16 buffer of rows of {E} elements per rank, {N} ranks per row")
+
+
+def headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=True, grad_chunk=0):
     """A fresh allocation of the headline step's buffers (one placement)."""
     from synthetic import grad_bits, master_init
-    grads = [grad_bits(w, 0, q, S, device=dev) for q in range(N)]
+    draws = [grad_bits(w, 0, q, S, device=dev) for q in range(N)]
+    grads = RankGrads(torch, zs, L, draws, grad_chunk)
+    del draws
     st = State(torch, L, master_init(w, S, device=dev, rank=r))
     full = torch.empty(L.flat_len, dtype=torch.int16, device=dev)
     peers = ([torch.full((S,), q + 1, dtype=torch.int16, device=dev) for q in range(N - 1)]
@@ -214,6 +282,10 @@ def headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=True):
 
 def state_chunk(args, zs):
     return zs.STATE_CHUNK_DEFAULT if args.state_chunk is None else args.state_chunk
+
+
+def grad_chunk(args, zs):
+    return zs.GRAD_CHUNK_DEFAULT if args.grad_chunk is None else args.grad_chunk
 
 
 def release(torch, *objs):
@@ -241,19 +313,20 @@ def run_headline(args, torch, zs, np):
     else:
         L = zs.shard_init("zero3", N, r, list(w.units))
     L = L.chunk_state(state_chunk(args, zs))
+    GE = grad_chunk(args, zs)
     S = L.shard_len
     U = L.info()["n_units"]
     print(f"# setup: {w.name}, rank {r}, shard {S} elements, {U} units, "
-          f"{args.placements} placements, state: {state_desc(L.state_chunk)}", file=sys.stderr,
-          flush=True)
+          f"{args.placements} placements, state: {state_desc(L.state_chunk)}, "
+          f"gradients: {grad_desc(GE, N)}", file=sys.stderr, flush=True)
     fused_b, gather_b = 42 * S, 4 * (N - 1) * S
     runs = []
     cpu = cmp = None
     for k in range(args.placements):
-        grads, st, full, peers = headline_buffers(torch, zs, w, L, S, N, r, dev)
+        grads, st, full, peers = headline_buffers(torch, zs, w, L, S, N, r, dev, grad_chunk=GE)
         master, m, v = st.views
         shard_ptrs = peers + [None]                  # own slice is written by the step
-        G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+        G = grads.grads
         t = [0]
 
         def step(ph):
@@ -273,11 +346,11 @@ def run_headline(args, torch, zs, np):
               flush=True)
         if k == args.placements - 1:
             if args.cpu_baseline_seconds > 0:
-                cpu = cpu_baseline(w, grads, st.master, S, r, args.cpu_baseline_seconds)
+                cpu = cpu_baseline(w, grads.ranks(), st.master, S, r, args.cpu_baseline_seconds)
             if args.vs_torch:
                 cmp = step_vs_torch(torch, zs, L, U, w, grads, st, full, G, r, S)
         del G, shard_ptrs
-        release(torch, grads, peers)
+        release(torch, peers)
         del grads, st, master, m, v, full, peers
         torch.cuda.empty_cache()
     order = sorted(range(len(runs)), key=lambda i: runs[i][0])
@@ -288,7 +361,7 @@ def run_headline(args, torch, zs, np):
                     "rank shard step: reduce 8 bf16 rank grads + Adam + "
                     "bf16 cast into the flat buffer + gather of 7 peer shards",
                     psi=L.flat_len, n_ranks=N, rank=r, shard_elems=S, units=U,
-                    state_layout=state_desc(L.state_chunk),
+                    state_layout=state_desc(L.state_chunk), grad_layout=grad_desc(GE, N),
                     algorithmic_bytes_per_step=fused_b + gather_b)
     out["step_gbps"] = (fused_b + gather_b) / (ms * 1e-3) / 1e9
     out["state_gbps_16psi_over_n"] = 16 * S / (ms * 1e-3) / 1e9
@@ -317,10 +390,12 @@ def step_vs_torch(torch, zs, L, U, w, grads, st, full, G, r, S, rounds=5, iters=
     mixed-dtype adds), one division by N, torch.optim.Adam(fused=True) on an
     fp32 copy of the master, and the bf16 cast into the rank's slice of the
     flat buffer.  Timed alternately with zero_adam_step (the fused kernel),
-    `iters` steps per round, on the current stream with HIP events."""
-    N = len(grads)
+    `iters` steps per round, on the current stream with HIP events.  The
+    PyTorch side gets each rank's gradient as its own contiguous tensor (a
+    copy when the kernel's are chunked)."""
+    N = grads.N
     master, m, v = st.views
-    gb = [g.view(torch.bfloat16) for g in grads]
+    gb = [grads.rank(q, 0, S).contiguous().view(torch.bfloat16) for q in range(N)]
     own = full.view(torch.bfloat16)[r * S:(r + 1) * S]
     p = torch.nn.Parameter(st.master(0, S).detach().clone())
     acc = torch.empty(S, device=master.device)
@@ -878,16 +953,17 @@ def calibrate_mix(args, torch, zs, np, rounds=5):
     w = WORKLOADS[2]
     N, r = w.n_ranks, w.n_ranks - 1
     L = zs.shard_init("zero3", N, r, list(w.units)).chunk_state(state_chunk(args, zs))
-    S, SE = L.shard_len, L.state_chunk
+    S, SE, GE = L.shard_len, L.state_chunk, grad_chunk(args, zs)
     kinds = {"fused_step": 42 * S, "step_streams_no_math": 42 * S, "reads_only": 28 * S,
              "writes_only": 14 * S}
     E = torch.cuda.Event
     per = {k: [] for k in kinds}
     for pl in range(args.calibrate_mix):
-        grads, st, full, _ = headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=False)
+        rg, st, full, _ = headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=False,
+                                           grad_chunk=GE)
         master, m, v = st.views
         own = full[r * S:(r + 1) * S]
-        G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+        G, grads = rg.grads, rg.ptrs
         t = [0]
 
         def fused():
@@ -897,11 +973,12 @@ def calibrate_mix(args, torch, zs, np, rounds=5):
 
         fns = {"fused_step": fused,
                "step_streams_no_math": lambda: zs.stream_mix(zs.MIX_STEP_STREAMS, grads, master,
-                                                             m, v, own, S, state_chunk=SE),
+                                                             m, v, own, S, state_chunk=SE,
+                                                             grad_chunk=GE),
                "reads_only": lambda: zs.stream_mix(zs.MIX_READS, grads, master, m, v, own, S,
-                                                   state_chunk=SE),
+                                                   state_chunk=SE, grad_chunk=GE),
                "writes_only": lambda: zs.stream_mix(zs.MIX_WRITES, grads, master, m, v, own, S,
-                                                    state_chunk=SE)}
+                                                    state_chunk=SE, grad_chunk=GE)}
         got = {k: [] for k in kinds}
         names = list(kinds)
         for rd in range(rounds + 1):
@@ -918,14 +995,14 @@ def calibrate_mix(args, torch, zs, np, rounds=5):
             per[k].append(sorted(got[k])[len(got[k]) // 2])
         print("# placement %d: %s" % (pl, ", ".join(f"{k} {per[k][-1]:.3f} ms" for k in kinds)),
               file=sys.stderr, flush=True)
-        del G, own
-        release(torch, grads)
-        del grads, st, master, m, v, full
+        del G, own, grads
+        release(torch)
+        del rg, st, master, m, v, full
         torch.cuda.empty_cache()
     med = {k: sorted(x)[len(x) // 2] for k, x in per.items()}
     return {"calibrate_mix": {
         "workload": "Mistral-7B ZeRO-3 rank shard, N=8, 905,000,000 elements",
-        "state_layout": state_desc(SE),
+        "state_layout": state_desc(SE), "grad_layout": grad_desc(GE, N),
         "placements": args.calibrate_mix, "rounds_per_placement": rounds,
         "ms_per_placement": per,
         "ms_median": med,

@@ -41,6 +41,7 @@ MAX_RANKS_PER_CALL = 64
 NOALLOC_MAX_PARTIALS = 524288
 STATE_CHUNK_MIN, STATE_CHUNK_MAX = 4, 1 << 24     # zero_layout_chunk_state bounds
 STATE_CHUNK_DEFAULT = 8192                         # the measured best on MI355X
+GRAD_CHUNK_DEFAULT = 16384                         # chunked gradients, likewise
 
 STRATEGY = {"ddp": DDP, "zero1": STAGE1, "zero1_allreduce": STAGE1, "zero2": STAGE2,
             "zero3": STAGE3, "fsdp": FSDP, "fsdp2": FSDP, "megatron_do": MEGATRON_DO}
@@ -52,7 +53,7 @@ _I64 = ctypes.c_int64
 
 class _Grads(ctypes.Structure):
     _fields_ = [("ptrs", ctypes.POINTER(ctypes.c_void_p)), ("index", ctypes.POINTER(ctypes.c_uint8)),
-                ("n", _I32), ("dtype", _I32), ("index_all", _I32), ("_reserved", _I32)]
+                ("n", _I32), ("dtype", _I32), ("index_all", _I32), ("chunk", _I32)]
 
 
 class AdamCfg(ctypes.Structure):
@@ -140,7 +141,7 @@ _lib.zero_fsdp_linear_backward.argtypes = [_P, _I32, ctypes.POINTER(ctypes.c_voi
                                            _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_linear_backward.restype = _I32
 _lib.zero_stream_mix.argtypes = [_I32, ctypes.POINTER(ctypes.c_void_p), _I32, _P, _P, _P, _P,
-                                 _I64, _I64, _P]
+                                 _I64, _I64, _I64, _P]
 _lib.zero_stream_mix.restype = _I32
 _lib.zero_grad_accumulate.argtypes = [_P, _P, _I64, _P]
 _lib.zero_grad_accumulate.restype = _I32
@@ -343,13 +344,28 @@ class Layout:
         """Floats each of master, m and v must hold from its pointer for a
         call over [unit_begin, unit_end), or None for a range the library
         will refuse."""
+        return self._chunked_count(unit_begin, unit_end, self.state_chunk, 3)
+
+    def grad_count(self, unit_begin: int, unit_end: int, chunk: int):
+        """Elements each rank's pointer into chunked gradients (chunk E) must
+        reach for a call over [unit_begin, unit_end); None as above."""
+        return self._chunked_count(unit_begin, unit_end, chunk, self.info()["world_n"])
+
+    def grad_len(self, chunk: int) -> int:
+        """Elements of one buffer holding all N ranks' gradients for this
+        shard in chunks of `chunk` (ceil(S / E) rows of N chunks)."""
+        E, N = chunk, self.info()["world_n"]
+        return -(-self.shard_len // E) * N * E
+
+    def _chunked_count(self, unit_begin, unit_end, E, k):
+        # a buffer of rows of k chunks of E elements, addressed by absolute
+        # shard index i at (i // E) k E + i % E from each pointer
         shard, _ = self.range_lens(unit_begin, unit_end)
-        E = self.state_chunk
         if shard is None or E == 0 or shard == 0:
             return shard
         last = self._unit_table()[unit_end - 1]
         i = last["shard_off"] + last["shard_len"] - 1     # highest shard index touched
-        return (i // E) * 3 * E + i % E + 1
+        return (i // E) * k * E + i % E + 1
 
     @property
     def flat_len(self) -> int:
@@ -384,7 +400,7 @@ def shard_init_rows(strategy, world_n: int, rank: int, shapes) -> Layout:
 class Grads:
     """Marshalled zero_grads; keeps its ctypes arrays alive."""
 
-    def __init__(self, bufs, dtype: int = BF16, index=INDEX_FULL):
+    def __init__(self, bufs, dtype: int = BF16, index=INDEX_FULL, chunk: int = 0):
         self._keep = list(bufs)              # keeps tensors alive; sliceable by callers
         ptrs = [_addr(b) for b in bufs]
         self._ptrs = (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs)
@@ -394,19 +410,33 @@ class Grads:
             idx_all = index
         else:
             self._index = (ctypes.c_uint8 * len(index))(*[int(i) for i in index])
-        self.s = _Grads(self._ptrs, self._index, len(ptrs), dtype, idx_all, 0)
+        self.s = _Grads(self._ptrs, self._index, len(ptrs), dtype, idx_all, chunk)
         self._checked = None
+
+    @classmethod
+    def chunked(cls, buf, n: int, chunk: int, dtype: int = BF16):
+        """N ranks' shard-indexed gradients interleaved in one buffer in
+        chunks of `chunk` elements (Layout.grad_len long): rank q's pointer
+        is the buffer's start + q * chunk."""
+        return cls([buf[q * chunk:] for q in range(n)], dtype, INDEX_SHARD, chunk)
+
+    @property
+    def chunk(self) -> int:
+        return self.s.chunk
 
     def ref(self):
         return ctypes.byref(self.s)
 
-    def check(self, lens) -> None:
-        """Each rank buffer holds its index mode's range (lens from
-        Layout.range_lens).  The buffers of a Grads never change, so a
-        range checked once is not checked again."""
+    def check(self, layout, unit_begin: int, unit_end: int) -> None:
+        """Each rank buffer holds what a call over [unit_begin, unit_end)
+        reads from it.  The buffers of a Grads never change, so a range
+        checked once is not checked again."""
+        shard, full = layout.range_lens(unit_begin, unit_end)
+        if self.chunk and shard is not None:
+            shard = layout.grad_count(unit_begin, unit_end, self.chunk)
+        lens = (shard, full)
         if lens == self._checked:
             return
-        shard, full = lens
         for q, b in enumerate(self._keep):
             mode = self.s.index_all if self._index is None else self._index[q]
             _need(b, f"gradient buffer of rank {q}", full if mode == INDEX_FULL else shard,
@@ -424,7 +454,7 @@ def reduce_shard(layout: Layout, unit_begin: int, unit_end: int, grads: Grads, o
                  out_index: int = INDEX_SHARD) -> None:
     shard, full = layout.range_lens(unit_begin, unit_end)
     if grads is not None:
-        grads.check((shard, full))
+        grads.check(layout, unit_begin, unit_end)
     _need(out, "out", full if out_index == INDEX_FULL else shard, "fp32")
     _need(sumsq_partials, "sumsq_partials", n_partials, "fp64")
     _check(_lib.zero_reduce_shard(layout.handle, unit_begin, unit_end, grads.ref() if grads else None,
@@ -455,7 +485,7 @@ def _check_step(layout, unit_begin, unit_end, master, m, v, param_out, param_ind
     if clip_coef is not None:
         _need(clip_coef, "clip_coef", 1, "fp32")
     if grads is not None:
-        grads.check(lens)
+        grads.check(layout, unit_begin, unit_end)
 
 
 def adam_step(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, master, m, v,
@@ -700,20 +730,25 @@ def fsdp_linear_backward(layout: Layout, unit: int, w_shards, batch: int, x, dy,
 
 
 def stream_mix(kind: int, grads, master, m, v, param, n: int, stream=None,
-               state_chunk: int = 0) -> None:
+               state_chunk: int = 0, grad_chunk: int = 0) -> None:
     """zero_stream_mix: the fused step's memory traffic without its
     arithmetic (kind MIX_STEP_STREAMS), its reads alone (MIX_READS) or its
     writes alone (MIX_WRITES), over n elements; state_chunk E > 0 takes
-    master, m, v in the chunked format (m = master + E, v = master + 2E)."""
+    master, m, v in the chunked format (m = master + E, v = master + 2E),
+    grad_chunk G > 0 the rank gradients chunked (grads[q] = grads[0] + qG)."""
+
+    def count(E, k):
+        return n if E <= 0 or n <= 0 else ((n - 1) // E) * k * E + (n - 1) % E + 1
+
     for q, x in enumerate(grads):
-        _need(x, f"gradient buffer of rank {q}", n, "bf16")
-    E = state_chunk
-    sc = n if E <= 0 or n <= 0 else ((n - 1) // E) * 3 * E + (n - 1) % E + 1
+        _need(x, f"gradient buffer of rank {q}", count(grad_chunk, len(grads)), "bf16")
+    sc = count(state_chunk, 3)
     for name, x in (("master", master), ("m", m), ("v", v)):
         _need(x, name, sc, "fp32")
     _need(param, "param", n, "bf16")
     _check(_lib.zero_stream_mix(kind, _ptrs(grads), len(grads), _addr(master), _addr(m), _addr(v),
-                                _addr(param), n, state_chunk, _stream(stream)), "zero_stream_mix")
+                                _addr(param), n, state_chunk, grad_chunk, _stream(stream)),
+           "zero_stream_mix")
 
 
 def grad_accumulate(main_grad, micro_bf16, n: int, stream=None) -> None:

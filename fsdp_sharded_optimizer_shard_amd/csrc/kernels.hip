@@ -104,7 +104,8 @@ struct StepArgs {
     float *master, *m, *v;
     int64_t st_base;     // chunked state: shard index of the range's first element
     int32_t st_shift;    // 0: three state arrays; else log2 of the state chunk
-    int32_t _pad1;
+    int32_t g_shift;     // 0: one buffer per rank; else log2 of the gradient chunk
+    int64_t g_base;      // chunked gradients: shard index of the range's first element
     const float *gin;    // kApply: averaged gradient
     int32_t gin_full;    // kApply: 1 if gin is full-indexed, 0 if shard-indexed
     int32_t _pad2;
@@ -222,6 +223,20 @@ __device__ __forceinline__ int64_t st_at(const StepArgs &a, int64_t si)
     return ((i >> sh) * 3 << sh) + (i & (((int64_t)1 << sh) - 1));
 }
 
+// Offset of shard element `si` (relative to the range) in a shard-indexed
+// rank gradient.  One buffer per rank: si itself.  Chunked gradients (chunk
+// E = 2^g_shift, N ranks in one buffer): element i = g_base + si of rank q
+// sits at (i / E) N E + i % E from rank q's pointer, which is rank 0's + qE.
+// As for the state, a 4-aligned group never crosses a chunk.
+__device__ __forceinline__ int64_t g_at(const StepArgs &a, int n, int64_t si)
+{
+    if (a.g_shift == 0)
+        return si;
+    const int64_t i = a.g_base + si;
+    const int sh = a.g_shift;
+    return ((i >> sh) * n << sh) + (i & (((int64_t)1 << sh) - 1));
+}
+
 // Sum of the N rank gradients for G groups of 4 consecutive elements, group
 // h at shard index si[h] / full index fi[h] (vector path).  Each rank is
 // added in ascending order, from +0.
@@ -230,11 +245,14 @@ __device__ __forceinline__ void reduce_groups(const StepArgs &a, const int64_t *
                                               const int64_t *fi, float (*acc)[4])
 {
     const int n = NR > 0 ? NR : a.n_ranks;
+    int64_t gi[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+    for (int h = 0; h < G; ++h) {
+        gi[h] = g_at(a, n, si[h]);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             acc[h][e] = 0.0f;
+    }
     // one group of 8 rank loads in flight per thread; other waves hide the
     // latency between groups (unrolling further only raises register use)
 #pragma unroll 1
@@ -249,7 +267,7 @@ __device__ __forceinline__ void reduce_groups(const StepArgs &a, const int64_t *
                     const uint16_t *base = static_cast<const uint16_t *>(a.grads[q]);
 #pragma unroll
                     for (int h = 0; h < G; ++h)
-                        w[k][h] = ld_nt(reinterpret_cast<const u32x2 *>(base + (full ? fi[h] : si[h])));
+                        w[k][h] = ld_nt(reinterpret_cast<const u32x2 *>(base + (full ? fi[h] : gi[h])));
                 }
             }
 #pragma unroll
@@ -274,7 +292,7 @@ __device__ __forceinline__ void reduce_groups(const StepArgs &a, const int64_t *
                     const float *base = static_cast<const float *>(a.grads[q]);
 #pragma unroll
                     for (int h = 0; h < G; ++h)
-                        w[k][h] = ld_nt(reinterpret_cast<const f32x4 *>(base + (full ? fi[h] : si[h])));
+                        w[k][h] = ld_nt(reinterpret_cast<const f32x4 *>(base + (full ? fi[h] : gi[h])));
                 }
             }
 #pragma unroll
@@ -297,8 +315,9 @@ __device__ __forceinline__ float reduce1(const StepArgs &a, int64_t si, int64_t 
 {
     const int n = NR > 0 ? NR : a.n_ranks;
     float acc = 0.0f;
+    const int64_t gi = g_at(a, n, si);
     for (int q = 0; q < n; ++q) {
-        const int64_t i = ((a.full_mask >> q) & 1) ? fi : si;
+        const int64_t i = ((a.full_mask >> q) & 1) ? fi : gi;
         const float x = BF16 ? bf16f(static_cast<const uint16_t *>(a.grads[q])[i])
                              : static_cast<const float *>(a.grads[q])[i];
         acc = acc + x;
@@ -784,11 +803,12 @@ zero_status for_each_chunk(int32_t ub, int32_t ue, F fn)
 }
 
 // Fills the segment table for units [u0, u1) of a call whose range starts
-// at `ub`; returns the number of tiles.  `state_abs`: the launch addresses a
-// chunked state by absolute shard index, so a slice takes the vector path
-// only if its absolute shard offset is a multiple of 4 as well.
+// at `ub`; returns the number of tiles.  `abs_index`: the launch addresses a
+// chunked state or chunked gradients by absolute shard index, so a slice
+// takes the vector path only if its absolute shard offset is a multiple of 4
+// as well.
 int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg *seg,
-                  int32_t *n_segs, bool state_abs = false)
+                  int32_t *n_segs, bool abs_index = false)
 {
     int64_t tiles = 0;
     int32_t k = 0;
@@ -802,7 +822,7 @@ int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg 
         s.full_off = L->flat_off[u] - L->flat_off[ub] + (int64_t)L->rank * len;
         s.tile0 = tiles;
         s.vec = (s.shard_off % 4 == 0 && s.full_off % 4 == 0 &&
-                 (!state_abs || L->shard_off[u] % 4 == 0)) ? 1 : 0;
+                 (!abs_index || L->shard_off[u] % 4 == 0)) ? 1 : 0;
         tiles += step_tiles_of(len);
     }
     *n_segs = k;
@@ -833,12 +853,39 @@ zero_status check_grads(const zero_layout *L, const zero_grads *g)
         if (g->index && g->index[q] != ZERO_INDEX_FULL && g->index[q] != ZERO_INDEX_SHARD)
             return fail(ZERO_ERR_INVALID_ARG, "unknown index %d for rank %d", g->index[q], q);
     }
+    if (g->chunk == 0)
+        return ZERO_OK;
+    const int64_t E = g->chunk;
+    if (E < ZERO_STATE_CHUNK_MIN || E > ZERO_STATE_CHUNK_MAX || (E & (E - 1)))
+        return fail(ZERO_ERR_INVALID_ARG,
+                    "grads->chunk = %d: 0 or a power of two in [%d, %d]", g->chunk,
+                    ZERO_STATE_CHUNK_MIN, ZERO_STATE_CHUNK_MAX);
+    const int64_t S = L->shard_off[L->n_units];
+    if ((S + E - 1) / E > INT64_MAX / 4 / E / g->n)
+        return fail(ZERO_ERR_INVALID_ARG, "chunked gradients of %lld elements per rank overflow",
+                    (long long)S);
+    const char *base = static_cast<const char *>(g->ptrs[0]);
+    for (int q = 0; q < g->n; ++q) {
+        if ((g->index ? g->index[q] : g->index_all) != ZERO_INDEX_SHARD)
+            return fail(ZERO_ERR_INVALID_ARG,
+                        "chunked gradients are shard-indexed (rank %d is full-indexed)", q);
+        if (static_cast<const char *>(g->ptrs[q]) != base + (int64_t)q * E * (int64_t)elem)
+            return fail(ZERO_ERR_INVALID_ARG,
+                        "chunked gradients: rank %d's pointer must be rank 0's + %d chunk elements",
+                        q, q);
+    }
     return ZERO_OK;
 }
 
-void fill_grads(const zero_grads *g, StepArgs &a, bool &all_aligned)
+// The rank buffers of a call whose range starts at unit `ub`.
+void fill_grads(const zero_layout *L, int32_t ub, const zero_grads *g, StepArgs &a,
+                bool &all_aligned)
 {
     a.n_ranks = g->n;
+    if (g->chunk) {
+        a.g_shift = __builtin_ctz((unsigned)g->chunk);
+        a.g_base = L->shard_off[ub];
+    }
     a.full_mask = 0;
     for (int q = 0; q < g->n; ++q) {
         a.grads[q] = g->ptrs[q];
@@ -993,11 +1040,11 @@ zero_status adam_launch(const zero_layout *L, int32_t ub, int32_t ue, const Adam
         std::memset(&a, 0, sizeof a);
         bool al = aligned16(master) && aligned16(m) && aligned16(v) && aligned16(param_out);
         if (grads)
-            fill_grads(grads, a, al);
+            fill_grads(L, ub, grads, a, al);
         else
             al = al && aligned16(grad_fp32);
         a.vec_ptrs = al;
-        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs, E > 0);
+        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs, E > 0 || (grads && grads->chunk));
         if (a.n_tiles == 0)
             return ZERO_OK;
         a.master = master;
@@ -1114,9 +1161,9 @@ zero_status zero_reduce_shard(const zero_layout *L, int32_t ub, int32_t ue,
         StepArgs a;
         std::memset(&a, 0, sizeof a);
         bool al = aligned16(out);
-        fill_grads(grads, a, al);
+        fill_grads(L, ub, grads, a, al);
         a.vec_ptrs = al;
-        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs);
+        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs, grads->chunk != 0);
         if (a.n_tiles == 0)
             return ZERO_OK;
         a.gout = out;
@@ -1357,7 +1404,7 @@ zero_status zero_gather_params(const zero_layout *L, int32_t ub, int32_t ue,
 
 zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t n_ranks,
                             float *master, float *m, float *v, uint16_t *param, int64_t n,
-                            int64_t state_chunk, void *stream)
+                            int64_t state_chunk, int64_t grad_chunk, void *stream)
 {
     if (kind != ZERO_MIX_STEP_STREAMS && kind != ZERO_MIX_READS && kind != ZERO_MIX_WRITES)
         return fail(ZERO_ERR_INVALID_ARG, "unknown stream-mix kind %d", kind);
@@ -1376,10 +1423,18 @@ zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t 
     if (E > 0 && (m != master + E || v != master + 2 * E))
         return fail(ZERO_ERR_INVALID_ARG, "chunked state: m and v must be master + state_chunk "
                     "and master + 2 state_chunk");
+    const int64_t GE = grad_chunk;
+    if (GE != 0 &&
+        (GE < ZERO_STATE_CHUNK_MIN || GE > ZERO_STATE_CHUNK_MAX || (GE & (GE - 1)) != 0))
+        return fail(ZERO_ERR_INVALID_ARG, "grad_chunk must be 0 or a power of two in [%d, %d] "
+                    "(got %lld)", ZERO_STATE_CHUNK_MIN, ZERO_STATE_CHUNK_MAX, (long long)GE);
     bool al = aligned16(master) && aligned16(m) && aligned16(v) && aligned16(param);
     for (int q = 0; q < n_ranks; ++q) {
         if (!grads[q])
             return fail(ZERO_ERR_INVALID_ARG, "gradient buffer of rank %d is NULL", q);
+        if (GE > 0 && grads[q] != grads[0] + q * GE)
+            return fail(ZERO_ERR_INVALID_ARG, "chunked gradients: rank %d's pointer must be "
+                        "rank 0's + %d grad_chunk elements", q, q);
         al = al && aligned16(grads[q]);
     }
     if (!al)
@@ -1401,6 +1456,8 @@ zero_status zero_stream_mix(int32_t kind, const uint16_t *const *grads, int32_t 
     a.v = v;
     if (E > 0)
         a.st_shift = __builtin_ctzll((unsigned long long)E);
+    if (GE > 0)
+        a.g_shift = __builtin_ctzll((unsigned long long)GE);
     a.pout = param;
     a.sink_key = __builtin_nanf("");
     const hipStream_t s = static_cast<hipStream_t>(stream);

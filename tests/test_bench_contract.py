@@ -84,3 +84,35 @@ def test_bench_state_holds_the_master_in_the_layouts_format(E):
         assert not b[:, 1:, :].any(), "m and v start at zero"
         assert st.views[1].data_ptr() == st.buf.data_ptr() + 4 * E
         assert st.views[2].data_ptr() == st.buf.data_ptr() + 8 * E
+
+
+@pytest.mark.parametrize("E", [0, 4, 1024, 16384])
+def test_bench_rank_grads_in_the_chunked_format(E):
+    # the benchmark's gradient holder puts rank q's element i at
+    # (i // E) N E + q E + i % E of one buffer (or in rank q's own buffer)
+    # and reads any range of any rank back, also through ranks()
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    import bench
+    from fsdp_sharded_optimizer_shard_amd import zs
+    L = zs.shard_init("zero3", 8, 7, [80_000, 333])
+    S, N = L.shard_len, 8
+    rng = np.random.default_rng(E)
+    draws = [torch.from_numpy(rng.integers(-2 ** 15, 2 ** 15, S, dtype=np.int16))
+             for _ in range(N)]
+    rg = bench.RankGrads(torch, zs, L, draws, E)
+    if E:
+        assert rg.buf.numel() == L.grad_len(E)
+        i = np.arange(S)
+        flat = rg.buf.numpy()
+        for q in range(N):
+            assert np.array_equal(flat[(i // E) * N * E + q * E + i % E], draws[q].numpy())
+        assert [p.data_ptr() - rg.buf.data_ptr() for p in rg.ptrs] == [2 * E * q
+                                                                      for q in range(N)]
+    views = rg.ranks()
+    for q in (0, 3, 7):
+        for off, n in ((0, S), (S - 1, 1), (5, 4099), (E + 1 if E < S else 2, 33)):
+            n = min(n, S - off)
+            assert torch.equal(rg.rank(q, off, n), draws[q][off:off + n]), (q, off, n)
+            assert torch.equal(views[q][off:off + n], draws[q][off:off + n])

@@ -43,6 +43,14 @@ def test_exports_every_declared_function():
     assert sorted(zs.EXPORTS) == declared
 
 
+def test_binding_constants_equal_the_headers():
+    txt = open(HEADER).read()
+    defs = dict(re.findall(r"#define (ZERO_[A-Z0-9_]+) (\d+)", txt))
+    for name in ("STATE_CHUNK_MIN", "STATE_CHUNK_MAX", "STATE_CHUNK_DEFAULT",
+                 "GRAD_CHUNK_DEFAULT", "MAX_RANKS_PER_CALL"):
+        assert int(defs["ZERO_" + name]) == getattr(zs, name), name
+
+
 def _same_as_oracle(strategy, units, n, r):
     L = zs.shard_init(strategy, n, r, units)
     O = plan(units, n, r, sharded=strategy != "ddp")
@@ -683,3 +691,107 @@ def test_stream_mix_chunked_state_validation():
              state_chunk=E)
     assert e.status == zs.ERR_INVALID_ARG and "chunked state" in str(e)
     zs.stream_mix(zs.MIX_READS, g8, *ok, 0, 0, state_chunk=E)   # n = 0: nothing to launch
+
+
+def test_stream_mix_chunked_grads_validation():
+    G = 512
+    ok = (FAKE, FAKE + 4 * 1024, FAKE + 8 * 1024, FAKE)
+    gc = [FAKE + 2 * G * q for q in range(8)]
+    for bad in (3, 2, 6, 2 * zs.STATE_CHUNK_MAX):
+        assert _err(zs.stream_mix, zs.MIX_READS, gc, *ok, 64, 0, state_chunk=1024,
+                    grad_chunk=bad).status == zs.ERR_INVALID_ARG
+    e = _err(zs.stream_mix, zs.MIX_READS, gc[:7] + [gc[7] + 16], *ok, 64, 0, state_chunk=1024,
+             grad_chunk=G)
+    assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
+    zs.stream_mix(zs.MIX_READS, gc, *ok, 0, 0, state_chunk=1024, grad_chunk=G)   # n = 0
+
+
+# --------------------------------------------------- chunked gradients --
+
+def _chunked_grads(n, E, step=None, dtype=None):
+    """Pointers of chunked gradients: rank q at FAKE + q * step bytes."""
+    dtype = zs.BF16 if dtype is None else dtype
+    step = E * (2 if dtype == zs.BF16 else 4) if step is None else step
+    return zs.Grads([FAKE + q * step for q in range(n)], dtype, zs.INDEX_SHARD, E)
+
+
+@pytest.mark.parametrize("E", [-4, 1, 2, 3, 6, 12, 1000, 2 * zs.STATE_CHUNK_MAX])
+def test_chunked_grads_reject_bad_chunks(E):
+    L = _layout()
+    g = zs.Grads([FAKE] * 4, zs.BF16, zs.INDEX_SHARD, E)
+    e = _err(_adam, L, grads=g)
+    assert e.status == zs.ERR_INVALID_ARG and "grads->chunk" in str(e)
+
+
+def test_chunked_grads_need_rank_pointers_one_chunk_apart():
+    # rank q's pointer is rank 0's + q E elements (bf16: 2 bytes, fp32: 4),
+    # every rank shard-indexed; anything else is refused on the host, by the
+    # fused step, the reduce and the no-allocation call alike
+    L, E = _layout(), 1024
+    cfg = zs.adam_cfg(step=1)
+    bad = [_chunked_grads(4, E, step=4 * E),                       # fp32 spacing for bf16
+           _chunked_grads(4, E, step=2 * E + 2),
+           _chunked_grads(4, E, dtype=zs.FP32, step=2 * E),        # bf16 spacing for fp32
+           zs.Grads([FAKE + 2 * E * q for q in (0, 1, 3, 2)], zs.BF16, zs.INDEX_SHARD, E)]
+    for g in bad:
+        e = _err(_adam, L, grads=g)
+        assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
+    full = zs.Grads([FAKE + 2 * E * q for q in range(4)], zs.BF16, zs.INDEX_FULL, E)
+    mixed = zs.Grads([FAKE + 2 * E * q for q in range(4)], zs.BF16,
+                     [zs.INDEX_SHARD] * 3 + [zs.INDEX_FULL], E)
+    for g in (full, mixed):
+        e = _err(_adam, L, grads=g)
+        assert e.status == zs.ERR_INVALID_ARG and "shard-indexed" in str(e)
+    g = bad[1]
+    e = _err(zs.reduce_shard, L, 0, 2, g, FAKE, stream=0)
+    assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
+    e = _err(lambda *a: zs.adam_step_clip_noalloc(*a, stream=0), L, 0, 2, cfg, 1.0, g, FAKE,
+             FAKE, FAKE, FAKE, FAKE)
+    assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
+
+
+def test_chunked_grads_counts_in_the_binding():
+    import torch
+
+    class Dev:
+        def __init__(self, n, off=0, dtype=torch.int16):
+            self._n, self._off, self.dtype = n, off, dtype
+            self.is_cuda, self.device = True, "cuda:0"
+
+        def numel(self):
+            return self._n
+
+        def element_size(self):
+            return 2 if self.dtype == torch.int16 else 4
+
+        def is_contiguous(self):
+            return True
+
+        def data_ptr(self):
+            return FAKE + self.element_size() * self._off
+
+        def __getitem__(self, sl):
+            return Dev(self._n - sl.start, self._off + sl.start, self.dtype)
+
+    E, N = 8, 4
+    L = zs.shard_init("zero3", N, 1, [1000, 24])     # shard 250 + 6
+    assert L.grad_len(E) == 32 * N * E
+    # the last shard index touched, 255, sits at (255 // 8) 32 + 7 = 999
+    # from each rank's pointer, whatever the range
+    assert L.grad_count(0, 2, E) == 1000 and L.grad_count(1, 2, E) == 1000
+    assert L.grad_count(0, 1, E) == (249 // 8) * 32 + 249 % 8 + 1
+    assert L.grad_count(1, 1, E) == 0 and L.grad_count(0, 3, E) is None
+    whole = Dev(L.grad_len(E))
+    G = zs.Grads.chunked(whole, N, E)
+    assert G.chunk == E and G.s.index_all == zs.INDEX_SHARD
+    assert [b.data_ptr() for b in G._keep] == [FAKE + 2 * E * q for q in range(N)]
+
+    def step(G):
+        zs.adam_step(L, 0, 2, zs.adam_cfg(step=1), Dev(256, 0, torch.float32),
+                     Dev(256, 0, torch.float32), Dev(256, 0, torch.float32), Dev(1024),
+                     grads=G, stream=0)
+
+    # rank 3's view of a buffer one element short reaches 999 only
+    with pytest.raises(ValueError, match="gradient buffer of rank 3 holds 999 elements, "
+                                         "the call touches 1000"):
+        step(zs.Grads.chunked(Dev(L.grad_len(E) - 1), N, E))

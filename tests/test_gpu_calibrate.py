@@ -93,3 +93,33 @@ def test_step_streams_on_a_chunked_state():
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     assert np.array_equal(param.cpu().numpy().view(np.uint16),
                           (got[pos].view(np.uint32) >> 16).astype(np.uint16))
+
+
+@pytest.mark.parametrize("n_ranks", [8, 3])
+def test_step_streams_on_chunked_gradients(n_ranks):
+    """The rank values come from the chunked positions (element i of rank q
+    at (i / G) N G + q G + i % G of one buffer); the rest of it is unread."""
+    n, E, G = 3 * 2048 + 4 * 37, 1024, 512
+    rng = np.random.default_rng(21 + n_ranks)
+    dev = torch.device("cuda:0")
+    grows = -(-n // G)
+    gbuf = rng.integers(0, 1 << 16, grows * n_ranks * G, dtype=np.uint16) & 0xbfff
+    dg = torch.from_numpy(gbuf.view(np.int16)).to(dev)
+    rows = -(-n // E)
+    buf = rng.standard_normal(rows * 3 * E).astype(np.float32)
+    dbuf = torch.from_numpy(buf.copy()).to(dev)
+    param = torch.zeros(n, dtype=torch.int16, device=dev)
+    zs.stream_mix(zs.MIX_STEP_STREAMS, [dg[q * G:] for q in range(n_ranks)],
+                  dbuf[0:], dbuf[E:], dbuf[2 * E:], param, n, state_chunk=E, grad_chunk=G)
+    torch.cuda.synchronize()
+    i = np.arange(n)
+    acc = np.zeros(n, np.float32)
+    for q in range(n_ranks):
+        x = gbuf[(i // G) * n_ranks * G + q * G + i % G]
+        acc = acc + (x.astype(np.uint32) << 16).view(np.float32)
+    pos = (i // E) * 3 * E + i % E
+    want = buf.copy()
+    for k in range(3):
+        want[pos + k * E] = buf[pos + k * E] + acc
+    got = dbuf.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

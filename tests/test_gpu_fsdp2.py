@@ -5,7 +5,8 @@ the same kernels, driven by row-granular slices, against the oracle.
     1-D weights) for every rank of N = 8, fused into one full buffer;
   * the exact Mistral-7B per-parameter layout (291 parameters,
     7,241,732,096 elements) at N = 8, rank 7, one call over all parameters
-    (10 launches of up to 32), 2 steps, sampled.
+    (10 launches of up to 32), 2 steps, sampled, with the chunked state and
+    chunked rank gradients the benchmark uses.
 """
 import numpy as np
 import pytest
@@ -13,6 +14,7 @@ import torch
 
 from oracle import _c, strategies
 from oracle.layout import valid_rows
+from chunked import grad_buffer, state_buffer, state_pos
 from gather_check import assert_gathered
 from synthetic import grad_bits, master_init, mistral7b_shapes, peer_bits, small_workload
 
@@ -89,9 +91,14 @@ def test_fsdp2_uneven_rows_all_ranks(E):
 
 
 def test_fsdp2_mistral7b_full_size_sampled():
+    """The exact Mistral-7B per-parameter layout (291 parameters) in the
+    benchmark's --fsdp2 launch: state chunked at the library default, the 8
+    rank gradients chunked into one buffer; two steps, sampled elements
+    (with every parameter's first shard element) against the oracle."""
     shapes = mistral7b_shapes()
     n, r = 8, 7
-    L = zs.shard_init_rows("fsdp2", n, r, shapes)
+    E, GE = zs.STATE_CHUNK_DEFAULT, zs.GRAD_CHUNK_DEFAULT
+    L = zs.shard_init_rows("fsdp2", n, r, shapes).chunk_state(E)
     S = L.shard_len
     assert L.flat_len == 7_241_732_096 and S == 905_216_512
     w = small_workload([L.flat_len], n, "fsdp2", steps=2, cfg=8)
@@ -100,26 +107,27 @@ def test_fsdp2_mistral7b_full_size_sampled():
                                     [L.query(u)["shard_off"] for u in range(len(shapes))],
                                     [S - 1]])).astype(np.int64)
     tidx = torch.from_numpy(idx).to(DEV)
+    pos = torch.from_numpy(state_pos(E, idx)).to(DEV)
     master = master_init(w, S, device=DEV, rank=r)
-    m = torch.zeros(S, device=DEV)
-    v = torch.zeros(S, device=DEV)
+    st = state_buffer(L, master)
     own = torch.empty(S, dtype=torch.int16, device=DEV)
     p_h = master[tidx].cpu().numpy().copy()
+    del master
     m_h = np.zeros(idx.size, np.float32)
     v_h = np.zeros(idx.size, np.float32)
     par_h = np.empty(idx.size, np.uint16)
     for t in range(w.steps):
-        grads = [grad_bits(w, t, q, S, device=DEV) for q in range(n)]
-        samp = [g[tidx].cpu().numpy().view(np.uint16) for g in grads]
-        zs.adam_step(L, 0, len(shapes), zs.adam_cfg(step=t + 1), master, m, v, own, zs.INDEX_SHARD,
-                     grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
-        del grads
+        gbuf, samp = grad_buffer(L, n, GE, lambda q: grad_bits(w, t, q, S, device=DEV), tidx)
+        zs.adam_step(L, 0, len(shapes), zs.adam_cfg(step=t + 1), *L.state_views(st), own,
+                     zs.INDEX_SHARD, grads=zs.Grads.chunked(gbuf, n, GE))
+        torch.cuda.synchronize()
+        del gbuf
         _c.rank_step(_c.hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, t + 1, False), samp, 1.0,
                      p_h, m_h, v_h, par_h)
     torch.cuda.synchronize()
-    assert np.array_equal(master[tidx].cpu().numpy().view(np.uint32), p_h.view(np.uint32))
-    assert np.array_equal(m[tidx].cpu().numpy().view(np.uint32), m_h.view(np.uint32))
-    assert np.array_equal(v[tidx].cpu().numpy().view(np.uint32), v_h.view(np.uint32))
+    assert np.array_equal(st[pos].cpu().numpy().view(np.uint32), p_h.view(np.uint32))
+    assert np.array_equal(st[pos + E].cpu().numpy().view(np.uint32), m_h.view(np.uint32))
+    assert np.array_equal(st[pos + 2 * E].cpu().numpy().view(np.uint32), v_h.view(np.uint32))
     assert np.array_equal(own[tidx].cpu().numpy().view(np.uint16), par_h)
     # gather the 7 peer shards into the full per-parameter buffer
     full = torch.empty(L.flat_len, dtype=torch.int16, device=DEV)

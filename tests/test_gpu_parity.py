@@ -11,10 +11,12 @@ fp64 global norm (summation order); its fp32 clip coefficient must match.
 Small cases span several 2048-element tiles, ragged tails, zero padding,
 slices that are not multiples of 8 (scalar path), N in {1, 2, 3, 4, 5, 8,
 64}, bf16 and fp32 gradients, full- and shard-indexed rank buffers, AdamW and
-L2 decay, whole-range and per-unit calls.  The full-size 7B / N = 8 shard
-is checked after 3 steps in the launch configuration the benchmark times:
-on sampled elements (with the gather into the 7.24e9-element buffer), and
-element by element over all 905,000,000 elements.
+L2 decay, whole-range and per-unit calls, three state arrays or a chunked
+state, one buffer per rank gradient or all N chunked into one.  The
+full-size 7B / N = 8 shard is checked after 3 steps in the launch
+configuration the benchmark times: on sampled elements (with the gather
+into the 7.24e9-element buffer), and element by element over all
+905,000,000 elements.
 """
 import numpy as np
 import pytest
@@ -73,6 +75,19 @@ def chunk_state(master, m, v, E):
     return buf.reshape(-1)
 
 
+def chunk_grads(xs, E):
+    """One chunked gradient buffer (rows of E elements of each of the N
+    ranks in order) holding N shard-length arrays; row tails stay zero."""
+    S, n = xs[0].size, len(xs)
+    rows = -(-S // E)
+    buf = np.zeros((rows, n, E), xs[0].dtype)
+    for q, x in enumerate(xs):
+        col = np.zeros(rows * E, x.dtype)
+        col[:S] = x
+        buf[:, q, :] = col.reshape(rows, E)
+    return buf.reshape(-1)
+
+
 def unchunk_state(buf, E, S):
     """(master, m, v) of shard length S out of a chunked state buffer."""
     b = np.asarray(buf).reshape(-1, 3, E)
@@ -119,11 +134,12 @@ class GpuRanks:
     buffer (the all-gather is implicit) or, for ZeRO-3, into its own shard
     buffer followed by zero_gather_params."""
 
-    def __init__(self, w, master0, oracle_cluster, state_chunk=0):
+    def __init__(self, w, master0, oracle_cluster, state_chunk=0, grad_chunk=0):
         self.w = w
         self.n = w.n_ranks
         self.oc = oracle_cluster
         self.E = state_chunk
+        self.GE = grad_chunk
         self.lays = [zs.shard_init(w.strategy, self.n, r, list(w.units)) for r in range(self.n)]
         if state_chunk:
             self.lays = [L.chunk_state(state_chunk) for L in self.lays]
@@ -156,20 +172,40 @@ class GpuRanks:
     def rank_grads(self, grads_t, r, index_modes, dtype):
         lay0 = self.oc.layouts[0]
         idx = owned_index(self.oc.layouts[r])
-        bufs = []
+        xs = []
         for q in range(self.n):
             full = strategies.pad(lay0, grads_t[q])
             if dtype == zs.FP32:
                 full = _c.bf16_to_f32(full)
-            x = full if index_modes[q] == zs.INDEX_FULL else full[idx]
-            bufs.append(dev_f32(x) if dtype == zs.FP32 else dev_bf16(x))
-        return bufs
+            xs.append(full if index_modes[q] == zs.INDEX_FULL else full[idx])
+        if self.GE:
+            buf = chunk_grads(xs, self.GE)
+            assert buf.size == self.lays[r].grad_len(self.GE)
+            return dev_f32(buf) if dtype == zs.FP32 else dev_bf16(buf)
+        return [dev_f32(x) if dtype == zs.FP32 else dev_bf16(x) for x in xs]
+
+    def grads_of(self, bufs, dtype, index_modes):
+        """zs.Grads over rank_grads' result (one chunked buffer, or N)."""
+        if self.GE:
+            return zs.Grads.chunked(bufs, self.n, self.GE, dtype)
+        return zs.Grads(bufs, dtype, list(index_modes))
 
     def step_fused(self, t, grads_t, index_modes, dtype=None, per_unit=False):
         dtype = zs.BF16 if dtype is None else dtype
         c = cfg_of(self.w, t)
         for r, L in enumerate(self.lays):
             bufs = self.rank_grads(grads_t, r, index_modes, dtype)
+            if self.GE:
+                # chunked gradients and a chunked state are passed from their
+                # start for every range; three state arrays move with the unit
+                G = self.grads_of(bufs, dtype, index_modes)
+                for u0, u1 in ([(u, u + 1) for u in range(self.U)] if per_unit else
+                               [(0, self.U)]):
+                    so = L.query(u0)["shard_off"] if u0 < self.U else 0
+                    st = self.state[r] if self.E else [x[so:] for x in self.state[r]]
+                    fo = L.query(u0)["flat_off"] if u0 < self.U else 0
+                    zs.adam_step(L, u0, u1, c, *st, self.full[fo:], zs.INDEX_FULL, grads=G)
+                continue
             if not per_unit:
                 G = zs.Grads(bufs, dtype, list(index_modes))
                 zs.adam_step(L, 0, self.U, c, *self.state[r], self.full, zs.INDEX_FULL, grads=G)
@@ -193,10 +229,11 @@ class GpuRanks:
         partials = torch.empty(sum(counts), dtype=torch.float64, device=DEV)
         gshard = []
         off = 0
+        modes = [zs.INDEX_SHARD if self.GE else zs.INDEX_FULL] * self.n
         for r, L in enumerate(self.lays):
-            bufs = self.rank_grads(grads_t, r, [zs.INDEX_FULL] * self.n, zs.BF16)
+            bufs = self.rank_grads(grads_t, r, modes, zs.BF16)
             g = torch.empty(L.shard_len, device=DEV)
-            zs.reduce_shard(L, 0, self.U, zs.Grads(bufs, zs.BF16, zs.INDEX_FULL), g,
+            zs.reduce_shard(L, 0, self.U, self.grads_of(bufs, zs.BF16, modes), g,
                             partials[off:], counts[r])
             off += counts[r]
             gshard.append(g)
@@ -382,6 +419,85 @@ def test_fp32_gradients_megatron(E):
         g.check(f"megatron fp32 step {t + 1}")
 
 
+GRAD_CHUNK_CASES = [
+    # units, N, strategy, decay, state chunk, gradient chunk
+    ([5000, 333, 20000], 4, "zero2", "adamw", 8192, 16384),
+    ([4097, 1, 0, 7], 3, "zero2", "l2", 0, 4),
+    ([2048 * 3 + 5], 5, "zero3", "none", 1024, 8),
+    ([640, 6400, 64000], 8, "fsdp", "adamw", 8192, 1024),
+    ([129 * 64, 64, 1], 64, "fsdp", "none", 16384, 64),
+]
+
+
+@pytest.mark.parametrize("units,n,strategy,decay,E,GE", GRAD_CHUNK_CASES)
+def test_fused_step_chunked_grads(units, n, strategy, decay, E, GE):
+    """The N rank gradients in one chunked buffer (rows of GE elements per
+    rank), with three state arrays or a chunked state: bit for bit the
+    oracle's results.  N = 3 and 5 give rows that are not a power of two;
+    chunks of 4 and 8 put every 4-element group at a chunk edge; units with
+    shard offsets that are not multiples of 4 run the scalar path."""
+    w = _w(units, n, strategy, decay)
+    master0, grads = draw(w, w.steps)
+    oc = strategies.make_cluster(strategy, units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=E, grad_chunk=GE)
+    for t in range(w.steps):
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        g.step_fused(t + 1, grads[t], _modes("shard", n))
+        g.check(f"{units} N={n} E={E} GE={GE} step {t + 1}")
+
+
+@pytest.mark.parametrize("E,GE", [(0, 4), (64, 4096), (4, 16)])
+def test_per_unit_calls_on_chunked_grads(E, GE):
+    """One call per unit, chunked gradients passed from the buffer's start
+    every time (unit shard offsets 1024, 1049, 3097, ...: vector and
+    scalar slices)."""
+    units, n = [4096, 100, 8192 + 3, 8], 4
+    w = _w(units, n, "fsdp", "adamw")
+    master0, grads = draw(w, 2)
+    oc = strategies.make_cluster("fsdp", units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=E, grad_chunk=GE)
+    for t in range(2):
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        g.step_fused(t + 1, grads[t], _modes("shard", n), per_unit=True)
+        g.check(f"per-unit chunked grads E={E} GE={GE} step {t + 1}")
+
+
+def test_fp32_chunked_grads_megatron():
+    """fp32 rank gradients in one chunked buffer through the fused path."""
+    units, n = [8192 * 3 + 17], 8
+    w = _w(units, n, "megatron_do", "none")
+    master0, grads = draw(w, 2)
+    oc = strategies.make_cluster("megatron_do", units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=1024, grad_chunk=2048)
+    for t in range(2):
+        strategies.step(oc, oracle_cfg(w), t + 1, [[x] for x in grads[t]])
+        g.step_fused(t + 1, grads[t], _modes("shard", n), dtype=zs.FP32)
+        g.check(f"megatron fp32 chunked grads step {t + 1}")
+
+
+def test_two_pass_clip_on_chunked_grads():
+    """reduce_shard from chunked gradients -> clip coefficient -> Adam from
+    fp32; the coefficient must equal the oracle's."""
+    units, n, max_norm = [25000, 25000, 24439], 8, 1e-4
+    w = small_workload(units, n, "zero2", steps=2, cfg=11, weight_decay=0.01, decoupled=True,
+                       max_grad_norm=max_norm, outlier_frac=0.01)
+    master0, grads = draw(w, w.steps)
+    oc = strategies.make_cluster("zero2", units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=2048, grad_chunk=8192)
+    lay0 = oc.layouts[0]
+    for t in range(w.steps):
+        g_mean = _c.average([strategies.pad(lay0, x) for x in grads[t]])
+        want_coef = _c.clip_coef(_c.sumsq(g_mean), max_norm)
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        gshard, coef, _ = g.step_two_pass(t + 1, grads[t], max_norm)
+        torch.cuda.synchronize()
+        assert coef.item() == np.float32(want_coef)
+        for r in range(n):
+            idx = owned_index(oc.layouts[r])
+            assert_f32_close(host_f32(gshard[r]), g_mean[idx], f"reduced grad rank {r}")
+        g.check(f"chunked grads clip step {t + 1}")
+
+
 @pytest.mark.parametrize("max_norm", [1.0, 1e-4])
 def test_two_pass_clip(max_norm):
     """reduce_shard -> clip_coef -> adam_step(grad_fp32, clip_coef), AdamW,
@@ -487,35 +603,51 @@ def _sample_index(S, rng):
 
 def test_config2_full_size_sampled():
     """Mistral-7B ZeRO-3 rank shard: 905,000,000 elements, N = 8, rank 7,
-    3 Adam steps through the fused path (the benchmark's launch), then the
-    gather of the 7 peer shards; sampled elements against the oracle."""
+    3 Adam steps through the fused path in the benchmark's launch (state
+    chunked at the library default, the 8 rank gradients chunked into one
+    buffer), then the gather of the 7 peer shards; sampled elements against
+    the oracle."""
     w = WORKLOADS[2]
     n, r = w.n_ranks, w.n_ranks - 1
-    L = zs.shard_init("zero3", n, r, list(w.units))
+    E, GE = zs.STATE_CHUNK_DEFAULT, zs.GRAD_CHUNK_DEFAULT
+    L = zs.shard_init("zero3", n, r, list(w.units)).chunk_state(E)
     S = L.shard_len
     assert S == 905_000_000
     rng = np.random.default_rng(2)
     idx = _sample_index(S, rng)
+    pos = torch.from_numpy((idx // E) * 3 * E + idx % E).to(DEV)
     tidx = torch.from_numpy(idx).to(DEV)
     master = master_init(w, S, device=DEV, rank=r)
-    m = torch.zeros(S, device=DEV)
-    v = torch.zeros(S, device=DEV)
+    rows, grows = -(-S // E), -(-S // GE)
+    st = torch.zeros(L.state_len, device=DEV)
+    col = torch.zeros(rows * E, device=DEV)
+    col[:S] = master
+    st.view(rows, 3, E)[:, 0, :].copy_(col.view(rows, E))
+    del col
     own = torch.empty(S, dtype=torch.int16, device=DEV)
     p_h = master[tidx].cpu().numpy()
+    del master
     m_h = np.zeros(idx.size, np.float32)
     v_h = np.zeros(idx.size, np.float32)
     par_h = np.empty(idx.size, np.uint16)
     for t in range(w.steps):
-        grads = [grad_bits(w, t, q, S, device=DEV) for q in range(n)]
-        samp = [host_bf16(gq[tidx]) for gq in grads]
-        zs.adam_step(L, 0, 1, cfg_of(w, t + 1), master, m, v, own, zs.INDEX_SHARD,
-                     grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
-        del grads
+        gbuf = torch.zeros(L.grad_len(GE), dtype=torch.int16, device=DEV)
+        col = torch.zeros(grows * GE, dtype=torch.int16, device=DEV)
+        samp = []
+        for q in range(n):
+            col[:S] = grad_bits(w, t, q, S, device=DEV)
+            samp.append(host_bf16(col[tidx]))
+            gbuf.view(grows, n, GE)[:, q, :].copy_(col.view(grows, GE))
+        del col
+        zs.adam_step(L, 0, 1, cfg_of(w, t + 1), *L.state_views(st), own, zs.INDEX_SHARD,
+                     grads=zs.Grads.chunked(gbuf, n, GE))
+        torch.cuda.synchronize()
+        del gbuf
         _c.rank_step(oracle_cfg(w).hparams(t + 1), samp, 1.0, p_h, m_h, v_h, par_h)
     torch.cuda.synchronize()
-    assert_f32_close(host_f32(master[tidx]), p_h, "config 2 master")
-    assert_f32_close(host_f32(m[tidx]), m_h, "config 2 m")
-    assert_f32_close(host_f32(v[tidx]), v_h, "config 2 v")
+    assert_f32_close(host_f32(st[pos]), p_h, "config 2 master")
+    assert_f32_close(host_f32(st[pos + E]), m_h, "config 2 m")
+    assert_f32_close(host_f32(st[pos + 2 * E]), v_h, "config 2 v")
     assert_bf16_equal(host_bf16(own[tidx]), par_h, "config 2 bf16 shard")
     # all-gather data movement into the full 7.24e9-element buffer: random
     # peer shards, every slot at the sampled positions and its edges
@@ -532,8 +664,9 @@ def test_config2_full_shard_every_element():
     3 fused Adam steps), compared element by element over the whole shard:
     the oracle steps every element from the same gradients, streamed from
     the GPU in 32M-element chunks, and master, m, v and the bf16 shard must
-    be bit-identical everywhere -- for three state arrays and for the
-    chunked state the benchmark times, side by side."""
+    be bit-identical everywhere -- for three state arrays with eight rank
+    buffers, and side by side for the benchmark's launch: the chunked state
+    and the rank gradients chunked into one buffer."""
     w = WORKLOADS[2]
     n, r = w.n_ranks, w.n_ranks - 1
     L = zs.shard_init("zero3", n, r, list(w.units))
@@ -558,20 +691,28 @@ def test_config2_full_shard_every_element():
     v_h = np.zeros(S, np.float32)
     par_h = np.empty(S, np.uint16)
     tmp = np.empty(CH, np.float32)
+    GE = zs.GRAD_CHUNK_DEFAULT
+    grows = -(-S // GE)
     for t in range(w.steps):
         grads = [grad_bits(w, t, q, S, device=DEV) for q in range(n)]
         G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
         zs.adam_step(L, 0, 1, cfg_of(w, t + 1), master, m, v, own, zs.INDEX_SHARD, grads=G)
+        gbuf = torch.zeros(LC.grad_len(GE), dtype=torch.int16, device=DEV)
+        col = torch.zeros(grows * GE, dtype=torch.int16, device=DEV)
+        for q in range(n):
+            col[:S] = grads[q]
+            gbuf.view(grows, n, GE)[:, q, :].copy_(col.view(grows, GE))
+        del col
         zs.adam_step(LC, 0, 1, cfg_of(w, t + 1), *LC.state_views(st_c), own_c, zs.INDEX_SHARD,
-                     grads=G)
+                     grads=zs.Grads.chunked(gbuf, n, GE))
         hp = oracle_cfg(w).hparams(t + 1)
         for off in range(0, S, CH):
             k = min(CH, S - off)
             g = [host_bf16(gq[off:off + k]) for gq in grads]
             _c.rank_step(hp, g, 1.0, p_h[off:off + k], m_h[off:off + k], v_h[off:off + k],
                          par_h[off:off + k], tmp[:k])
-        del grads, G
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        del grads, G, gbuf
     bad = {}
     for name, dev_t, want in (("master", master, p_h), ("m", m, m_h), ("v", v, v_h)):
         nbad = 0
@@ -587,8 +728,8 @@ def test_config2_full_shard_every_element():
         for name, x, want in zip(("master", "m", "v"), got, (p_h, m_h, v_h)):
             nbad[name] += int(np.count_nonzero(x.view(np.uint32) !=
                                                want[off:off + k].view(np.uint32)))
-    bad.update({f"chunked {k}": x for k, x in nbad.items()})
-    for name, o in (("bf16 shard", own), ("chunked-state bf16 shard", own_c)):
+    bad.update({f"chunked state and gradients: {k}": x for k, x in nbad.items()})
+    for name, o in (("bf16 shard", own), ("chunked state and gradients: bf16 shard", own_c)):
         nb = 0
         for off in range(0, S, CH):
             nb += int(np.count_nonzero(host_bf16(o[off:off + CH]) != par_h[off:off + CH]))

@@ -46,13 +46,27 @@ def _state(L, master0, E):
     return list(L.state_views(buf)) + [buf]
 
 
-def _both_paths(strategy, units, n, r, cfg_id, max_norm, steps, state_chunk=0):
+def _both_paths(strategy, units, n, r, cfg_id, max_norm, steps, state_chunk=0, grad_chunk=0):
     from fsdp_sharded_optimizer_shard_amd import zs
     w, L, grads, master0 = _case(strategy, units, n, r, cfg_id)
     if state_chunk:
         L = L.chunk_state(state_chunk)
     U, P, S = len(units), L.flat_len, L.shard_len
     G = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
+    if grad_chunk:
+        # rank q's shard slices, chunked into one buffer (rows of grad_chunk
+        # elements per rank)
+        E = grad_chunk
+        rows = -(-S // E)
+        owned = torch.cat([torch.arange(L.query(u)["rank_flat_off"],
+                                        L.query(u)["rank_flat_off"] + L.query(u)["shard_len"])
+                           for u in range(U)]).to(DEV)
+        gbuf = torch.zeros(L.grad_len(E), dtype=torch.int16, device=DEV)
+        col = torch.zeros(rows * E, dtype=torch.int16, device=DEV)
+        for q in range(n):
+            col[:S] = grads[q][owned]
+            gbuf.view(rows, n, E)[:, q, :].copy_(col.view(rows, E))
+        G = zs.Grads.chunked(gbuf, n, E)
     out = {}
     for path in ("three_calls", "noalloc"):
         st = _state(L, master0, state_chunk)
@@ -91,6 +105,19 @@ def test_two_calls_in_a_row_match_the_three_call_path():
             got = res["noalloc"][k]
             nbad = int(np.count_nonzero(got != want))
             assert nbad == 0, f"{name}: {k}: {nbad} of {want.size} differ"
+
+
+def test_chunked_gradients_call_matches_the_three_call_path():
+    # the rank gradients chunked into one buffer, on a chunked state and on
+    # three arrays
+    for E in (1024, 0):
+        res = _both_paths("zero3", [20_000, 333, 4099], 8, 5, 24, 0.005, steps=2, state_chunk=E,
+                          grad_chunk=512)
+        assert res["coef"] < 1.0
+        for k, want in res["three_calls"].items():
+            got = res["noalloc"][k]
+            nbad = int(np.count_nonzero(got != want))
+            assert nbad == 0, f"chunked gradients, state chunk {E}: {k}: {nbad} of {want.size} differ"
 
 
 def test_chunked_state_call_matches_the_three_call_path():
