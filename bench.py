@@ -82,9 +82,10 @@ def parse():
                          "chunks (zero_layout_chunk_state); 0 keeps three arrays; default: "
                          "the library's ZERO_STATE_CHUNK_DEFAULT")
     ap.add_argument("--grad-chunk", type=int, default=None, metavar="E",
-                    help="the headline's 8 shard-indexed rank gradients as one buffer of rows "
-                         "of E elements per rank (zero_grads.chunk); 0 keeps 8 buffers; "
-                         "default: the library's ZERO_GRAD_CHUNK_DEFAULT")
+                    help="the shard-indexed rank gradients of the 7B step (and of each unit of "
+                         "--config 4) as one receive buffer of rows of E elements per rank "
+                         "(zero_grads.chunk); 0 keeps one buffer per rank; default: the "
+                         "library's ZERO_GRAD_CHUNK_DEFAULT")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
@@ -205,19 +206,20 @@ def state_desc(E):
 
 
 class RankGrads:
-    """The N ranks' shard-indexed bf16 gradients for one shard: N buffers, or
-    one buffer of rows of E elements per rank (rank q's element i at
+    """The N ranks' shard-indexed bf16 gradients of S elements each (a
+    shard, or the largest unit's slice for per-unit calls): N buffers, or
+    one receive buffer of rows of E elements per rank (rank q's element i at
     (i // E) N E + q E + i % E), the chunked format zero_grads.chunk names."""
 
-    def __init__(self, torch, zs, L, draws, E):
-        self.zs, self.E, self.N, self.S = zs, E, len(draws), L.shard_len
+    def __init__(self, torch, zs, draws, E):
+        self.zs, self.E, self.N, self.S = zs, E, len(draws), draws[0].numel()
         self._grads = None
         if E == 0:
             self.bufs, self.buf = list(draws), None
             return
         rows, dev = -(-self.S // E), draws[0].device
         self.bufs = None
-        self.buf = torch.zeros(L.grad_len(E), dtype=torch.int16, device=dev)
+        self.buf = torch.zeros(rows * self.N * E, dtype=torch.int16, device=dev)
         cells = self.buf.view(rows, self.N, E)
         col = torch.zeros(rows * E, dtype=torch.int16, device=dev)
         for q, d in enumerate(draws):
@@ -270,7 +272,8 @@ def headline_buffers(torch, zs, w, L, S, N, r, dev, rank_peers=True, grad_chunk=
     """A fresh allocation of the headline step's buffers (one placement)."""
     from synthetic import grad_bits, master_init
     draws = [grad_bits(w, 0, q, S, device=dev) for q in range(N)]
-    grads = RankGrads(torch, zs, L, draws, grad_chunk)
+    grads = RankGrads(torch, zs, draws, grad_chunk)
+    assert grad_chunk == 0 or grads.buf.numel() == L.grad_len(grad_chunk)
     del draws
     st = State(torch, L, master_init(w, S, device=dev, rank=r))
     full = torch.empty(L.flat_len, dtype=torch.int16, device=dev)
@@ -719,11 +722,13 @@ def run_fsdp70b(args, torch, zs, np):
     N, r = w.n_ranks, w.n_ranks - 1
     units = list(w.units)
     L = zs.shard_init("fsdp", N, r, units).chunk_state(state_chunk(args, zs))
-    S, SE = L.shard_len, L.state_chunk
+    S, SE, GE = L.shard_len, L.state_chunk, grad_chunk(args, zs)
     q = [L.query(u) for u in range(len(units))]
     smax = max(x["shard_len"] for x in q)
-    grads = [grad_bits(w, 0, k, smax, device=dev) for k in range(N)]
-    G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+    # one set of unit receive buffers, sized for the largest unit and
+    # reused by every unit (each reads the first s_u elements per rank)
+    rg = RankGrads(torch, zs, [grad_bits(w, 0, k, smax, device=dev) for k in range(N)], GE)
+    G = rg.grads
     st = State(torch, L, torch.empty(S, device=dev).normal_(0, 0.02))
     master, m, v = st.views
     full_unit = torch.empty(N * smax, dtype=torch.int16, device=dev)
@@ -762,13 +767,14 @@ def run_fsdp70b(args, torch, zs, np):
     if not args.one_stream:
         variants.append(("sweep_two_streams_cap2", 2, gstream, ring))
     for label, cap, gs, bufs in variants:
-        ios = [(grads, peer_list, bufs[u % len(bufs)]) for u in range(len(units))]
+        ios = [(rg.ptrs, peer_list, bufs[u % len(bufs)]) for u in range(len(units))]
 
         def sweep_step(ph, cap=cap, gs=gs, ios=ios):
             t[0] += 1
             cfg = zs.adam_cfg(step=t[0])
             phase(ph, "sweep", lambda: zs.fsdp_sweep(L, 0, len(units), cfg, zs.BF16, ios, master,
-                                                     m, v, cap, gather_stream=gs))
+                                                     m, v, cap, gather_stream=gs,
+                                                     grad_chunk=GE))
         sms, _ = timed(args, torch, sweep_step)
         sweeps[label] = {"ms_per_step": sms, "shard_params_per_s": S / (sms * 1e-3),
                          "gbps": (fb + gb) / (sms * 1e-3) / 1e9}
@@ -779,7 +785,7 @@ def run_fsdp70b(args, torch, zs, np):
                     "rank grads + Adam + bf16 into the unit buffer, gather of 63 peers); value "
                     "is the faster zero_fsdp_sweep variant",
                     psi=w.psi, n_ranks=N, rank=r, shard_elems=S, units=len(units),
-                    state_layout=state_desc(SE))
+                    state_layout=state_desc(SE), grad_layout="per unit: " + grad_desc(GE, N))
     out["per_unit_calls_ms_per_step"] = ms
     out["sweeps"] = sweeps
     out["kernels"] = kern
@@ -790,7 +796,7 @@ def run_fsdp70b(args, torch, zs, np):
     if args.cpu_baseline_seconds > 0:
         # one layer unit x 64 ranks on the CPU, extrapolated to the 81 units
         s0 = q[0]["shard_len"]
-        out["cpu_baseline"] = cpu_baseline(w, grads, st.master, s0, r,
+        out["cpu_baseline"] = cpu_baseline(w, rg.ranks(), st.master, s0, r,
                                            args.cpu_baseline_seconds,
                                            what="rank-{r} shard of layer unit 0", total=S)
     return out

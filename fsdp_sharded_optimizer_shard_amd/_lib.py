@@ -121,10 +121,10 @@ class _UnitIO(ctypes.Structure):
                 ("peer_shards", ctypes.POINTER(ctypes.c_void_p)), ("unit_full", _P)]
 
 
-_lib.zero_fsdp_sweep.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _I32,
+_lib.zero_fsdp_sweep.argtypes = [_P, _I32, _I32, ctypes.POINTER(AdamCfg), _I32, _I32,
                                  ctypes.POINTER(_UnitIO), _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_sweep.restype = _I32
-_lib.zero_fsdp_sweep_table.argtypes = [_P, _I32, _I32, _P, _I64, _P, _I32,
+_lib.zero_fsdp_sweep_table.argtypes = [_P, _I32, _I32, _P, _I64, _P, _I32, _I32,
                                        ctypes.POINTER(_UnitIO), _P, _P, _P, _I32, _P, _P]
 _lib.zero_fsdp_sweep_table.restype = _I32
 _lib.zero_gemm_bf16.argtypes = [_I64, _I64, _I64, _P, _I64, _I32, _P, _I64, _I32, _P, _I64, _I32,
@@ -343,29 +343,34 @@ class Layout:
     def state_count(self, unit_begin: int, unit_end: int):
         """Floats each of master, m and v must hold from its pointer for a
         call over [unit_begin, unit_end), or None for a range the library
-        will refuse."""
-        return self._chunked_count(unit_begin, unit_end, self.state_chunk, 3)
-
-    def grad_count(self, unit_begin: int, unit_end: int, chunk: int):
-        """Elements each rank's pointer into chunked gradients (chunk E) must
-        reach for a call over [unit_begin, unit_end); None as above."""
-        return self._chunked_count(unit_begin, unit_end, chunk, self.info()["world_n"])
-
-    def grad_len(self, chunk: int) -> int:
-        """Elements of one buffer holding all N ranks' gradients for this
-        shard in chunks of `chunk` (ceil(S / E) rows of N chunks)."""
-        E, N = chunk, self.info()["world_n"]
-        return -(-self.shard_len // E) * N * E
-
-    def _chunked_count(self, unit_begin, unit_end, E, k):
-        # a buffer of rows of k chunks of E elements, addressed by absolute
-        # shard index i at (i // E) k E + i % E from each pointer
+        will refuse.  A chunked state is addressed by absolute shard index."""
         shard, _ = self.range_lens(unit_begin, unit_end)
+        E = self.state_chunk
         if shard is None or E == 0 or shard == 0:
             return shard
         last = self._unit_table()[unit_end - 1]
         i = last["shard_off"] + last["shard_len"] - 1     # highest shard index touched
-        return (i // E) * k * E + i % E + 1
+        return (i // E) * 3 * E + i % E + 1
+
+    def grad_count(self, unit_begin: int, unit_end: int, chunk: int):
+        """Elements each rank's pointer into chunked gradients (chunk E) must
+        reach for a call over [unit_begin, unit_end): the range's last
+        element i sits at (i // E) N E + i % E (None as above)."""
+        shard, _ = self.range_lens(unit_begin, unit_end)
+        if shard is None or chunk == 0 or shard == 0:
+            return shard
+        i, E = shard - 1, chunk
+        return (i // E) * self.info()["world_n"] * E + i % E + 1
+
+    def grad_len(self, chunk: int, unit_begin: int = 0, unit_end: Optional[int] = None) -> int:
+        """Elements of one buffer holding all N ranks' gradients for the
+        range's part of this shard (the whole shard by default) in chunks of
+        `chunk`: ceil(S / E) rows of N chunks."""
+        ue = self.info()["n_units"] if unit_end is None else unit_end
+        shard, _ = self.range_lens(unit_begin, ue)
+        if shard is None:
+            raise ValueError(f"unit range [{unit_begin}, {ue}) is outside the layout")
+        return -(-shard // chunk) * self.info()["world_n"] * chunk
 
     @property
     def flat_len(self) -> int:
@@ -579,7 +584,8 @@ def _need_len(what: str, seq, n: int) -> None:
         raise ValueError(f"{what}: expected {n} entries, got {len(seq)}")
 
 
-def _unit_ios(layout: Layout, unit_begin: int, unit_end: int, units, grad_dtype=BF16):
+def _unit_ios(layout: Layout, unit_begin: int, unit_end: int, units, grad_dtype=BF16,
+              grad_chunk=0):
     if 0 <= unit_begin <= unit_end:
         _need_len("units", units, unit_end - unit_begin)
         n, parts = layout.info()["world_n"], _parts(layout)
@@ -588,10 +594,12 @@ def _unit_ios(layout: Layout, unit_begin: int, unit_end: int, units, grad_dtype=
             _need_len("rank_grads", grads, n)
             _need_len("peer_shards", peers, parts)
             if unit_begin + i < len(table):
-                q = table[unit_begin + i]
+                u = unit_begin + i
+                q = table[u]
+                count = (layout.grad_count(u, u + 1, grad_chunk) if grad_chunk else
+                         q["shard_len"])
                 for k, x in enumerate(grads):
-                    _need(x, f"unit {unit_begin + i} gradient of rank {k}", q["shard_len"],
-                          _kind(grad_dtype))
+                    _need(x, f"unit {u} gradient of rank {k}", count, _kind(grad_dtype))
                 for k, x in enumerate(peers):
                     _need(x, f"unit {unit_begin + i} shard of rank {k}", q["shard_len"], "bf16")
                 _need(full, f"unit {unit_begin + i} buffer", q["padded_len"], "bf16")
@@ -607,28 +615,30 @@ def _unit_ios(layout: Layout, unit_begin: int, unit_end: int, units, grad_dtype=
 
 def fsdp_sweep(layout: Layout, unit_begin: int, unit_end: int, cfg: AdamCfg, grad_dtype: int,
                units, master, m, v, max_inflight: int = 2, step_stream=None,
-               gather_stream=None) -> None:
+               gather_stream=None, grad_chunk: int = 0) -> None:
     """units: one (rank_grads, peer_shards, unit_full) per unit of the range;
     rank_grads are world_n buffers and peer_shards one per slice (world_n,
     or 1 under DDP; None allowed).  gather_stream defaults to step_stream
-    (sequential)."""
-    arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype)
+    (sequential).  grad_chunk E > 0: every unit's rank_grads are the
+    pointers of one chunked receive buffer over the shard (Grads.chunked)."""
+    arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype, grad_chunk)
     sc = layout.state_count(unit_begin, unit_end)
     for name, x in (("master", master), ("m", m), ("v", v)):
         _need(x, name, sc, "fp32")
     ss = _stream(step_stream)
     gs = ss if gather_stream is None else _stream(gather_stream)
     _check(_lib.zero_fsdp_sweep(layout.handle, unit_begin, unit_end, ctypes.byref(cfg), grad_dtype,
-                                arr, _addr(master), _addr(m), _addr(v), max_inflight, ss, gs),
+                                grad_chunk, arr, _addr(master), _addr(m), _addr(v), max_inflight,
+                                ss, gs),
            "zero_fsdp_sweep")
 
 
 def fsdp_sweep_table(layout: Layout, unit_begin: int, unit_end: int, table, n_entries: int,
                      step_counter, grad_dtype: int, units, master, m, v, max_inflight: int = 2,
-                     step_stream=None, gather_stream=None) -> None:
+                     step_stream=None, gather_stream=None, grad_chunk: int = 0) -> None:
     """fsdp_sweep with the step scalars of table[*step_counter - 1] (device
     table and counter); advances the counter once, after the last unit."""
-    arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype)
+    arr, keep = _unit_ios(layout, unit_begin, unit_end, units, grad_dtype, grad_chunk)
     sc = layout.state_count(unit_begin, unit_end)
     for name, x in (("master", master), ("m", m), ("v", v)):
         _need(x, name, sc, "fp32")
@@ -637,7 +647,8 @@ def fsdp_sweep_table(layout: Layout, unit_begin: int, unit_end: int, table, n_en
     ss = _stream(step_stream)
     gs = ss if gather_stream is None else _stream(gather_stream)
     _check(_lib.zero_fsdp_sweep_table(layout.handle, unit_begin, unit_end, _addr(table),
-                                      n_entries, _addr(step_counter), grad_dtype, arr,
+                                      n_entries, _addr(step_counter), grad_dtype, grad_chunk,
+                                      arr,
                                       _addr(master), _addr(m), _addr(v), max_inflight, ss, gs),
            "zero_fsdp_sweep_table")
 

@@ -42,4 +42,9 @@ zero_status check_range(const zero_layout *L, int32_t unit_begin, int32_t unit_e
 zero_status check_state(const zero_layout *L, const float *master, const float *m,
                         const float *v);
 
+// Checks a call's rank gradient buffers against the layout: count, dtype,
+// pointers, index modes and, for chunked gradients, the chunk and the
+// pointers one chunk apart.
+zero_status check_grads(const zero_layout *L, const zero_grads *g);
+
 }  // namespace zs

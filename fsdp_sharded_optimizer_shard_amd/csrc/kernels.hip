@@ -105,7 +105,6 @@ struct StepArgs {
     int64_t st_base;     // chunked state: shard index of the range's first element
     int32_t st_shift;    // 0: three state arrays; else log2 of the state chunk
     int32_t g_shift;     // 0: one buffer per rank; else log2 of the gradient chunk
-    int64_t g_base;      // chunked gradients: shard index of the range's first element
     const float *gin;    // kApply: averaged gradient
     int32_t gin_full;    // kApply: 1 if gin is full-indexed, 0 if shard-indexed
     int32_t _pad2;
@@ -225,16 +224,15 @@ __device__ __forceinline__ int64_t st_at(const StepArgs &a, int64_t si)
 
 // Offset of shard element `si` (relative to the range) in a shard-indexed
 // rank gradient.  One buffer per rank: si itself.  Chunked gradients (chunk
-// E = 2^g_shift, N ranks in one buffer): element i = g_base + si of rank q
-// sits at (i / E) N E + i % E from rank q's pointer, which is rank 0's + qE.
-// As for the state, a 4-aligned group never crosses a chunk.
+// E = 2^g_shift, N ranks in one buffer): element si of rank q sits at
+// (si / E) N E + si % E from rank q's pointer, which is rank 0's + qE.  A
+// group of 4 at a 4-aligned si never crosses a chunk.
 __device__ __forceinline__ int64_t g_at(const StepArgs &a, int n, int64_t si)
 {
     if (a.g_shift == 0)
         return si;
-    const int64_t i = a.g_base + si;
     const int sh = a.g_shift;
-    return ((i >> sh) * n << sh) + (i & (((int64_t)1 << sh) - 1));
+    return ((si >> sh) * n << sh) + (si & (((int64_t)1 << sh) - 1));
 }
 
 // Sum of the N rank gradients for G groups of 4 consecutive elements, group
@@ -804,9 +802,8 @@ zero_status for_each_chunk(int32_t ub, int32_t ue, F fn)
 
 // Fills the segment table for units [u0, u1) of a call whose range starts
 // at `ub`; returns the number of tiles.  `abs_index`: the launch addresses a
-// chunked state or chunked gradients by absolute shard index, so a slice
-// takes the vector path only if its absolute shard offset is a multiple of 4
-// as well.
+// chunked state by absolute shard index, so a slice takes the vector path
+// only if its absolute shard offset is a multiple of 4 as well.
 int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg *seg,
                   int32_t *n_segs, bool abs_index = false)
 {
@@ -828,6 +825,8 @@ int64_t fill_segs(const zero_layout *L, int32_t ub, int32_t u0, int32_t u1, Seg 
     *n_segs = k;
     return tiles;
 }
+
+}  // namespace
 
 zero_status check_grads(const zero_layout *L, const zero_grads *g)
 {
@@ -877,15 +876,13 @@ zero_status check_grads(const zero_layout *L, const zero_grads *g)
     return ZERO_OK;
 }
 
-// The rank buffers of a call whose range starts at unit `ub`.
-void fill_grads(const zero_layout *L, int32_t ub, const zero_grads *g, StepArgs &a,
-                bool &all_aligned)
+namespace {
+
+void fill_grads(const zero_grads *g, StepArgs &a, bool &all_aligned)
 {
     a.n_ranks = g->n;
-    if (g->chunk) {
+    if (g->chunk)
         a.g_shift = __builtin_ctz((unsigned)g->chunk);
-        a.g_base = L->shard_off[ub];
-    }
     a.full_mask = 0;
     for (int q = 0; q < g->n; ++q) {
         a.grads[q] = g->ptrs[q];
@@ -1040,11 +1037,11 @@ zero_status adam_launch(const zero_layout *L, int32_t ub, int32_t ue, const Adam
         std::memset(&a, 0, sizeof a);
         bool al = aligned16(master) && aligned16(m) && aligned16(v) && aligned16(param_out);
         if (grads)
-            fill_grads(L, ub, grads, a, al);
+            fill_grads(grads, a, al);
         else
             al = al && aligned16(grad_fp32);
         a.vec_ptrs = al;
-        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs, E > 0 || (grads && grads->chunk));
+        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs, E > 0);
         if (a.n_tiles == 0)
             return ZERO_OK;
         a.master = master;
@@ -1161,9 +1158,9 @@ zero_status zero_reduce_shard(const zero_layout *L, int32_t ub, int32_t ue,
         StepArgs a;
         std::memset(&a, 0, sizeof a);
         bool al = aligned16(out);
-        fill_grads(L, ub, grads, a, al);
+        fill_grads(grads, a, al);
         a.vec_ptrs = al;
-        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs, grads->chunk != 0);
+        a.n_tiles = fill_segs(L, ub, u0, u1, a.seg, &a.n_segs);
         if (a.n_tiles == 0)
             return ZERO_OK;
         a.gout = out;

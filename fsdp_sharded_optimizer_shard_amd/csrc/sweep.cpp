@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <string>
 #include <vector>
 
 #include "internal.h"
@@ -53,7 +54,7 @@ zero_status hip_check(hipError_t e, const char *what)
 // the last unit's step.
 template <typename StepUnit, typename Finish>
 zero_status sweep(const zero_layout *L, int32_t ub, int32_t ue, int32_t grad_dtype,
-                  const zero_unit_io *io, float *master, float *m, float *v,
+                  int32_t grad_chunk, const zero_unit_io *io, float *master, float *m, float *v,
                   int32_t max_inflight, void *step_stream, void *gather_stream,
                   StepUnit step_unit, Finish finish)
 {
@@ -100,6 +101,11 @@ zero_status sweep(const zero_layout *L, int32_t ub, int32_t ue, int32_t grad_dty
         if (L->parts > 1 && x.peer_shards[L->rank])
             return zs::fail(ZERO_ERR_INVALID_ARG, "unit %d: this rank's own peer_shards entry "
                             "must be NULL (the step writes that slice)", u);
+        const zero_grads g{x.rank_grads, nullptr, n, grad_dtype, ZERO_INDEX_SHARD, grad_chunk};
+        if ((st = zs::check_grads(L, &g)) != ZERO_OK) {
+            const std::string why = zero_last_error();
+            return zs::fail(st, "unit %d: %s", u, why.c_str());
+        }
     }
     const hipStream_t ss = static_cast<hipStream_t>(step_stream);
     const hipStream_t gs = static_cast<hipStream_t>(gather_stream);
@@ -115,7 +121,7 @@ zero_status sweep(const zero_layout *L, int32_t ub, int32_t ue, int32_t grad_dty
             (st = hip_check(hipStreamWaitEvent(ss, gathered.ev[k - max_inflight], 0),
                             "hipStreamWaitEvent")) != ZERO_OK)
             return st;
-        const zero_grads g{x.rank_grads, nullptr, n, grad_dtype, ZERO_INDEX_SHARD, 0};
+        const zero_grads g{x.rank_grads, nullptr, n, grad_dtype, ZERO_INDEX_SHARD, grad_chunk};
         // three state arrays: the unit's step gets them from the unit's
         // first element; a chunked state is always passed from its start
         const int64_t so = L->state_chunk ? 0 : L->shard_off[u] - L->shard_off[ub];
@@ -144,13 +150,14 @@ zero_status sweep(const zero_layout *L, int32_t ub, int32_t ue, int32_t grad_dty
 
 extern "C" zero_status zero_fsdp_sweep(const zero_layout *L, int32_t ub, int32_t ue,
                                        const zero_adam_cfg *cfg, int32_t grad_dtype,
-                                       const zero_unit_io *io, float *master, float *m, float *v,
+                                       int32_t grad_chunk, const zero_unit_io *io,
+                                       float *master, float *m, float *v,
                                        int32_t max_inflight, void *step_stream,
                                        void *gather_stream)
 {
     if (!cfg)
         return zs::fail(ZERO_ERR_INVALID_ARG, "cfg is required");
-    return sweep(L, ub, ue, grad_dtype, io, master, m, v, max_inflight, step_stream,
+    return sweep(L, ub, ue, grad_dtype, grad_chunk, io, master, m, v, max_inflight, step_stream,
                  gather_stream,
                  [&](int32_t u, const zero_grads &g, int64_t so, uint16_t *full) {
                      return zero_adam_step(L, u, u + 1, cfg, nullptr, ZERO_INDEX_SHARD, nullptr,
@@ -163,7 +170,8 @@ extern "C" zero_status zero_fsdp_sweep(const zero_layout *L, int32_t ub, int32_t
 extern "C" zero_status zero_fsdp_sweep_table(const zero_layout *L, int32_t ub, int32_t ue,
                                              const zero_adam_table_entry *table,
                                              int64_t n_entries, int64_t *step_counter,
-                                             int32_t grad_dtype, const zero_unit_io *io,
+                                             int32_t grad_dtype, int32_t grad_chunk,
+                                             const zero_unit_io *io,
                                              float *master, float *m, float *v,
                                              int32_t max_inflight, void *step_stream,
                                              void *gather_stream)
@@ -173,7 +181,7 @@ extern "C" zero_status zero_fsdp_sweep_table(const zero_layout *L, int32_t ub, i
                         "required");
     if (reinterpret_cast<uintptr_t>(table) % 4 || reinterpret_cast<uintptr_t>(step_counter) % 8)
         return zs::fail(ZERO_ERR_ALIGNMENT, "misaligned step table or counter");
-    return sweep(L, ub, ue, grad_dtype, io, master, m, v, max_inflight, step_stream,
+    return sweep(L, ub, ue, grad_dtype, grad_chunk, io, master, m, v, max_inflight, step_stream,
                  gather_stream,
                  [&](int32_t u, const zero_grads &g, int64_t so, uint16_t *full) {
                      return zero_adam_step_table(L, u, u + 1, table, n_entries, step_counter,

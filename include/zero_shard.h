@@ -116,12 +116,13 @@ typedef struct zero_layout zero_layout;
    uint16 bit patterns, or fp32).
 
    Chunked gradients (chunk = E > 0): the N shard-indexed contributions to
-   this rank's shard sit in one buffer of ceil(S/E) rows, each row holding
-   E elements of rank 0, then E of rank 1, ..., then E of rank N-1 (S = the
-   shard length).  Rank q's gradient for shard element i (counted from the
-   shard's first element, whatever the call's range) is at
-   ptrs[0] + (i / E) N E + q E + i % E; ptrs[q] must be ptrs[0] + qE
-   elements and every rank shard-indexed (ZERO_ERR_INVALID_ARG otherwise).
+   this rank's part of the call's range sit in one buffer of ceil(S/E) rows,
+   each row holding E elements of rank 0, then E of rank 1, ..., then E of
+   rank N-1 (S = the range's shard length).  Rank q's gradient for element i
+   of the range (counted from its first element, as for every shard-indexed
+   buffer) is at ptrs[0] + (i / E) N E + q E + i % E; ptrs[q] must be
+   ptrs[0] + qE elements and every rank shard-indexed (ZERO_ERR_INVALID_ARG
+   otherwise).  A per-unit call therefore takes a per-unit receive buffer.
    The same bytes and sums as N separate buffers, read from one region
    instead of N: it is the receive buffer a rank would let its peers fill
    in a reduce-scatter.  On one MI355X the 7B / N = 8 fused step (state
@@ -420,7 +421,10 @@ typedef struct zero_unit_io {
     const void *const *rank_grads;      /* host array of world_n device pointers:
                                            this unit's rank gradients, each
                                            indexed over this rank's slice of the
-                                           unit (s_u elements, unit-local)     */
+                                           unit (s_u elements, unit-local); or,
+                                           with grad_chunk > 0, the pointers of
+                                           this unit's chunked receive buffer
+                                           (zero_grads.chunk)                  */
     const uint16_t *const *peer_shards; /* host array of world_n device pointers
                                            (s_u bf16 each) gathered into the
                                            unit buffer; NULL entries skipped,
@@ -452,10 +456,14 @@ typedef struct zero_unit_io {
    to per-unit zero_adam_step + zero_gather_params calls.  Host-side errors
    launch nothing; a HIP error part-way returns ZERO_ERR_HIP with the units
    before it enqueued.  `io` is a host array of (unit_end - unit_begin)
-   entries. */
+   entries.  grad_chunk = 0 takes each unit's rank gradients as world_n
+   buffers; E > 0 as one chunked receive buffer per unit, as
+   zero_grads.chunk describes, checked for every unit before anything is
+   launched. */
 zero_status zero_fsdp_sweep(const zero_layout *layout, int32_t unit_begin,
                             int32_t unit_end, const zero_adam_cfg *cfg,
-                            int32_t grad_dtype, const zero_unit_io *io,
+                            int32_t grad_dtype, int32_t grad_chunk,
+                            const zero_unit_io *io,
                             float *master, float *m, float *v,
                             int32_t max_inflight, void *step_stream,
                             void *gather_stream);
@@ -468,7 +476,8 @@ zero_status zero_fsdp_sweep(const zero_layout *layout, int32_t unit_begin,
 zero_status zero_fsdp_sweep_table(const zero_layout *layout, int32_t unit_begin,
                                   int32_t unit_end, const zero_adam_table_entry *table,
                                   int64_t n_entries, int64_t *step_counter,
-                                  int32_t grad_dtype, const zero_unit_io *io,
+                                  int32_t grad_dtype, int32_t grad_chunk,
+                                  const zero_unit_io *io,
                                   float *master, float *m, float *v,
                                   int32_t max_inflight, void *step_stream,
                                   void *gather_stream);

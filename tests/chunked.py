@@ -23,15 +23,15 @@ def state_buffer(L, master):
     return buf
 
 
-def grad_buffer(L, n, E, draw, tidx=None):
-    """One buffer of layout L's shard gradients for n ranks in chunks of E
-    (Layout.grad_len long) filled with draw(q), a device int16 tensor of
-    shard length, for each rank q; and, with tidx (a device index tensor),
-    each rank's values at those shard positions as host uint16 arrays."""
-    S = L.shard_len
+def grad_buffer(S, n, E, draw, tidx=None):
+    """One receive buffer of S elements per rank for n ranks in chunks of E
+    (ceil(S / E) rows of n chunks, as Layout.grad_len counts) filled with
+    draw(q), a device int16 tensor of S elements, for each rank q; and,
+    with tidx (a device index tensor), each rank's values at those
+    positions as host uint16 arrays."""
     rows = -(-S // E)
     first = draw(0)
-    buf = torch.zeros(L.grad_len(E), dtype=torch.int16, device=first.device)
+    buf = torch.zeros(rows * n * E, dtype=torch.int16, device=first.device)
     col = torch.zeros(rows * E, dtype=torch.int16, device=first.device)
     samples = []
     for q in range(n):

@@ -101,7 +101,7 @@ def test_bench_rank_grads_in_the_chunked_format(E):
     rng = np.random.default_rng(E)
     draws = [torch.from_numpy(rng.integers(-2 ** 15, 2 ** 15, S, dtype=np.int16))
              for _ in range(N)]
-    rg = bench.RankGrads(torch, zs, L, draws, E)
+    rg = bench.RankGrads(torch, zs, draws, E)
     if E:
         assert rg.buf.numel() == L.grad_len(E)
         i = np.arange(S)

@@ -775,10 +775,11 @@ def test_chunked_grads_counts_in_the_binding():
 
     E, N = 8, 4
     L = zs.shard_init("zero3", N, 1, [1000, 24])     # shard 250 + 6
-    assert L.grad_len(E) == 32 * N * E
-    # the last shard index touched, 255, sits at (255 // 8) 32 + 7 = 999
-    # from each rank's pointer, whatever the range
-    assert L.grad_count(0, 2, E) == 1000 and L.grad_count(1, 2, E) == 1000
+    assert L.grad_len(E) == 32 * N * E and L.grad_len(E, 1, 2) == N * E
+    # counted from the range's first element: the whole range's last, 255,
+    # sits at (255 // 8) 32 + 7 = 999 from each rank's pointer; unit 1 alone
+    # (6 elements) ends at 5
+    assert L.grad_count(0, 2, E) == 1000 and L.grad_count(1, 2, E) == 6
     assert L.grad_count(0, 1, E) == (249 // 8) * 32 + 249 % 8 + 1
     assert L.grad_count(1, 1, E) == 0 and L.grad_count(0, 3, E) is None
     whole = Dev(L.grad_len(E))
@@ -795,3 +796,25 @@ def test_chunked_grads_counts_in_the_binding():
     with pytest.raises(ValueError, match="gradient buffer of rank 3 holds 999 elements, "
                                          "the call touches 1000"):
         step(zs.Grads.chunked(Dev(L.grad_len(E) - 1), N, E))
+
+
+def test_sweep_checks_every_units_chunked_gradients_before_launching():
+    # unit 1's receive buffer has a pointer off by one element: refused as
+    # an argument error naming the unit, before unit 0 is launched (a launch
+    # here, with no GPU, would have failed with ZERO_ERR_HIP instead)
+    L, E = _layout(), 1024
+    cfg = zs.adam_cfg(step=1)
+    good = [FAKE + 2 * E * q for q in range(4)]
+    bad = good[:3] + [good[3] + 2]
+    peers = [FAKE, None, FAKE, FAKE]
+    units = [(good, peers, FAKE), (bad, peers, FAKE)]
+    e = _err(zs.fsdp_sweep, L, 0, 2, cfg, zs.BF16, units, FAKE, FAKE + 16, FAKE + 32, 2, 0, 0,
+             grad_chunk=E)
+    assert e.status == zs.ERR_INVALID_ARG and "unit 1: chunked gradients" in str(e)
+    e = _err(zs.fsdp_sweep, L, 0, 2, cfg, zs.BF16, [(good, peers, FAKE)] * 2, FAKE, FAKE + 16,
+             FAKE + 32, 2, 0, 0, grad_chunk=3)
+    assert e.status == zs.ERR_INVALID_ARG and "unit 0: grads->chunk" in str(e)
+    table = FAKE + 4096
+    e = _err(zs.fsdp_sweep_table, L, 0, 2, table, 4, FAKE + 8192, zs.BF16, units, FAKE,
+             FAKE + 16, FAKE + 32, 2, 0, 0, grad_chunk=E)
+    assert e.status == zs.ERR_INVALID_ARG and "unit 1: chunked gradients" in str(e)

@@ -117,7 +117,8 @@ def test_fsdp2_mistral7b_full_size_sampled():
     v_h = np.zeros(idx.size, np.float32)
     par_h = np.empty(idx.size, np.uint16)
     for t in range(w.steps):
-        gbuf, samp = grad_buffer(L, n, GE, lambda q: grad_bits(w, t, q, S, device=DEV), tidx)
+        gbuf, samp = grad_buffer(S, n, GE, lambda q: grad_bits(w, t, q, S, device=DEV), tidx)
+        assert gbuf.numel() == L.grad_len(GE)
         zs.adam_step(L, 0, len(shapes), zs.adam_cfg(step=t + 1), *L.state_views(st), own,
                      zs.INDEX_SHARD, grads=zs.Grads.chunked(gbuf, n, GE))
         torch.cuda.synchronize()

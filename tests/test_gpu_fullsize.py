@@ -13,7 +13,8 @@ benchmark uses (default launch width, whole-range or per-unit calls).
     sampled elements against the oracle, the accumulation sampled over the
     full buffer.
   * Llama-70B FSDP full shard (N = 64, 81 units, rank 63): per unit, reduce
-    64 rank gradients + Adam + cast into the unit's full buffer, then gather
+    64 rank gradients (one chunked receive buffer per unit, as the
+    benchmark times) + Adam + cast into the unit's full buffer, then gather
     the 63 peer shards; sampled elements of every unit against the oracle.
 
 Every workload keeps its fp32 master, m and v in the chunked state format
@@ -29,6 +30,7 @@ import pytest
 import torch
 
 from oracle import _c, strategies
+from chunked import grad_buffer
 from gather_check import assert_gathered
 from synthetic import KIND_MICRO, WORKLOADS, grad_bits, master_init, peer_bits
 
@@ -252,20 +254,24 @@ def test_config4_llama70b_fsdp_per_unit_sampled():
     peers = [peer_bits(w, q, smax, device=DEV) for q in range(n - 1)]
     rng = np.random.default_rng(4)
     cfg = cfg_of(w, 1)
+    GE = zs.GRAD_CHUNK_DEFAULT
     for u in range(len(units)):
         q = L.query(u)
         su, so = q["shard_len"], q["shard_off"]
-        grads = [grad_bits(w, 0, k, su, device=DEV, unit=u) for k in range(n)]
         idx = sample(rng, su, 4096, edge=64)
         tidx = torch.from_numpy(idx).to(DEV)
         pos = torch.from_numpy(chunk_pos(E, so + idx)).to(DEV)
-        samp = [host_bf16(g[tidx]) for g in grads]
+        # the unit's 64 rank gradients in one chunked receive buffer (the
+        # benchmark's launch), counted from the unit's first element
+        recv, samp = grad_buffer(su, n, GE, lambda k: grad_bits(w, 0, k, su, device=DEV, unit=u),
+                                 tidx)
+        assert recv.numel() == L.grad_len(GE, u, u + 1)
         p_h = host_f32(buf[pos]).copy()
         # a chunked state is passed from its start for every unit
         zs.adam_step(L, u, u + 1, cfg, *st, full_unit, zs.INDEX_FULL,
-                     grads=zs.Grads(grads, zs.BF16, zs.INDEX_SHARD))
+                     grads=zs.Grads.chunked(recv, n, GE))
         zs.gather_params(L, u, u + 1, peers + [None], full_unit)
-        del grads
+        del recv
         m_h = np.zeros(idx.size, np.float32)
         v_h = np.zeros(idx.size, np.float32)
         par_h = np.empty(idx.size, np.uint16)

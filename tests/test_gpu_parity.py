@@ -179,15 +179,20 @@ class GpuRanks:
                 full = _c.bf16_to_f32(full)
             xs.append(full if index_modes[q] == zs.INDEX_FULL else full[idx])
         if self.GE:
-            buf = chunk_grads(xs, self.GE)
-            assert buf.size == self.lays[r].grad_len(self.GE)
-            return dev_f32(buf) if dtype == zs.FP32 else dev_bf16(buf)
+            return xs          # host arrays; chunked per call by chunked_grads
         return [dev_f32(x) if dtype == zs.FP32 else dev_bf16(x) for x in xs]
+
+    def chunked_grads(self, xs, dtype, lo=0, hi=None):
+        """zs.Grads over one chunked receive buffer holding shard elements
+        [lo, hi) of every rank's shard-indexed gradient."""
+        buf = chunk_grads([x[lo:hi] for x in xs], self.GE)
+        d = dev_f32(buf) if dtype == zs.FP32 else dev_bf16(buf)
+        return zs.Grads.chunked(d, self.n, self.GE, dtype)
 
     def grads_of(self, bufs, dtype, index_modes):
         """zs.Grads over rank_grads' result (one chunked buffer, or N)."""
         if self.GE:
-            return zs.Grads.chunked(bufs, self.n, self.GE, dtype)
+            return self.chunked_grads(bufs, dtype)
         return zs.Grads(bufs, dtype, list(index_modes))
 
     def step_fused(self, t, grads_t, index_modes, dtype=None, per_unit=False):
@@ -196,14 +201,19 @@ class GpuRanks:
         for r, L in enumerate(self.lays):
             bufs = self.rank_grads(grads_t, r, index_modes, dtype)
             if self.GE:
-                # chunked gradients and a chunked state are passed from their
-                # start for every range; three state arrays move with the unit
-                G = self.grads_of(bufs, dtype, index_modes)
+                # chunked gradients are counted from the range's start: one
+                # receive buffer per call; a chunked state is passed from its
+                # start for every range, three state arrays move with the unit
                 for u0, u1 in ([(u, u + 1) for u in range(self.U)] if per_unit else
                                [(0, self.U)]):
-                    so = L.query(u0)["shard_off"] if u0 < self.U else 0
+                    q = L.query(u0)
+                    so, fo = q["shard_off"], q["flat_off"]
+                    hi = so + sum(L.query(u)["shard_len"] for u in range(u0, u1))
+                    if hi == so:
+                        continue
+                    G = self.chunked_grads(bufs, dtype, so, hi)
+                    assert G._keep[0].numel() == L.grad_len(self.GE, u0, u1)
                     st = self.state[r] if self.E else [x[so:] for x in self.state[r]]
-                    fo = L.query(u0)["flat_off"] if u0 < self.U else 0
                     zs.adam_step(L, u0, u1, c, *st, self.full[fo:], zs.INDEX_FULL, grads=G)
                 continue
             if not per_unit:
@@ -448,9 +458,9 @@ def test_fused_step_chunked_grads(units, n, strategy, decay, E, GE):
 
 @pytest.mark.parametrize("E,GE", [(0, 4), (64, 4096), (4, 16)])
 def test_per_unit_calls_on_chunked_grads(E, GE):
-    """One call per unit, chunked gradients passed from the buffer's start
-    every time (unit shard offsets 1024, 1049, 3097, ...: vector and
-    scalar slices)."""
+    """One call per unit, each with its own chunked receive buffer (unit
+    shard offsets 1024, 1049, 3097, ...: vector and scalar slices, and
+    unit lengths that are not multiples of the chunk)."""
     units, n = [4096, 100, 8192 + 3, 8], 4
     w = _w(units, n, "fsdp", "adamw")
     master0, grads = draw(w, 2)

@@ -2,14 +2,17 @@
 
 The sweep must give exactly what per-unit zero_adam_step + zero_gather_params
 give -- which the oracle pins -- for every in-flight cap, on two streams or
-one, with distinct per-unit buffers or a ring of reused ones.  Also the full
-Llama-70B sweep (N = 64, 81 units) with a ring of two unit buffers, sampled.
+one, with distinct per-unit buffers or a ring of reused ones, per-unit rank
+gradients as N buffers or one chunked receive buffer.  Also the full
+Llama-70B sweep (N = 64, 81 units) with a ring of two unit buffers and
+chunked receive buffers, sampled.
 """
 import numpy as np
 import pytest
 import torch
 
 from oracle import _c, strategies
+from chunked import grad_buffer
 from gather_check import assert_gathered
 from synthetic import WORKLOADS, grad_bits, master_init, peer_bits, small_workload
 
@@ -32,10 +35,14 @@ def h32(t):
     return t.cpu().numpy()
 
 
-@pytest.mark.parametrize("cap,two,E", [(0, True, 0), (1, True, 0), (2, True, 0), (3, True, 0),
-                                       (2, False, 0), (2, True, 16), (0, True, 2048)])
-def test_sweep_small_ragged_matches_oracle(cap, two, E):
-    """E > 0: master, m and v in one chunked buffer of E-element chunks."""
+@pytest.mark.parametrize("cap,two,E,GE", [(0, True, 0, 0), (1, True, 0, 0), (2, True, 0, 0),
+                                          (3, True, 0, 0), (2, False, 0, 0), (2, True, 16, 0),
+                                          (0, True, 2048, 0), (2, True, 0, 4), (1, True, 16, 64),
+                                          (2, False, 2048, 1024)])
+def test_sweep_small_ragged_matches_oracle(cap, two, E, GE):
+    """E > 0: master, m and v in one chunked buffer of E-element chunks.
+    GE > 0: each unit's rank gradients in one chunked receive buffer of
+    GE-element rows per rank."""
     units, n, r = [4096, 100, 8192 + 3, 8, 0, 64 * 33, 5000, 2048 * 3], 8, 5
     w = small_workload(units, n, "fsdp", steps=2, cfg=10, weight_decay=0.01, decoupled=True)
     psi = sum(units)
@@ -73,13 +80,26 @@ def test_sweep_small_ragged_matches_oracle(cap, two, E):
         padded = [strategies.pad(olay, g) for g in grads]
         ios = []
         for u, x in enumerate(q):
-            b = x["rank_flat_off"]
-            # a zero-size unit still needs non-NULL rank buffers (NULL = missing replica)
-            rg = [torch.from_numpy(p[b:b + max(1, x["shard_len"])].view(np.int16).copy()).to(DEV)
-                  for p in padded] if x["shard_len"] else [fulls[u]] * n
+            b, s = x["rank_flat_off"], x["shard_len"]
+            if GE:
+                # rows of GE elements of each rank's slice, in rank order; a
+                # zero-size unit still gets pointers one chunk apart
+                rows = max(1, -(-s // GE))
+                cells = np.zeros((rows, n, GE), np.uint16)
+                for k, p in enumerate(padded):
+                    col = np.zeros(rows * GE, np.uint16)
+                    col[:s] = p[b:b + s]
+                    cells[:, k, :] = col.reshape(rows, GE)
+                recv = torch.from_numpy(cells.reshape(-1).view(np.int16)).to(DEV)
+                rg = [recv[k * GE:] for k in range(n)]
+            else:
+                # a zero-size unit still needs non-NULL rank buffers (NULL =
+                # missing replica)
+                rg = [torch.from_numpy(p[b:b + max(1, s)].view(np.int16).copy()).to(DEV)
+                      for p in padded] if s else [fulls[u]] * n
             ios.append((rg, [None if k == r else peers[u][k] for k in range(n)], fulls[u]))
         zs.fsdp_sweep(L, 0, U, zs.adam_cfg(weight_decay=0.01, decoupled=True, step=t + 1),
-                      zs.BF16, ios, master, m, v, cap, gather_stream=gs)
+                      zs.BF16, ios, master, m, v, cap, gather_stream=gs, grad_chunk=GE)
         torch.cuda.synchronize()
     st = strategies.full_state(oc, padded=True)
     if E:
@@ -106,7 +126,8 @@ def test_sweep_small_ragged_matches_oracle(cap, two, E):
 
 def test_sweep_ring_of_two_buffers_full_llama70b():
     """The whole 81-unit sweep at N = 64 with K = 2 and two unit buffers
-    reused in turn (the bench's configuration); every unit's state sampled
+    reused in turn, every unit's 64 rank gradients read from one chunked
+    receive buffer (the bench's configuration); every unit's state sampled
     against the oracle, the last two units' buffers checked."""
     w = WORKLOADS[4]
     n, r = w.n_ranks, w.n_ranks - 1
@@ -115,7 +136,11 @@ def test_sweep_ring_of_two_buffers_full_llama70b():
     L = zs.shard_init("fsdp", n, r, units)
     q = [L.query(u) for u in range(U)]
     smax = max(x["shard_len"] for x in q)
+    GE = zs.GRAD_CHUNK_DEFAULT
+    # every unit reads elements [0, s_u) of each rank's draw: the prefix of
+    # one receive buffer laid out for the largest unit
     grads = [grad_bits(w, 0, k, smax, device=DEV) for k in range(n)]
+    recv, _ = grad_buffer(smax, n, GE, lambda k: grads[k])
     peers = [peer_bits(w, k, smax, device=DEV) for k in range(n)]
     ring = [torch.zeros(n * smax, dtype=torch.int16, device=DEV) for _ in range(2)]
     master = torch.empty(L.shard_len, device=DEV)
@@ -134,10 +159,11 @@ def test_sweep_ring_of_two_buffers_full_llama70b():
     for u, x in enumerate(q):
         t_idx = torch.from_numpy(samp[u][0]).to(DEV)
         gsamp[u] = [h16(g[t_idx]) for g in grads]
-    ios = [(grads, [None if k == r else peers[k] for k in range(n)], ring[u % 2])
-           for u in range(U)]
+    rg = [recv[k * GE:] for k in range(n)]
+    ios = [(rg, [None if k == r else peers[k] for k in range(n)], ring[u % 2]) for u in range(U)]
     gs = torch.cuda.Stream()
-    zs.fsdp_sweep(L, 0, U, zs.adam_cfg(step=1), zs.BF16, ios, master, m, v, 2, gather_stream=gs)
+    zs.fsdp_sweep(L, 0, U, zs.adam_cfg(step=1), zs.BF16, ios, master, m, v, 2, gather_stream=gs,
+                  grad_chunk=GE)
     torch.cuda.synchronize()
     hp = _c.hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, False)
     for u, x in enumerate(q):
