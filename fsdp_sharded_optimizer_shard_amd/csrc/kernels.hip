@@ -52,6 +52,7 @@ constexpr int kMaxSegs = 32;                // units per launch (kernarg table)
 constexpr int kStepTile = 1024;             // elements per step-kernel tile
 constexpr int kStepThreads = 256;           // step kernel: one 4-element group per lane
 constexpr int kStepBlocksPerCU = 5;         // step kernel occupancy cap (LDS reservation)
+constexpr int kStep64BlocksPerCU = 3;       // the same for the N = 64 specialisation
 constexpr int kGatherBlocksPerCU = 13;      // gather occupancy cap (LDS reservation)
 constexpr int kAccThreads = 512;            // accumulate: one 4-element group per lane
 constexpr int kWaveElems = 256;             // elements one wave covers (64 lanes x 4)
@@ -784,7 +785,6 @@ size_t lds_reserve()
     return (size_t)v;
 }
 
-size_t step_lds_reserve() { return lds_reserve<kStepBlocksPerCU>(); }
 
 // Splits a unit range into launches of at most kMaxSegs units each and
 // calls fn(first_unit, last_unit_exclusive).
@@ -927,17 +927,23 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
 // better; the kernel's time is that of its memory traffic (the same streams
 // without the arithmetic run no faster; zero_stream_mix).
 //
-// A launch whose tiles fit on the GPU at once under the cap (at most
-// kStepBlocksPerCU per CU) never has more in flight than the cap allows, so
-// it reserves nothing: small launches (a tiny shard, one bucket of a few
-// tiles) keep the plain dispatch.
+// The N = 64 specialisation (the Llama-70B units) runs at most 3 blocks per
+// CU: with its 64 rank gradients in one chunked receive buffer, paired over
+// eight placements of one layer unit, 3 blocks took 0.970 x the time of 5
+// (0.967-0.998; 2 blocks 0.968 x, 4 blocks 1.000 x, 6 blocks 1.013 x);
+// with 64 separate rank buffers every cap from 2 to 6 is within 0.4 %.  The
+// same sweep at N = 8 keeps 5 (4 equal, 3 1.12 x, 6 1.025 x).
+//
+// A launch whose tiles fit on the GPU at once under the cap never has more
+// in flight than the cap allows, so it reserves nothing: small launches (a
+// tiny shard, one bucket of a few tiles) keep the plain dispatch.
 template <int MODE, int NR, bool BF16>
 void launch_one(const StepArgs &a, hipStream_t st)
 {
-    const size_t lds =
-        a.n_tiles > (int64_t)device_cus() * kStepBlocksPerCU ? step_lds_reserve() : 0;
+    constexpr int cap = NR == 64 ? kStep64BlocksPerCU : kStepBlocksPerCU;
+    const size_t lds = a.n_tiles > (int64_t)device_cus() * cap ? lds_reserve<cap>() : 0;
     static const int resident =
-        resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads, step_lds_reserve());
+        resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads, lds_reserve<cap>());
     const int64_t blocks = stream_grid(a.n_tiles, resident, kStepThreads);
     hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kStepThreads),
                        lds, st, a);
