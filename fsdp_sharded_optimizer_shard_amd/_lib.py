@@ -366,6 +366,8 @@ class Layout:
         """Elements of one buffer holding all N ranks' gradients for the
         range's part of this shard (the whole shard by default) in chunks of
         `chunk`: ceil(S / E) rows of N chunks."""
+        if chunk <= 0:
+            raise ValueError(f"chunk must be positive (got {chunk})")
         ue = self.info()["n_units"] if unit_end is None else unit_end
         shard, _ = self.range_lens(unit_begin, ue)
         if shard is None:

@@ -776,6 +776,9 @@ def test_chunked_grads_counts_in_the_binding():
     E, N = 8, 4
     L = zs.shard_init("zero3", N, 1, [1000, 24])     # shard 250 + 6
     assert L.grad_len(E) == 32 * N * E and L.grad_len(E, 1, 2) == N * E
+    for bad in ((0,), (E, 0, 3)):
+        with pytest.raises(ValueError):
+            L.grad_len(*bad)
     # counted from the range's first element: the whole range's last, 255,
     # sits at (255 // 8) 32 + 7 = 999 from each rank's pointer; unit 1 alone
     # (6 elements) ends at 5
