@@ -3,10 +3,12 @@ bits, on the fused step, the gather and the fp32 accumulation.
 
 The workloads stop at 1.1e9 elements per shard, where byte offsets already
 pass 2^31 but element indices do not. Here one unit holds 2^31 + 4099
-elements, so the last group of four is ragged and takes the scalar path.
-Inputs are drawn on the device. The elements compared lie around index 2^31,
-at both ends and at random. Each is checked bit for bit against the oracle
-run on the same values. Peak device memory is about 35 GB.
+elements, so the last group of four is ragged and takes the scalar path;
+one case runs a shard of that length in the chunked state and chunked
+gradient formats. Inputs are drawn on the device. The elements compared lie
+around index 2^31, at both ends and at random. Each is checked bit for bit
+against the oracle run on the same values. Peak device memory is about
+45 GB.
 """
 import numpy as np
 import pytest
@@ -125,4 +127,42 @@ def test_grad_accumulate_past_2_31_elements():
     _c.accumulate_bf16(a_h, np.ascontiguousarray(mb_h))
     _same_bits(_at(acc, ti), a_h, "main gradient")
     del acc, micro, ti
+    _release()
+
+
+def test_chunked_formats_past_2_31_shard_elements():
+    # two ranks, each with a shard of 2^31 + 4099 elements: the chunked
+    # state and the chunked receive buffer of both ranks' gradients are
+    # addressed with shard indices past 2^31 (and buffer offsets past 2^32)
+    n, E, GE = BIG, 8192, 16384
+    L = zs.shard_init("zero3", 2, 1, [2 * n]).chunk_state(E)
+    assert L.shard_len == n
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(34)
+    st = torch.empty(L.state_len, device=DEV)
+    st.normal_(0.0, 0.02, generator=gen)
+    st.view(-1, 3, E)[:, 2, :].abs_()            # v >= 0
+    recv = torch.empty(L.grad_len(GE), dtype=torch.int16, device=DEV)
+    step = 1 << 30
+    for off in range(0, recv.numel(), step):
+        k = min(step, recv.numel() - off)
+        recv[off:off + k] = _bf16_randn(k, 1e-3, gen)
+    out = torch.empty(n, dtype=torch.int16, device=DEV)
+    idx = _samples(n, 34)
+    pos = torch.from_numpy((idx // E) * 3 * E + idx % E).to(DEV)
+    gpos = [torch.from_numpy((idx // GE) * 2 * GE + q * GE + idx % GE).to(DEV) for q in range(2)]
+    p_h, m_h, v_h = _at(st, pos), _at(st, pos + E), _at(st, pos + 2 * E)
+    g_h = [_at(recv, gp).view(np.uint16) for gp in gpos]
+    cfg = zs.adam_cfg(lr=1e-3, weight_decay=0.01, decoupled=True, step=3)
+    zs.adam_step(L, 0, 1, cfg, *L.state_views(st), out, zs.INDEX_SHARD,
+                 grads=zs.Grads.chunked(recv, 2, GE))
+    torch.cuda.synchronize()
+    par_h = np.empty(idx.size, np.uint16)
+    _c.rank_step(_c.hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 3, True), g_h, 1.0, p_h, m_h, v_h,
+                 par_h)
+    _same_bits(_at(st, pos), p_h, "master")
+    _same_bits(_at(st, pos + E), m_h, "m")
+    _same_bits(_at(st, pos + 2 * E), v_h, "v")
+    _same_bits(_at(out, torch.from_numpy(idx).to(DEV)).view(np.uint16), par_h, "bf16 param")
+    del st, recv, out, pos, gpos
     _release()
