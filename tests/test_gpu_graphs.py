@@ -84,14 +84,20 @@ def test_fused_step_and_gather_in_a_graph():
     _replay_and_compare(lambda: step(G), lambda: step(E), G, E)
 
 
-def test_chunked_state_steps_in_a_graph():
-    # master, m and v in one chunked buffer: the fused step with its gather,
-    # then the apply pass of the two-pass path, captured and replayed
+@pytest.mark.parametrize("GE", [0, 512])
+def test_chunked_state_steps_in_a_graph(GE):
+    # master, m and v in one chunked buffer (and, GE > 0, the rank gradients
+    # in one chunked receive buffer, the benchmark's launch): the fused step
+    # with its gather, then the two-pass path, captured and replayed
     units, n, r, E = [5000, 3000, 777], 4, 1, 1024
     L = zs.shard_init("zero3", n, r, units).chunk_state(E)
     S, P = L.shard_len, L.flat_len
     w = small_workload(units, n, "zero3", cfg=12)
-    grads = [grad_bits(w, 0, q, S, device=DEV) for q in range(n)]
+    if GE:
+        recv = grad_bits(w, 0, 0, L.grad_len(GE), device=DEV)
+        grads = [recv[q * GE:] for q in range(n)]
+    else:
+        grads = [grad_bits(w, 0, q, S, device=DEV) for q in range(n)]
     peers = [None if q == r else grad_bits(w, 1, q, S, device=DEV) for q in range(n)]
     cfg = zs.adam_cfg(lr=1e-3, weight_decay=0.01, decoupled=True, step=3)
     npart = zs.reduce_partials_count(L, 0, len(units))
@@ -104,7 +110,7 @@ def test_chunked_state_steps_in_a_graph():
                 torch.empty(npart, dtype=torch.float64, device=DEV), torch.empty(1, device=DEV)]
 
     def step(b):
-        G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD)
+        G = zs.Grads(grads, zs.BF16, zs.INDEX_SHARD, GE)
         zs.adam_step(L, 0, len(units), cfg, *L.state_views(b[0]), b[1], grads=G)
         zs.gather_params(L, 0, len(units), peers, b[1])
         zs.reduce_shard(L, 0, len(units), G, b[2], b[3], npart)
