@@ -390,18 +390,25 @@ def test_table_steps_replayed_from_one_graph():
         _same(a, b, f"past the table, output {i}")
 
 
-def test_table_sweep_replayed_from_one_graph():
+@pytest.mark.parametrize("GE", [0, 64])
+def test_table_sweep_replayed_from_one_graph(GE):
     """One captured two-stream zero_fsdp_sweep_table call replays as the
     sweeps of steps 1..T (a learning-rate schedule), each bit-identical to
-    zero_fsdp_sweep with that step's configuration."""
+    zero_fsdp_sweep with that step's configuration; GE > 0 with each unit's
+    rank gradients in one chunked receive buffer."""
     units, n, r, T = [4096, 1000, 2500, 777], 4, 3, 4
     U = len(units)
     L = zs.shard_init("fsdp", n, r, units)
     q = [L.query(u) for u in range(U)]
     S = L.shard_len
     w = small_workload(units, n, "fsdp", cfg=12)
-    grads = [[grad_bits(w, 0, k, q[u]["shard_len"], device=DEV, unit=u) for k in range(n)]
-             for u in range(U)]
+    if GE:
+        recv = [grad_bits(w, 0, 0, L.grad_len(GE, u, u + 1), device=DEV, unit=u)
+                for u in range(U)]
+        grads = [[recv[u][k * GE:] for k in range(n)] for u in range(U)]
+    else:
+        grads = [[grad_bits(w, 0, k, q[u]["shard_len"], device=DEV, unit=u) for k in range(n)]
+                 for u in range(U)]
     peers = [[None if k == r else grad_bits(w, 1, k, q[u]["shard_len"], device=DEV, unit=u)
               for k in range(n)] for u in range(U)]
     cfgs = [zs.adam_cfg(lr=2e-3 * (1.0 - 0.2 * k), weight_decay=0.01, decoupled=True, step=k + 1)
@@ -419,14 +426,16 @@ def test_table_sweep_replayed_from_one_graph():
 
     G, E = buffers(), buffers()
     W = buffers()
-    zs.fsdp_sweep(L, 0, U, cfgs[0], zs.BF16, ios(W), W[0], W[1], W[2], 2, gather_stream=gs)
+    zs.fsdp_sweep(L, 0, U, cfgs[0], zs.BF16, ios(W), W[0], W[1], W[2], 2, gather_stream=gs,
+                  grad_chunk=GE)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         zs.fsdp_sweep_table(L, 0, U, table, T, counter, zs.BF16, ios(G), G[0], G[1], G[2], 2,
-                            gather_stream=gs)
+                            gather_stream=gs, grad_chunk=GE)
     for k in range(T):
-        zs.fsdp_sweep(L, 0, U, cfgs[k], zs.BF16, ios(E), E[0], E[1], E[2], 2, gather_stream=gs)
+        zs.fsdp_sweep(L, 0, U, cfgs[k], zs.BF16, ios(E), E[0], E[1], E[2], 2, gather_stream=gs,
+                      grad_chunk=GE)
         graph.replay()
         _noise()
         torch.cuda.synchronize()
