@@ -3,7 +3,8 @@
 The sweep must give exactly what per-unit zero_adam_step + zero_gather_params
 give -- which the oracle pins -- for every in-flight cap, on two streams or
 one, with distinct per-unit buffers or a ring of reused ones, per-unit rank
-gradients as N buffers or one chunked receive buffer.  Also the full
+gradients as N buffers or one chunked receive buffer, on fixed and on ten
+seeded random configurations.  Also the full
 Llama-70B sweep (N = 64, 81 units) with a ring of two unit buffers and
 chunked receive buffers, sampled.
 """
@@ -43,7 +44,28 @@ def test_sweep_small_ragged_matches_oracle(cap, two, E, GE):
     """E > 0: master, m and v in one chunked buffer of E-element chunks.
     GE > 0: each unit's rank gradients in one chunked receive buffer of
     GE-element rows per rank."""
-    units, n, r = [4096, 100, 8192 + 3, 8, 0, 64 * 33, 5000, 2048 * 3], 8, 5
+    _sweep_case([4096, 100, 8192 + 3, 8, 0, 64 * 33, 5000, 2048 * 3], 8, 5, cap, two, E, GE,
+                seed=cap)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_sweep_random_configuration(seed):
+    """Seeded random sweeps: 1-9 units of 0 to 12,000 elements, N up to 64,
+    any rank, cap 0-3 on one or two streams, both memory formats."""
+    rng = np.random.default_rng(500 + seed)
+    units = [int(rng.choice([0, rng.integers(1, 50), rng.integers(100, 12000)]))
+             for _ in range(int(rng.integers(1, 10)))]
+    if sum(units) == 0:
+        units.append(999)
+    n = int(rng.choice([2, 3, 4, 8, 16, 64]))
+    r = int(rng.integers(0, n))
+    cap, two = int(rng.integers(0, 4)), bool(rng.integers(0, 2))
+    E = int(rng.choice([0, 4, 64, 8192]))
+    GE = int(rng.choice([0, 4, 16, 4096]))
+    _sweep_case(units, n, r, cap, two, E, GE, seed=100 + seed)
+
+
+def _sweep_case(units, n, r, cap, two, E, GE, seed):
     w = small_workload(units, n, "fsdp", steps=2, cfg=10, weight_decay=0.01, decoupled=True)
     psi = sum(units)
     master0 = master_init(w, psi).numpy()
@@ -67,7 +89,7 @@ def test_sweep_small_ragged_matches_oracle(cap, two, E, GE):
         master = torch.from_numpy(mfull[idx].copy()).to(DEV)
         m = torch.zeros(S, device=DEV)
         v = torch.zeros(S, device=DEV)
-    rng = np.random.default_rng(cap)
+    rng = np.random.default_rng(seed)
     q = [L.query(u) for u in range(U)]
     peers_h = [[rng.integers(0, 1 << 16, x["shard_len"], dtype=np.uint16) for _ in range(n)]
                for x in q]
