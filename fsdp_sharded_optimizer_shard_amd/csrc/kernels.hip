@@ -12,10 +12,11 @@
 //     written by one instruction -- rocprof FETCH_SIZE / WRITE_SIZE equal the
 //     algorithmic bytes; the gather and the accumulation walk 2048-element
 //     tiles;
-//   * the step kernel runs at most 5 blocks (20 waves) per CU and the
-//     gather at most 13 (26 waves): fewer requests in flight mix the read
-//     and write streams better (measured below, at launch_one and at the
-//     gather launch);
+//   * the step kernel runs at most 5 blocks (20 waves) per CU (3 in its
+//     N = 64 specialisation) and the gather at most 13 (26 waves): fewer
+//     requests in flight mix the read and write streams better; the
+//     read-dominated reduce pass runs uncapped (measured below, at
+//     launch_one and at the gather launch);
 //   * one pass: the reduce over ranks, the Adam update and the bf16 cast are
 //     fused so each byte crosses HBM once;
 //   * one launch covers a tile space that concatenates the slices of many
@@ -934,16 +935,38 @@ AdamScalars make_scalars(const zero_adam_cfg *c)
 // with 64 separate rank buffers every cap from 2 to 6 is within 0.4 %.  The
 // same sweep at N = 8 keeps 5 (4 equal, 3 1.12 x, 6 1.025 x).
 //
+// The reduce pass, four fifths reads, runs uncapped: on the GPT-2-small
+// rank shard (8 full-indexed rank buffers) full occupancy took 0.962 x the
+// time of 5 blocks per CU (0.956-0.969, eight placements; 6 or 8 blocks
+// the same, 4 blocks 1.12 x), on a 1e8-element shard 0.988 x.  The apply
+// pass keeps 5 (full occupancy 1.020 x on the GPT-2 shard, 1.023 x on the
+// 7B shard; 4 blocks equal).
+//
 // A launch whose tiles fit on the GPU at once under the cap never has more
 // in flight than the cap allows, so it reserves nothing: small launches (a
 // tiny shard, one bucket of a few tiles) keep the plain dispatch.
+template <int MODE, int NR>
+constexpr int step_cap()
+{
+    return MODE == kReduce ? 0 : NR == 64 ? kStep64BlocksPerCU : kStepBlocksPerCU;
+}
+
+template <int CAP>
+size_t step_lds(int64_t n_tiles)
+{
+    if constexpr (CAP == 0)
+        return 0;
+    else
+        return n_tiles > (int64_t)device_cus() * CAP ? lds_reserve<CAP>() : 0;
+}
+
 template <int MODE, int NR, bool BF16>
 void launch_one(const StepArgs &a, hipStream_t st)
 {
-    constexpr int cap = NR == 64 ? kStep64BlocksPerCU : kStepBlocksPerCU;
-    const size_t lds = a.n_tiles > (int64_t)device_cus() * cap ? lds_reserve<cap>() : 0;
+    constexpr int cap = step_cap<MODE, NR>();
+    const size_t lds = step_lds<cap>(a.n_tiles);
     static const int resident =
-        resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads, lds_reserve<cap>());
+        resident_blocks(step_kernel<MODE, NR, BF16>, kStepThreads, step_lds<cap>(INT64_MAX));
     const int64_t blocks = stream_grid(a.n_tiles, resident, kStepThreads);
     hipLaunchKernelGGL((step_kernel<MODE, NR, BF16>), dim3((unsigned)blocks), dim3(kStepThreads),
                        lds, st, a);

@@ -125,11 +125,11 @@ def test_chunked_state_steps_in_a_graph(GE):
 
 
 def test_launches_with_the_occupancy_reservation_in_a_graph():
-    # the step kernel and the gather reserve LDS (their occupancy caps) only
-    # for launches of more blocks than fit on the GPU at once, 5 and 13 per
-    # CU: a shard of 2.5 million elements (2442 step tiles of 1024; 1222
-    # gather tiles of 2048 for each of 3 sources) takes both paths, under
-    # capture
+    # the fused and apply passes and the gather reserve LDS (their occupancy
+    # caps) only for launches of more blocks than fit on the GPU at once, 5
+    # and 13 per CU (the reduce pass runs uncapped): a shard of 2.5 million
+    # elements (2442 step tiles of 1024; 1222 gather tiles of 2048 for each
+    # of 3 sources) takes both paths, under capture
     units, n, r = [8_000_000, 2_000_003], 4, 1
     L = zs.shard_init("zero3", n, r, units)
     S, P = L.shard_len, L.flat_len
