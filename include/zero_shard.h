@@ -229,8 +229,9 @@ zero_status zero_layout_rows(const zero_layout *layout, int32_t unit,
    writes each chunk's three parts next to each other instead of in three
    arrays gigabytes apart, which HBM serves faster: on one MI355X the
    7B / N = 8 step kernel takes 0.938 x the three-array time with
-   E = 8192 (0.910-0.982 over six buffer placements).  chunk = 0 gives the three-array format back; otherwise `chunk`
-   is a power of two in [ZERO_STATE_CHUNK_MIN, ZERO_STATE_CHUNK_MAX]. */
+   E = 8192 (0.910-0.982 over six buffer placements).  chunk = 0 gives the
+   three-array format back; otherwise `chunk` is a power of two in
+   [ZERO_STATE_CHUNK_MIN, ZERO_STATE_CHUNK_MAX]. */
 #define ZERO_STATE_CHUNK_MIN 4
 #define ZERO_STATE_CHUNK_MAX 16777216
 #define ZERO_STATE_CHUNK_DEFAULT 8192 /* the measured best on MI355X */
