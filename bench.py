@@ -82,10 +82,11 @@ def parse():
                          "chunks (zero_layout_chunk_state); 0 keeps three arrays; default: "
                          "the library's ZERO_STATE_CHUNK_DEFAULT")
     ap.add_argument("--grad-chunk", type=int, default=None, metavar="E",
-                    help="the shard-indexed rank gradients of the 7B step (and of each unit of "
-                         "--config 4) as one receive buffer of rows of E elements per rank "
-                         "(zero_grads.chunk); 0 keeps one buffer per rank; default: the "
-                         "library's ZERO_GRAD_CHUNK_DEFAULT")
+                    help="the rank gradients of the 7B step, of each rank of --config 1 and of "
+                         "each unit of --config 4 as one receive buffer of rows of E elements "
+                         "per rank (zero_grads.chunk); 0 keeps one buffer per rank (full-"
+                         "indexed for --config 1); default: the library's "
+                         "ZERO_GRAD_CHUNK_DEFAULT")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
@@ -520,8 +521,22 @@ def run_gpt2_clip(args, torch, zs, np):
     lays = [zs.shard_init("zero2", N, r, list(w.units)).chunk_state(state_chunk(args, zs))
             for r in range(N)]
     S, P = lays[0].shard_len, lays[0].flat_len
+    GE = grad_chunk(args, zs)
     grads = [grad_bits(w, 0, q, P, device=dev) for q in range(N)]
-    G = zs.Grads(grads, zs.BF16, zs.INDEX_FULL)
+    if GE:
+        # each rank reads its slices of the N gradients from its own
+        # receive buffer (rows of GE elements per rank): what a bucketed
+        # reduce-scatter leaves on it
+        recv = []
+        for L in lays:
+            own = torch.cat([torch.arange(L.query(u)["rank_flat_off"],
+                                          L.query(u)["rank_flat_off"] + L.query(u)["shard_len"],
+                                          device=dev) for u in range(U)])
+            recv.append(RankGrads(torch, zs, [g[own] for g in grads], GE))
+            assert recv[-1].buf.numel() == L.grad_len(GE)
+        Gr = [x.grads for x in recv]
+    else:
+        Gr = [zs.Grads(grads, zs.BF16, zs.INDEX_FULL)] * N
     full = torch.empty(P, dtype=torch.int16, device=dev)
     st = [State(torch, L, master_init(w, L.shard_len, device=dev, rank=r)).views
           for r, L in enumerate(lays)]
@@ -538,7 +553,7 @@ def run_gpt2_clip(args, torch, zs, np):
                           weight_decay=w.weight_decay, decoupled=w.decoupled, step=t[0])
         for r in range(N):
             phase(ph, "reduce_with_sumsq",
-                  lambda r=r: zs.reduce_shard(lays[r], 0, U, G, gsh[r], partials[offs[r]:],
+                  lambda r=r: zs.reduce_shard(lays[r], 0, U, Gr[r], gsh[r], partials[offs[r]:],
                                               counts[r]))
         phase(ph, "clip_coef", lambda: zs.clip_coef(partials, partials.numel(),
                                                     w.max_grad_norm, coef))
@@ -559,7 +574,9 @@ def run_gpt2_clip(args, torch, zs, np):
                     "GPT-2-small flat buffer, 5 x 25M buckets, N=8: reduce + global-norm clip "
                     "+ AdamW + bf16 for all 8 ranks",
                     psi=w.psi, n_ranks=N, shard_elems=S, buckets=list(w.units),
-                    state_layout=state_desc(lays[0].state_chunk))
+                    state_layout=state_desc(lays[0].state_chunk),
+                    grad_layout=("per rank: " + grad_desc(GE, N)) if GE else
+                    f"{N} full-indexed bf16 gradient buffers, read by every rank")
     out["step_gbps"] = N * (rb + ab) / (ms * 1e-3) / 1e9
     out["kernels"] = kern
     out["roofline"] = roofline(dom[0], dom[1], kern[dom[0]]["ms_per_launch_mean"])
@@ -576,7 +593,7 @@ def run_gpt2_clip(args, torch, zs, np):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         for r in range(N):
-            zs.reduce_shard(lays[r], 0, U, G, gsh[r], partials[offs[r]:], counts[r])
+            zs.reduce_shard(lays[r], 0, U, Gr[r], gsh[r], partials[offs[r]:], counts[r])
         zs.clip_coef(partials, partials.numel(), w.max_grad_norm, coef)
         for r in range(N):
             zs.adam_step_table(lays[r], 0, U, table, n_rep, counter, *st[r], full,

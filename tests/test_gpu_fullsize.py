@@ -3,9 +3,11 @@ benchmark uses (default launch width, whole-range or per-unit calls).
 
   * GPT-2-small flat buffer (Psi = 124,439,808, N = 8, five 25M-element
     buckets, AdamW wd 0.01, global clip at 1.0, 1 % outliers x100, 5 steps):
-    all 8 ranks on the GPU through reduce -> clip -> Adam; every element of
-    every rank's master / m / v and the whole bf16 buffer compared with the
-    oracle's strategy simulation after every step.
+    all 8 ranks on the GPU through reduce -> clip -> Adam, reading the 8
+    full gradient buffers or (the benchmark's launch) a chunked receive
+    buffer per rank; every element of every rank's master / m / v and the
+    whole bf16 buffer compared with the oracle's strategy simulation after
+    every step.
   * Megatron distributed optimizer (Psi = 7.24e9, N = 8, rank 7): the fp32
     main gradient accumulated from 4 bf16 micro-batches over the whole
     buffer, 7 peer fp32 gradient shards (sums of 4 draws each), the fp32
@@ -104,7 +106,11 @@ def sample(rng, n, k, edge=2048):
 
 # ------------------------------------------------------------ config 1 --
 
-def test_config1_gpt2_small_clip_all_ranks():
+@pytest.mark.parametrize("GE", [0, 16384])
+def test_config1_gpt2_small_clip_all_ranks(GE):
+    """GE = 0: every rank reads its slices of the 8 full gradient buffers;
+    GE > 0: each rank reads them from its own chunked receive buffer (the
+    benchmark's launch)."""
     w = WORKLOADS[1]
     n, units = w.n_ranks, list(w.units)
     psi = w.psi
@@ -129,13 +135,23 @@ def test_config1_gpt2_small_clip_all_ranks():
     gshard = [torch.empty(L.shard_len, device=DEV) for L in lays]
     coef = torch.empty(1, device=DEV)
     norm = torch.empty(1, dtype=torch.float64, device=DEV)
+    owned = [torch.from_numpy(np.concatenate([np.arange(b, b + k) for b, _, k in
+                                              oc.layouts[r].owned_runs()])).to(DEV)
+             for r in range(n)]
     for t in range(w.steps):
         gd = [grad_bits(w, t, q, psi, device=DEV) for q in range(n)]
         gh = [host_bf16(x) for x in gd]
-        G = zs.Grads(gd, zs.BF16, zs.INDEX_FULL)
+        if GE:
+            Gr = []
+            for r, L in enumerate(lays):
+                recv, _ = grad_buffer(L.shard_len, n, GE, lambda q: gd[q][owned[r]])
+                assert recv.numel() == L.grad_len(GE)
+                Gr.append(zs.Grads.chunked(recv, n, GE))
+        else:
+            Gr = [zs.Grads(gd, zs.BF16, zs.INDEX_FULL)] * n
         off = 0
         for r, L in enumerate(lays):
-            zs.reduce_shard(L, 0, len(units), G, gshard[r], partials[off:], counts[r])
+            zs.reduce_shard(L, 0, len(units), Gr[r], gshard[r], partials[off:], counts[r])
             off += counts[r]
         zs.clip_coef(partials, partials.numel(), w.max_grad_norm, coef, norm)
         for r, L in enumerate(lays):
