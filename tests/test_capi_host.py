@@ -821,3 +821,31 @@ def test_sweep_checks_every_units_chunked_gradients_before_launching():
     e = _err(zs.fsdp_sweep_table, L, 0, 2, table, 4, FAKE + 8192, zs.BF16, units, FAKE,
              FAKE + 16, FAKE + 32, 2, 0, 0, grad_chunk=E)
     assert e.status == zs.ERR_INVALID_ARG and "unit 1: chunked gradients" in str(e)
+
+
+@settings(max_examples=150, deadline=None)
+@given(units=st.lists(st.integers(0, 3000), min_size=1, max_size=12),
+       n=st.integers(1, 64), data=st.data(),
+       e_log=st.integers(2, 12))
+def test_chunked_counts_match_brute_force(units, n, data, e_log):
+    # the binding's element counts for the two chunked formats (what every
+    # pointer must reach before a launch) against the largest offset any
+    # element of the range actually uses, computed element by element
+    r = data.draw(st.integers(0, n - 1))
+    ub = data.draw(st.integers(0, len(units)))
+    ue = data.draw(st.integers(ub, len(units)))
+    E = 1 << e_log
+    L = zs.shard_init("zero3", n, r, units)
+    C = L.chunk_state(E)
+    q = [L.query(u) for u in range(len(units))]
+    base = q[ub]["shard_off"] if ub < len(units) else 0
+    absl = [q[u]["shard_off"] + j for u in range(ub, ue) for j in range(q[u]["shard_len"])]
+    rel = [i - base for i in absl]          # chunked gradients count from the range
+    want_g = max(((i // E) * n * E + i % E + 1 for i in rel), default=0)
+    want_s = max(((i // E) * 3 * E + i % E + 1 for i in absl), default=0)
+    assert L.grad_count(ub, ue, E) == want_g
+    assert C.state_count(ub, ue) == want_s
+    S = L.range_lens(ub, ue)[0]
+    if S:
+        assert L.grad_len(E, ub, ue) == -(-S // E) * n * E >= want_g
+    assert C.state_len >= want_s
