@@ -44,19 +44,22 @@ def setup_module(module):
 
 # ------------------------------------------------------------ cases --
 
-def test_config0_tiny_zero2_ten_steps():
+@pytest.mark.parametrize("E", [0, 8192])
+def test_config0_tiny_zero2_ten_steps(E):
     """Psi = 2^20, N = 4, Adam, 10 steps, all four ranks into one buffer;
-    checked bit-exactly after every step (and DDP == ZeRO in the oracle)."""
+    checked bit-exactly after every step (and DDP == ZeRO in the oracle);
+    with three state arrays and with the chunked state the benchmark
+    times."""
     w = WORKLOADS[0]
     master0, grads = draw(w, w.steps)
     oc = strategies.make_cluster("zero2", list(w.units), w.n_ranks, master0)
     ddp = strategies.make_cluster("ddp", list(w.units), w.n_ranks, master0)
-    g = GpuRanks(w, master0, oc)
+    g = GpuRanks(w, master0, oc, state_chunk=E)
     for t in range(w.steps):
         strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
         strategies.step(ddp, oracle_cfg(w), t + 1, grads[t])
         g.step_fused(t + 1, grads[t], [zs.INDEX_FULL] * w.n_ranks)
-        g.check(f"config 0 step {t + 1}")
+        g.check(f"config 0 E={E} step {t + 1}")
     assert np.array_equal(strategies.full_params(ddp), strategies.full_params(oc))
 
 
