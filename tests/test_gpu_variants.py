@@ -83,7 +83,10 @@ def test_zero1_over_allreduce_matches_oracle():
                                   S[name][idx].view(np.uint32)), (r, name)
 
 
-def test_ddp_bucket_as_ready_equals_whole_range():
+@pytest.mark.parametrize("E", [0, 8192])
+def test_ddp_bucket_as_ready_equals_whole_range(E):
+    """E > 0: master, m and v in one chunked buffer (the benchmark's
+    --ddp-buckets launch)."""
     buckets, n = [25000, 25000, 24439, 4096, 1], 8
     w = small_workload(buckets, n, "ddp", steps=2, cfg=6, weight_decay=0.01, decoupled=True,
                        max_grad_norm=1.0, outlier_frac=0.01)
@@ -91,6 +94,8 @@ def test_ddp_bucket_as_ready_equals_whole_range():
     master0 = master_init(w, psi).numpy()
     oc = strategies.make_cluster("ddp", buckets, n, master0)
     L = zs.shard_init("ddp", n, 0, buckets)
+    if E:
+        L = L.chunk_state(E)
     U = len(buckets)
     assert L.flat_len == psi
     tiles = [zs.reduce_partials_count(L, u, u + 1) for u in range(U)]
@@ -98,9 +103,18 @@ def test_ddp_bucket_as_ready_equals_whole_range():
     assert sum(tiles) == zs.reduce_partials_count(L, 0, U)
     runs = {}
     for mode in ("buckets", "whole"):
-        p = torch.from_numpy(master0.copy()).to(DEV)
-        m = torch.zeros(psi, device=DEV)
-        v = torch.zeros(psi, device=DEV)
+        if E:
+            rows = -(-psi // E)
+            cells = np.zeros((rows, 3, E), np.float32)
+            col = np.zeros(rows * E, np.float32)
+            col[:psi] = master0
+            cells[:, 0, :] = col.reshape(rows, E)
+            buf = torch.from_numpy(cells.reshape(-1)).to(DEV)
+            p, m, v = L.state_views(buf)
+        else:
+            p = torch.from_numpy(master0.copy()).to(DEV)
+            m = torch.zeros(psi, device=DEV)
+            v = torch.zeros(psi, device=DEV)
         out = torch.zeros(psi, dtype=torch.int16, device=DEV)
         g = torch.empty(psi, device=DEV)
         partials = torch.empty(sum(tiles), dtype=torch.float64, device=DEV)
@@ -125,7 +139,9 @@ def test_ddp_bucket_as_ready_equals_whole_range():
             if mode == "buckets":
                 strategies.step(oc, strategies.AdamConfig(weight_decay=0.01, decoupled=True,
                                                           max_grad_norm=1.0), t + 1, grads)
-        runs[mode] = (h16(out), p.cpu().numpy(), coefs)
+        master = (buf.cpu().numpy().reshape(-1, 3, E)[:, 0, :].reshape(-1)[:psi].copy() if E
+                  else p.cpu().numpy())
+        runs[mode] = (h16(out), master, coefs)
     assert runs["buckets"][2] == runs["whole"][2]
     assert np.array_equal(runs["buckets"][0], runs["whole"][0])
     assert np.array_equal(runs["buckets"][1].view(np.uint32), runs["whole"][1].view(np.uint32))
