@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from oracle import _c, strategies
-from chunked import grad_buffer
+from chunked import grad_buffer, state_buffer, state_pos
 from gather_check import assert_gathered
 from synthetic import WORKLOADS, grad_bits, master_init, peer_bits, small_workload
 
@@ -146,16 +146,20 @@ def _sweep_case(units, n, r, cap, two, E, GE, seed):
                 assert np.array_equal(seg, peers_h[u][k]), (u, k)
 
 
-def test_sweep_ring_of_two_buffers_full_llama70b():
+@pytest.mark.parametrize("E", [0, 8192])
+def test_sweep_ring_of_two_buffers_full_llama70b(E):
     """The whole 81-unit sweep at N = 64 with K = 2 and two unit buffers
     reused in turn, every unit's 64 rank gradients read from one chunked
-    receive buffer (the bench's configuration); every unit's state sampled
-    against the oracle, the last two units' buffers checked."""
+    receive buffer, master, m and v as three arrays or (E > 0, the bench's
+    configuration) one chunked buffer; every unit's state sampled against
+    the oracle, the last two units' buffers checked."""
     w = WORKLOADS[4]
     n, r = w.n_ranks, w.n_ranks - 1
     units = list(w.units)
     U = len(units)
     L = zs.shard_init("fsdp", n, r, units)
+    if E:
+        L = L.chunk_state(E)
     q = [L.query(u) for u in range(U)]
     smax = max(x["shard_len"] for x in q)
     GE = zs.GRAD_CHUNK_DEFAULT
@@ -165,18 +169,34 @@ def test_sweep_ring_of_two_buffers_full_llama70b():
     recv, _ = grad_buffer(smax, n, GE, lambda k: grads[k])
     peers = [peer_bits(w, k, smax, device=DEV) for k in range(n)]
     ring = [torch.zeros(n * smax, dtype=torch.int16, device=DEV) for _ in range(2)]
-    master = torch.empty(L.shard_len, device=DEV)
+    master0 = torch.empty(L.shard_len, device=DEV)
     for u, x in enumerate(q):
         so, su = x["shard_off"], x["shard_len"]
-        master[so:so + su] = master_init(w, su, device=DEV, rank=r, unit=u)
-    m = torch.zeros(L.shard_len, device=DEV)
-    v = torch.zeros(L.shard_len, device=DEV)
+        master0[so:so + su] = master_init(w, su, device=DEV, rank=r, unit=u)
+    if E:
+        sbuf = state_buffer(L, master0)
+        master, m, v = L.state_views(sbuf)
+        arrays = None
+    else:
+        master, m, v = (master0, torch.zeros(L.shard_len, device=DEV),
+                        torch.zeros(L.shard_len, device=DEV))
+        arrays = (master, m, v)
+
+    def at(k, i):
+        # part k (master, m, v) of the state at shard indices i, the positions
+        # checked on the host against the buffer they index
+        if arrays is None:
+            p, t = state_pos(E, i) + k * E, sbuf
+        else:
+            p, t = i, arrays[k]
+        assert p.min() >= 0 and p.max() < t.numel()
+        return t[torch.from_numpy(p).to(DEV)]
     rng = np.random.default_rng(44)
     samp = {}
     for u, x in enumerate(q):
         idx = np.unique(np.concatenate([rng.integers(0, x["shard_len"], 2048),
                                         [0, x["shard_len"] - 1]])).astype(np.int64)
-        samp[u] = (idx, h32(master[x["shard_off"] + torch.from_numpy(idx).to(DEV)]).copy())
+        samp[u] = (idx, h32(at(0, x["shard_off"] + idx)).copy())
     gsamp = {}
     for u, x in enumerate(q):
         t_idx = torch.from_numpy(samp[u][0]).to(DEV)
@@ -194,14 +214,14 @@ def test_sweep_ring_of_two_buffers_full_llama70b():
         v_h = np.zeros(idx.size, np.float32)
         par_h = np.empty(idx.size, np.uint16)
         _c.rank_step(hp, gsamp[u], 1.0, p_h, m_h, v_h, par_h)
-        t_idx = torch.from_numpy(idx).to(DEV) + x["shard_off"]
-        assert np.array_equal(h32(master[t_idx]).view(np.uint32), p_h.view(np.uint32)), u
-        assert np.array_equal(h32(m[t_idx]).view(np.uint32), m_h.view(np.uint32)), u
-        assert np.array_equal(h32(v[t_idx]).view(np.uint32), v_h.view(np.uint32)), u
+        ai = x["shard_off"] + idx
+        assert np.array_equal(h32(at(0, ai)).view(np.uint32), p_h.view(np.uint32)), u
+        assert np.array_equal(h32(at(1, ai)).view(np.uint32), m_h.view(np.uint32)), u
+        assert np.array_equal(h32(at(2, ai)).view(np.uint32), v_h.view(np.uint32)), u
         if u >= U - 2:
             s = x["shard_len"]
-            buf = ring[u % 2]
-            own = h16(buf[r * s + torch.from_numpy(idx).to(DEV)])
+            ub = ring[u % 2]
+            own = h16(ub[r * s + torch.from_numpy(idx).to(DEV)])
             assert np.array_equal(own, par_h), u
-            assert_gathered(buf, 0, s, [None if k == r else peers[k] for k in range(n)], idx,
+            assert_gathered(ub, 0, s, [None if k == r else peers[k] for k in range(n)], idx,
                             f"sweep unit {u} gather")
