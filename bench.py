@@ -82,11 +82,11 @@ def parse():
                          "chunks (zero_layout_chunk_state); 0 keeps three arrays; default: "
                          "the library's ZERO_STATE_CHUNK_DEFAULT")
     ap.add_argument("--grad-chunk", type=int, default=None, metavar="E",
-                    help="the rank gradients of the 7B step, of each rank of --config 1 and of "
-                         "each unit of --config 4 as one receive buffer of rows of E elements "
-                         "per rank (zero_grads.chunk); 0 keeps one buffer per rank (full-"
-                         "indexed for --config 1); default: the library's "
-                         "ZERO_GRAD_CHUNK_DEFAULT")
+                    help="the rank gradients of the 7B step, of each rank of --config 1, of "
+                         "the peers of --config 3 and of each unit of --config 4 as one "
+                         "receive buffer of rows of E elements per rank (zero_grads.chunk); 0 "
+                         "keeps one buffer per rank (full-indexed for --config 1); default: "
+                         "the library's ZERO_GRAD_CHUNK_DEFAULT")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="instead of a step, run a plain bf16 copy of BYTES through "
                          "zero_gather_params (counter calibration)")
@@ -687,8 +687,26 @@ def run_megatron(args, torch, zs, np):
     S, P = L.shard_len, L.flat_len
     main = torch.zeros(P, device=dev)
     micro = grad_bits(w, 0, r, P, device=dev, kind=KIND_MICRO)
-    peers32 = [torch.empty(S, device=dev).normal_(0, 1e-3) for _ in range(N - 1)]
-    G = zs.Grads(peers32 + [main], zs.FP32, [zs.INDEX_SHARD] * (N - 1) + [zs.INDEX_FULL])
+    GE = grad_chunk(args, zs)
+    if GE:
+        # the 7 peers' fp32 shards in one receive buffer (rows of GE elements
+        # per rank; the own rank's slot unused) beside the own full-indexed
+        # main gradient
+        rows = -(-S // GE)
+        recv = torch.zeros(rows * N * GE, device=dev)
+        assert recv.numel() == L.grad_len(GE)
+        col = torch.zeros(rows * GE, device=dev)
+        for q in range(N - 1):
+            col[:S].normal_(0, 1e-3)
+            recv.view(rows, N, GE)[:, q, :].copy_(col.view(rows, GE))
+        del col
+        G = zs.Grads.chunked(recv, N, GE, zs.FP32, full={r: main})
+        grad_layout = (f"own fp32 main gradient full-indexed; the {N - 1} peers' fp32 shards in "
+                       f"one buffer of rows of {GE} elements per rank, {N} rank slots per row")
+    else:
+        peers32 = [torch.empty(S, device=dev).normal_(0, 1e-3) for _ in range(N - 1)]
+        G = zs.Grads(peers32 + [main], zs.FP32, [zs.INDEX_SHARD] * (N - 1) + [zs.INDEX_FULL])
+        grad_layout = f"own fp32 main gradient full-indexed; {N - 1} fp32 peer shard buffers"
     master, m, v = State(torch, L, master_init(w, S, device=dev, rank=r)).views
     replica = torch.empty(P, dtype=torch.int16, device=dev)
     peers16 = [torch.full((S,), q + 1, dtype=torch.int16, device=dev) for q in range(N - 1)]
@@ -718,7 +736,7 @@ def run_megatron(args, torch, zs, np):
                     "over the whole buffer + fp32 reduce + Adam + bf16 + gather of 7 peers "
                     "(the step also zeroes main_grad with torch, untimed per phase)",
                     psi=w.psi, n_ranks=N, rank=r, shard_elems=S, micro_batches=w.micro_batches,
-                    state_layout=state_desc(L.state_chunk))
+                    state_layout=state_desc(L.state_chunk), grad_layout=grad_layout)
     out["optimizer_only_shard_params_per_s"] = S / (opt_ms * 1e-3)
     out["kernels"] = kern
     dom = max(("accumulate_fp32", acc_b), ("fused_fp32_reduce_adam_cast", fb),

@@ -421,11 +421,17 @@ class Grads:
         self._checked = None
 
     @classmethod
-    def chunked(cls, buf, n: int, chunk: int, dtype: int = BF16):
+    def chunked(cls, buf, n: int, chunk: int, dtype: int = BF16, full=None):
         """N ranks' shard-indexed gradients interleaved in one buffer in
         chunks of `chunk` elements (Layout.grad_len long): rank q's pointer
-        is the buffer's start + q * chunk."""
-        return cls([buf[q * chunk:] for q in range(n)], dtype, INDEX_SHARD, chunk)
+        is the buffer's start + q * chunk.  `full` maps ranks whose
+        gradient is a full-indexed buffer of its own (a rank's own main
+        gradient) to that buffer; their slots in `buf` are not read."""
+        full = full or {}
+        bufs = [full[q] if q in full else buf[q * chunk:] for q in range(n)]
+        index = ([INDEX_FULL if q in full else INDEX_SHARD for q in range(n)] if full
+                 else INDEX_SHARD)
+        return cls(bufs, dtype, index, chunk)
 
     @property
     def chunk(self) -> int:

@@ -864,16 +864,25 @@ zero_status check_grads(const zero_layout *L, const zero_grads *g)
     if ((S + E - 1) / E > INT64_MAX / 4 / E / g->n)
         return fail(ZERO_ERR_INVALID_ARG, "chunked gradients of %lld elements per rank overflow",
                     (long long)S);
-    const char *base = static_cast<const char *>(g->ptrs[0]);
+    // The shard-indexed ranks share one receive buffer: rank q's pointer is
+    // the buffer's start + q chunks.  A full-indexed rank (a rank's own
+    // main gradient) keeps its own buffer, and its slot in the receive
+    // buffer is never read.
+    const char *base = nullptr;
     for (int q = 0; q < g->n; ++q) {
         if ((g->index ? g->index[q] : g->index_all) != ZERO_INDEX_SHARD)
+            continue;
+        const char *want = base ? base + (int64_t)q * E * (int64_t)elem : nullptr;
+        if (!base)
+            base = static_cast<const char *>(g->ptrs[q]) - (int64_t)q * E * (int64_t)elem;
+        else if (static_cast<const char *>(g->ptrs[q]) != want)
             return fail(ZERO_ERR_INVALID_ARG,
-                        "chunked gradients are shard-indexed (rank %d is full-indexed)", q);
-        if (static_cast<const char *>(g->ptrs[q]) != base + (int64_t)q * E * (int64_t)elem)
-            return fail(ZERO_ERR_INVALID_ARG,
-                        "chunked gradients: rank %d's pointer must be rank 0's + %d chunk elements",
+                        "chunked gradients: rank %d's pointer must be the receive buffer's "
+                        "start + %d chunk elements",
                         q, q);
     }
+    if (!base)
+        return fail(ZERO_ERR_INVALID_ARG, "chunked gradients need a shard-indexed rank");
     return ZERO_OK;
 }
 

@@ -115,14 +115,17 @@ typedef struct zero_layout zero_layout;
 /* The N ranks' gradient buffers for one call, all of one dtype (bf16 as raw
    uint16 bit patterns, or fp32).
 
-   Chunked gradients (chunk = E > 0): the N shard-indexed contributions to
-   this rank's part of the call's range sit in one buffer of ceil(S/E) rows,
-   each row holding E elements of rank 0, then E of rank 1, ..., then E of
-   rank N-1 (S = the range's shard length).  Rank q's gradient for element i
-   of the range (counted from its first element, as for every shard-indexed
-   buffer) is at ptrs[0] + (i / E) N E + q E + i % E; ptrs[q] must be
-   ptrs[0] + qE elements and every rank shard-indexed (ZERO_ERR_INVALID_ARG
-   otherwise).  A per-unit call therefore takes a per-unit receive buffer.
+   Chunked gradients (chunk = E > 0): the shard-indexed contributions to
+   this rank's part of the call's range sit in one receive buffer R of
+   ceil(S/E) rows, each row holding E elements of rank 0, then E of rank 1,
+   ..., then E of rank N-1 (S = the range's shard length).  Rank q's
+   gradient for element i of the range (counted from its first element, as
+   for every shard-indexed buffer) is at R + (i / E) N E + q E + i % E, and
+   ptrs[q] must be R + qE elements (ZERO_ERR_INVALID_ARG otherwise; at
+   least one rank shard-indexed).  A full-indexed rank -- a rank's own
+   main gradient, as in the Megatron distributed optimizer -- keeps its own
+   buffer at ptrs[q]; its slot in R is never read.  A per-unit call
+   therefore takes a per-unit receive buffer.
    The same bytes and sums as N separate buffers, read from one region
    instead of N: it is the receive buffer a rank would let its peers fill
    in a reduce-scatter.  On one MI355X the 7B / N = 8 fused step (state

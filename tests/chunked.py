@@ -23,20 +23,34 @@ def state_buffer(L, master):
     return buf
 
 
-def grad_buffer(S, n, E, draw, tidx=None):
+def grad_buffer(S, n, E, draw, tidx=None, hole=()):
     """One receive buffer of S elements per rank for n ranks in chunks of E
     (ceil(S / E) rows of n chunks, as Layout.grad_len counts) filled with
-    draw(q), a device int16 tensor of S elements, for each rank q; and,
-    with tidx (a device index tensor), each rank's values at those
-    positions as host uint16 arrays."""
+    draw(q), a device tensor of S elements (int16 bf16 bits or fp32), for
+    each rank q not in `hole`; the chunks of the ranks in `hole` (a rank's
+    own full-indexed gradient, kept elsewhere) hold NaN.  With tidx (a
+    device index tensor), also each drawn rank's values at those positions
+    as host arrays (uint16 for bf16), None for a hole."""
     rows = -(-S // E)
-    first = draw(0)
-    buf = torch.zeros(rows * n * E, dtype=torch.int16, device=first.device)
-    col = torch.zeros(rows * E, dtype=torch.int16, device=first.device)
+    buf = col = None
     samples = []
     for q in range(n):
-        col[:S] = first if q == 0 else draw(q)
+        if q in hole:
+            samples.append(None)
+            continue
+        x = draw(q)
+        if buf is None:
+            buf = torch.zeros(rows * n * E, dtype=x.dtype, device=x.device)
+            col = torch.zeros(rows * E, dtype=x.dtype, device=x.device)
+        col[:S] = x
+        del x
         if tidx is not None:
-            samples.append(col[tidx].cpu().numpy().view(np.uint16))
+            h = col[tidx].cpu().numpy()
+            samples.append(h.view(np.uint16) if h.dtype == np.int16 else h)
         buf.view(rows, n, E)[:, q, :].copy_(col.view(rows, E))
+    for q in hole:
+        if buf.dtype == torch.int16:
+            buf.view(rows, n, E)[:, q, :] = 0x7FC0
+        else:
+            buf.view(rows, n, E)[:, q, :] = float("nan")
     return buf, samples

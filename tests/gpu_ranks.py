@@ -163,17 +163,25 @@ class GpuRanks:
             return xs          # host arrays; chunked per call by chunked_grads
         return [dev_f32(x) if dtype == zs.FP32 else dev_bf16(x) for x in xs]
 
-    def chunked_grads(self, xs, dtype, lo=0, hi=None):
+    def chunked_grads(self, xs, dtype, lo=0, hi=None, index_modes=None, flo=0):
         """zs.Grads over one chunked receive buffer holding shard elements
-        [lo, hi) of every rank's shard-indexed gradient."""
-        buf = chunk_grads([x[lo:hi] for x in xs], self.GE)
-        d = dev_f32(buf) if dtype == zs.FP32 else dev_bf16(buf)
-        return zs.Grads.chunked(d, self.n, self.GE, dtype)
+        [lo, hi) of every shard-indexed rank's gradient.  A full-indexed
+        rank keeps its own buffer from flat element `flo` on; its slot in
+        the receive buffer holds NaN, which no result may show."""
+        full = [q for q in range(self.n)
+                if index_modes is not None and index_modes[q] == zs.INDEX_FULL]
+        k = len(next(x for q, x in enumerate(xs) if q not in full)[lo:hi])
+        hole = (np.full(k, np.nan, np.float32) if dtype == zs.FP32 else
+                np.full(k, 0x7FC0, np.uint16))
+        buf = chunk_grads([hole if q in full else x[lo:hi] for q, x in enumerate(xs)], self.GE)
+        dev = dev_f32 if dtype == zs.FP32 else dev_bf16
+        own = {q: dev(xs[q][flo:]) for q in full}
+        return zs.Grads.chunked(dev(buf), self.n, self.GE, dtype, full=own)
 
     def grads_of(self, bufs, dtype, index_modes):
         """zs.Grads over rank_grads' result (one chunked buffer, or N)."""
         if self.GE:
-            return self.chunked_grads(bufs, dtype)
+            return self.chunked_grads(bufs, dtype, index_modes=index_modes)
         return zs.Grads(bufs, dtype, list(index_modes))
 
     def step_fused(self, t, grads_t, index_modes, dtype=None, per_unit=False):
@@ -192,8 +200,10 @@ class GpuRanks:
                     hi = so + sum(L.query(u)["shard_len"] for u in range(u0, u1))
                     if hi == so:
                         continue
-                    G = self.chunked_grads(bufs, dtype, so, hi)
-                    assert G._keep[0].numel() == L.grad_len(self.GE, u0, u1)
+                    G = self.chunked_grads(bufs, dtype, so, hi, index_modes, fo)
+                    q0 = index_modes.index(zs.INDEX_SHARD)
+                    assert (G._keep[q0].numel() + q0 * self.GE ==
+                            L.grad_len(self.GE, u0, u1))
                     st = self.state[r] if self.E else [x[so:] for x in self.state[r]]
                     zs.adam_step(L, u0, u1, c, *st, self.full[fo:], zs.INDEX_FULL, grads=G)
                 continue

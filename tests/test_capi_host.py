@@ -724,9 +724,10 @@ def test_chunked_grads_reject_bad_chunks(E):
 
 
 def test_chunked_grads_need_rank_pointers_one_chunk_apart():
-    # rank q's pointer is rank 0's + q E elements (bf16: 2 bytes, fp32: 4),
-    # every rank shard-indexed; anything else is refused on the host, by the
-    # fused step, the reduce and the no-allocation call alike
+    # every shard-indexed rank q's pointer is the receive buffer's start
+    # + q E elements (bf16: 2 bytes, fp32: 4); anything else is refused on
+    # the host, by the fused step, the reduce and the no-allocation call
+    # alike
     L, E = _layout(), 1024
     cfg = zs.adam_cfg(step=1)
     bad = [_chunked_grads(4, E, step=4 * E),                       # fp32 spacing for bf16
@@ -737,17 +738,35 @@ def test_chunked_grads_need_rank_pointers_one_chunk_apart():
         e = _err(_adam, L, grads=g)
         assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
     full = zs.Grads([FAKE + 2 * E * q for q in range(4)], zs.BF16, zs.INDEX_FULL, E)
-    mixed = zs.Grads([FAKE + 2 * E * q for q in range(4)], zs.BF16,
-                     [zs.INDEX_SHARD] * 3 + [zs.INDEX_FULL], E)
-    for g in (full, mixed):
-        e = _err(_adam, L, grads=g)
-        assert e.status == zs.ERR_INVALID_ARG and "shard-indexed" in str(e)
+    e = _err(_adam, L, grads=full)
+    assert e.status == zs.ERR_INVALID_ARG and "need a shard-indexed rank" in str(e)
     g = bad[1]
     e = _err(zs.reduce_shard, L, 0, 2, g, FAKE, stream=0)
     assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
     e = _err(lambda *a: zs.adam_step_clip_noalloc(*a, stream=0), L, 0, 2, cfg, 1.0, g, FAKE,
              FAKE, FAKE, FAKE, FAKE)
     assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
+
+
+def test_chunked_grads_beside_a_full_indexed_own_gradient():
+    # a full-indexed rank (a rank's own main gradient) keeps a buffer of its
+    # own; the shard-indexed ranks' pointers are still the receive buffer's
+    # start + q E, the receive buffer's start found from any of them.  An
+    # empty unit range runs every check and launches nothing.
+    L, E, R, OWN = _layout(), 1024, FAKE, FAKE + (1 << 30)
+    for own in (0, 1, 3):
+        ptrs = [OWN if q == own else R + 4 * E * q for q in range(4)]
+        idx = [zs.INDEX_FULL if q == own else zs.INDEX_SHARD for q in range(4)]
+        _adam(L, 1, 1, grads=zs.Grads(ptrs, zs.FP32, idx, E))
+        # any one of the three shard-indexed ranks out of place is refused
+        for q in (x for x in range(4) if x != own):
+            moved = [p + 4 * E if k == q else p for k, p in enumerate(ptrs)]
+            e = _err(_adam, L, 1, 1, grads=zs.Grads(moved, zs.FP32, idx, E))
+            assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e), (own, q)
+        e = _err(zs.reduce_shard, L, 1, 1, zs.Grads(
+            [p + 4 if k == (own + 1) % 4 else p for k, p in enumerate(ptrs)], zs.FP32, idx, E),
+            FAKE, stream=0)
+        assert e.status == zs.ERR_INVALID_ARG and "chunked gradients" in str(e)
 
 
 def test_chunked_grads_counts_in_the_binding():
@@ -799,6 +818,17 @@ def test_chunked_grads_counts_in_the_binding():
     with pytest.raises(ValueError, match="gradient buffer of rank 3 holds 999 elements, "
                                          "the call touches 1000"):
         step(zs.Grads.chunked(Dev(L.grad_len(E) - 1), N, E))
+    # rank 1's own full-indexed gradient beside the receive buffer: its
+    # pointer is its own buffer's, its index full, and it must cover the
+    # range's flat length (1024 elements) rather than the chunked count
+    own = Dev(1024, 1 << 20)
+    G = zs.Grads.chunked(whole, N, E, full={1: own})
+    assert [b.data_ptr() for b in G._keep] == [FAKE, own.data_ptr(), FAKE + 4 * E, FAKE + 6 * E]
+    assert [G._index[q] for q in range(N)] == [zs.INDEX_SHARD, zs.INDEX_FULL, zs.INDEX_SHARD,
+                                               zs.INDEX_SHARD]
+    with pytest.raises(ValueError, match="gradient buffer of rank 1 holds 1023 elements, "
+                                         "the call touches 1024"):
+        step(zs.Grads.chunked(whole, N, E, full={1: Dev(1023, 1 << 20)}))
 
 
 def test_sweep_checks_every_units_chunked_gradients_before_launching():

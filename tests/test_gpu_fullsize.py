@@ -176,8 +176,14 @@ def test_config1_gpt2_small_clip_all_ranks(GE):
 
 # ------------------------------------------------------------ config 3 --
 
-def test_config3_megatron_full_size_sampled():
+@pytest.mark.parametrize("peers", ["separate", "chunked"])
+def test_config3_megatron_full_size_sampled(peers):
+    """The Megatron distributed-optimizer step at full size: the own main
+    gradient accumulated over the whole buffer, the 7 peers' fp32 shards in
+    buffers of their own (GE = 0) or in one chunked receive buffer beside
+    the full-indexed own main gradient (GE > 0, the benchmark's launch)."""
     w = WORKLOADS[3]
+    GE = zs.GRAD_CHUNK_DEFAULT if peers == "chunked" else 0
     n, r = w.n_ranks, w.n_ranks - 1
     E = zs.STATE_CHUNK_DEFAULT
     L = zs.shard_init("megatron_do", n, r, list(w.units)).chunk_state(E)
@@ -222,10 +228,15 @@ def test_config3_megatron_full_size_sampled():
     pos = torch.from_numpy(chunk_pos(E, idx)).to(DEV)
     replica = torch.zeros(P, dtype=torch.int16, device=DEV)
     p_h = host_f32(buf[pos]).copy()
-    ranks_fp32 = peers + [main]
-    index = [zs.INDEX_SHARD] * (n - 1) + [zs.INDEX_FULL]
-    zs.adam_step(L, 0, 1, cfg_of(w, 1), master, m, v, replica, zs.INDEX_FULL,
-                 grads=zs.Grads(ranks_fp32, zs.FP32, index))
+    if GE:
+        recv, _ = grad_buffer(S, n, GE, lambda q: peers[q], hole=(n - 1,))
+        assert recv.numel() == L.grad_len(GE)
+        del peers
+        G = zs.Grads.chunked(recv, n, GE, zs.FP32, full={n - 1: main})
+    else:
+        index = [zs.INDEX_SHARD] * (n - 1) + [zs.INDEX_FULL]
+        G = zs.Grads(peers + [main], zs.FP32, index)
+    zs.adam_step(L, 0, 1, cfg_of(w, 1), master, m, v, replica, zs.INDEX_FULL, grads=G)
     peer_bf16 = [peer_bits(w, q, S, device=DEV) for q in range(n - 1)]
     zs.gather_params(L, 0, 1, peer_bf16 + [None], replica)
     torch.cuda.synchronize()

@@ -250,17 +250,43 @@ def test_per_unit_calls_on_chunked_grads(E, GE):
         g.check(f"per-unit chunked grads E={E} GE={GE} step {t + 1}")
 
 
-def test_fp32_chunked_grads_megatron():
-    """fp32 rank gradients in one chunked buffer through the fused path."""
+@pytest.mark.parametrize("modes", ["shard", "own"])
+def test_fp32_chunked_grads_megatron(modes):
+    """fp32 rank gradients in one chunked buffer through the fused path;
+    "own": the last rank's gradient full-indexed in a buffer of its own (a
+    rank's main gradient in the Megatron distributed optimizer), its slot
+    in the receive buffer NaN."""
     units, n = [8192 * 3 + 17], 8
     w = _w(units, n, "megatron_do", "none")
     master0, grads = draw(w, 2)
     oc = strategies.make_cluster("megatron_do", units, n, master0)
     g = GpuRanks(w, master0, oc, state_chunk=1024, grad_chunk=2048)
+    index = (_modes("shard", n) if modes == "shard" else
+             [zs.INDEX_SHARD] * (n - 1) + [zs.INDEX_FULL])
     for t in range(2):
         strategies.step(oc, oracle_cfg(w), t + 1, [[x] for x in grads[t]])
-        g.step_fused(t + 1, grads[t], _modes("shard", n), dtype=zs.FP32)
-        g.check(f"megatron fp32 chunked grads step {t + 1}")
+        g.step_fused(t + 1, grads[t], index, dtype=zs.FP32)
+        g.check(f"megatron fp32 chunked grads ({modes}) step {t + 1}")
+
+
+@pytest.mark.parametrize("per_unit", [False, True])
+@pytest.mark.parametrize("units,n,E,GE", [
+    ([5000, 333, 20000], 4, 8192, 1024),
+    ([2048 * 3 + 5, 7], 5, 0, 8),
+])
+def test_chunked_grads_beside_full_indexed_ranks(units, n, E, GE, per_unit):
+    """bf16: the even ranks full-indexed in buffers of their own (rank 0
+    among them, so the receive buffer's start comes from rank 1), the odd
+    ranks in one chunked receive buffer whose even slots hold NaN; whole
+    range and one call per unit."""
+    w = _w(units, n, "zero2", "adamw")
+    master0, grads = draw(w, 2)
+    oc = strategies.make_cluster("zero2", units, n, master0)
+    g = GpuRanks(w, master0, oc, state_chunk=E, grad_chunk=GE)
+    for t in range(2):
+        strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
+        g.step_fused(t + 1, grads[t], _modes("mixed", n), per_unit=per_unit)
+        g.check(f"{units} N={n} mixed chunked per_unit={per_unit} step {t + 1}")
 
 
 def test_two_pass_clip_on_chunked_grads():
