@@ -5,9 +5,11 @@ modes and both memory formats drawn together rather than one at a time.
 Each case draws: 1-6 units of 0 to 20,000 elements (ragged tails, empty
 units, slices that are not multiples of 4), N from 1 to 64, a sharded
 strategy, Adam / AdamW / L2, a state chunk (three arrays or 4 to 8192), a
-gradient chunk (one buffer per rank, or rows of 4 to 4096 elements per rank,
-then every rank shard-indexed), per-rank index modes otherwise, and whole-
-range or per-unit calls; two steps each.
+gradient chunk (one buffer per rank, or rows of 4 to 4096 elements per rank),
+per-rank index modes (with a gradient chunk: every rank shard-indexed, or,
+from a second generator, a random set of ranks full-indexed in buffers of
+their own beside the receive buffer, at least one rank left in it), and
+whole-range or per-unit calls; two steps each.
 """
 import numpy as np
 import pytest
@@ -46,13 +48,17 @@ def _case(seed):
     GE = int(rng.choice([0, 0, 4, 16, 256, 4096]))
     if GE:
         modes = [zs.INDEX_SHARD] * n
+        alt = np.random.default_rng(5000 + seed)
+        if n > 1 and alt.integers(0, 2):
+            for q in alt.choice(n, int(alt.integers(1, n)), replace=False):
+                modes[int(q)] = zs.INDEX_FULL
     else:
         modes = [int(x) for x in rng.choice([zs.INDEX_FULL, zs.INDEX_SHARD], n)]
     per_unit = bool(rng.integers(0, 2))
     return units, n, strategy, decay, E, GE, modes, per_unit
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_configuration(seed):
     units, n, strategy, decay, E, GE, modes, per_unit = _case(seed)
     kw = {"adamw": dict(weight_decay=0.01, decoupled=True),
