@@ -3,8 +3,8 @@
 The sweep must give exactly what per-unit zero_adam_step + zero_gather_params
 give -- which the oracle pins -- for every in-flight cap, on two streams or
 one, with distinct per-unit buffers or a ring of reused ones, per-unit rank
-gradients as N buffers or one chunked receive buffer, on fixed and on ten
-seeded random configurations.  Also the full
+gradients as N buffers or one chunked receive buffer, bf16 or fp32, on fixed
+and on ten seeded random configurations.  Also the full
 Llama-70B sweep (N = 64, 81 units) with a ring of two unit buffers and
 chunked receive buffers, sampled.
 """
@@ -36,16 +36,18 @@ def h32(t):
     return t.cpu().numpy()
 
 
-@pytest.mark.parametrize("cap,two,E,GE", [(0, True, 0, 0), (1, True, 0, 0), (2, True, 0, 0),
-                                          (3, True, 0, 0), (2, False, 0, 0), (2, True, 16, 0),
-                                          (0, True, 2048, 0), (2, True, 0, 4), (1, True, 16, 64),
-                                          (2, False, 2048, 1024)])
-def test_sweep_small_ragged_matches_oracle(cap, two, E, GE):
+@pytest.mark.parametrize("cap,two,E,GE,fp32", [
+    (0, True, 0, 0, False), (1, True, 0, 0, False), (2, True, 0, 0, False),
+    (3, True, 0, 0, False), (2, False, 0, 0, False), (2, True, 16, 0, False),
+    (0, True, 2048, 0, False), (2, True, 0, 4, False), (1, True, 16, 64, False),
+    (2, False, 2048, 1024, False), (2, True, 0, 0, True), (1, True, 2048, 64, True)])
+def test_sweep_small_ragged_matches_oracle(cap, two, E, GE, fp32):
     """E > 0: master, m and v in one chunked buffer of E-element chunks.
     GE > 0: each unit's rank gradients in one chunked receive buffer of
-    GE-element rows per rank."""
+    GE-element rows per rank.  fp32: the rank gradients as fp32 (the bf16
+    draws widened, so the sums and the oracle's results are the same)."""
     _sweep_case([4096, 100, 8192 + 3, 8, 0, 64 * 33, 5000, 2048 * 3], 8, 5, cap, two, E, GE,
-                seed=cap)
+                seed=cap, fp32=fp32)
 
 
 @pytest.mark.parametrize("seed", range(10))
@@ -65,7 +67,7 @@ def test_sweep_random_configuration(seed):
     _sweep_case(units, n, r, cap, two, E, GE, seed=100 + seed)
 
 
-def _sweep_case(units, n, r, cap, two, E, GE, seed):
+def _sweep_case(units, n, r, cap, two, E, GE, seed, fp32=False):
     w = small_workload(units, n, "fsdp", steps=2, cfg=10, weight_decay=0.01, decoupled=True)
     psi = sum(units)
     master0 = master_init(w, psi).numpy()
@@ -100,6 +102,10 @@ def _sweep_case(units, n, r, cap, two, E, GE, seed):
         grads = [grad_bits(w, t, k, psi).numpy().view(np.uint16) for k in range(n)]
         strategies.step(oc, strategies.AdamConfig(weight_decay=0.01, decoupled=True), t + 1, grads)
         padded = [strategies.pad(olay, g) for g in grads]
+        if fp32:
+            # bf16 bit patterns widened to fp32 (exact)
+            padded = [(p.astype(np.uint32) << 16).view(np.float32) for p in padded]
+        gdt = np.float32 if fp32 else np.uint16
         ios = []
         for u, x in enumerate(q):
             b, s = x["rank_flat_off"], x["shard_len"]
@@ -107,21 +113,27 @@ def _sweep_case(units, n, r, cap, two, E, GE, seed):
                 # rows of GE elements of each rank's slice, in rank order; a
                 # zero-size unit still gets pointers one chunk apart
                 rows = max(1, -(-s // GE))
-                cells = np.zeros((rows, n, GE), np.uint16)
+                cells = np.zeros((rows, n, GE), gdt)
                 for k, p in enumerate(padded):
-                    col = np.zeros(rows * GE, np.uint16)
+                    col = np.zeros(rows * GE, gdt)
                     col[:s] = p[b:b + s]
                     cells[:, k, :] = col.reshape(rows, GE)
-                recv = torch.from_numpy(cells.reshape(-1).view(np.int16)).to(DEV)
+                flat = cells.reshape(-1)
+                recv = torch.from_numpy(flat if fp32 else flat.view(np.int16)).to(DEV)
                 rg = [recv[k * GE:] for k in range(n)]
+            elif s:
+                rg = [torch.from_numpy((p[b:b + s] if fp32 else
+                                        p[b:b + s].view(np.int16)).copy()).to(DEV)
+                      for p in padded]
             else:
                 # a zero-size unit still needs non-NULL rank buffers (NULL =
                 # missing replica)
-                rg = [torch.from_numpy(p[b:b + max(1, s)].view(np.int16).copy()).to(DEV)
-                      for p in padded] if s else [fulls[u]] * n
+                rg = [torch.zeros(1, dtype=torch.float32 if fp32 else torch.int16,
+                                  device=DEV)] * n
             ios.append((rg, [None if k == r else peers[u][k] for k in range(n)], fulls[u]))
         zs.fsdp_sweep(L, 0, U, zs.adam_cfg(weight_decay=0.01, decoupled=True, step=t + 1),
-                      zs.BF16, ios, master, m, v, cap, gather_stream=gs, grad_chunk=GE)
+                      zs.FP32 if fp32 else zs.BF16, ios, master, m, v, cap, gather_stream=gs,
+                      grad_chunk=GE)
         torch.cuda.synchronize()
     st = strategies.full_state(oc, padded=True)
     if E:
