@@ -270,23 +270,27 @@ def test_fp32_chunked_grads_megatron(modes):
 
 
 @pytest.mark.parametrize("per_unit", [False, True])
-@pytest.mark.parametrize("units,n,E,GE", [
-    ([5000, 333, 20000], 4, 8192, 1024),
-    ([2048 * 3 + 5, 7], 5, 0, 8),
+@pytest.mark.parametrize("units,n,E,GE,which", [
+    ([5000, 333, 20000], 4, 8192, 1024, "even"),
+    ([2048 * 3 + 5, 7], 5, 0, 8, "even"),
+    ([3000, 9001], 6, 64, 16, "last"),
 ])
-def test_chunked_grads_beside_full_indexed_ranks(units, n, E, GE, per_unit):
-    """bf16: the even ranks full-indexed in buffers of their own (rank 0
-    among them, so the receive buffer's start comes from rank 1), the odd
-    ranks in one chunked receive buffer whose even slots hold NaN; whole
-    range and one call per unit."""
+def test_chunked_grads_beside_full_indexed_ranks(units, n, E, GE, which, per_unit):
+    """bf16: some ranks full-indexed in buffers of their own, the others in
+    one chunked receive buffer whose unused slots hold NaN; whole range and
+    one call per unit.  "even": the even ranks full-indexed (rank 0 among
+    them, so the buffer's start comes from rank 1); "last": every rank but
+    the last full-indexed, so one rank alone fixes the buffer's start."""
     w = _w(units, n, "zero2", "adamw")
     master0, grads = draw(w, 2)
     oc = strategies.make_cluster("zero2", units, n, master0)
     g = GpuRanks(w, master0, oc, state_chunk=E, grad_chunk=GE)
+    modes = (_modes("mixed", n) if which == "even" else
+             [zs.INDEX_FULL] * (n - 1) + [zs.INDEX_SHARD])
     for t in range(2):
         strategies.step(oc, oracle_cfg(w), t + 1, grads[t])
-        g.step_fused(t + 1, grads[t], _modes("mixed", n), per_unit=per_unit)
-        g.check(f"{units} N={n} mixed chunked per_unit={per_unit} step {t + 1}")
+        g.step_fused(t + 1, grads[t], modes, per_unit=per_unit)
+        g.check(f"{units} N={n} {which} full-indexed, chunked per_unit={per_unit} step {t + 1}")
 
 
 def test_two_pass_clip_on_chunked_grads():
