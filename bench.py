@@ -95,16 +95,24 @@ def parse():
 
 class Phases:
     """HIP-event timing of named phases on one stream; several launches of
-    one phase in a step are summed, and each launch is also kept."""
+    one phase in a step are summed, and each launch is also kept.  A phase
+    run with chain=True starts at the previous phase's end event instead of
+    an event of its own: for launches issued back to back with nothing else
+    enqueued between them, it halves the events (each costs a few
+    microseconds of stream time, which adds up over short kernels)."""
 
     def __init__(self, torch, stream):
         self.torch, self.stream = torch, stream
         self.marks = []        # (name, start_event, end_event) in launch order
 
-    def run(self, name, fn):
+    def run(self, name, fn, chain=False):
         E = self.torch.cuda.Event
-        a, b = E(enable_timing=True), E(enable_timing=True)
-        a.record(self.stream)
+        if chain and self.marks:
+            a = self.marks[-1][2]
+        else:
+            a = E(enable_timing=True)
+            a.record(self.stream)
+        b = E(enable_timing=True)
         fn()
         b.record(self.stream)
         self.marks.append((name, a, b))
@@ -137,11 +145,11 @@ def timed(args, torch, step):
     return 1e3 * wall / args.steps, ph.summary(args.steps)
 
 
-def phase(ph, name, fn):
+def phase(ph, name, fn, chain=False):
     if ph is None:
         fn()
     else:
-        ph.run(name, fn)
+        ph.run(name, fn, chain)
 
 
 def roofline(name, bytes_per_launch, ms_per_launch, traffic=None, counters=COUNTERS):
@@ -468,7 +476,7 @@ def run_tiny(args, torch, zs, np):
         for r in range(N):
             phase(ph, "fused_reduce_adam_cast",
                   lambda r=r: zs.adam_step(lays[r], 0, 1, cfg, *st[r], full, zs.INDEX_FULL,
-                                           grads=G))
+                                           grads=G), chain=r > 0)
 
     ms, kern = timed(args, torch, step)
     b = (2 * N + 26) * S
@@ -551,16 +559,18 @@ def run_gpt2_clip(args, torch, zs, np):
         t[0] += 1
         cfg = zs.adam_cfg(lr=w.lr, beta1=w.beta1, beta2=w.beta2, eps=w.eps,
                           weight_decay=w.weight_decay, decoupled=w.decoupled, step=t[0])
+        # the 17 launches go back to back: each one's events start at the
+        # previous one's end
         for r in range(N):
             phase(ph, "reduce_with_sumsq",
                   lambda r=r: zs.reduce_shard(lays[r], 0, U, Gr[r], gsh[r], partials[offs[r]:],
-                                              counts[r]))
+                                              counts[r]), chain=r > 0)
         phase(ph, "clip_coef", lambda: zs.clip_coef(partials, partials.numel(),
-                                                    w.max_grad_norm, coef))
+                                                    w.max_grad_norm, coef), chain=True)
         for r in range(N):
             phase(ph, "adamw_apply_cast",
                   lambda r=r: zs.adam_step(lays[r], 0, U, cfg, *st[r], full, zs.INDEX_FULL,
-                                           grad_fp32=gsh[r], clip_coef=coef))
+                                           grad_fp32=gsh[r], clip_coef=coef), chain=True)
 
     ms, kern = timed(args, torch, step)
     rb, ab = (2 * N + 4) * S, 30 * S
@@ -650,12 +660,12 @@ def run_gpt2_ddp_buckets(args, torch, zs, np):
         for u in reversed(range(U)):
             phase(ph, f"reduce_bucket_{u}",
                   lambda u=u: zs.reduce_shard(L, u, u + 1, Gu[u], g[fo[u]:], partials[offs[u]:],
-                                              tiles[u]))
+                                              tiles[u]), chain=u < U - 1)
         phase(ph, "clip_coef", lambda: zs.clip_coef(partials, partials.numel(),
-                                                    w.max_grad_norm, coef))
+                                                    w.max_grad_norm, coef), chain=True)
         phase(ph, "adamw_apply_cast",
               lambda: zs.adam_step(L, 0, U, cfg, p, m, v, out, zs.INDEX_FULL, grad_fp32=g,
-                                   clip_coef=coef))
+                                   clip_coef=coef), chain=True)
 
     ms, kern = timed(args, torch, step)
     for u in range(U):
@@ -780,9 +790,10 @@ def run_fsdp70b(args, torch, zs, np):
             so = 0 if SE else x["shard_off"]
             phase(ph, "fused_reduce64_adam_cast",
                   lambda u=u, so=so: zs.adam_step(L, u, u + 1, cfg, master[so:], m[so:], v[so:],
-                                                  full_unit, zs.INDEX_FULL, grads=G))
+                                                  full_unit, zs.INDEX_FULL, grads=G), chain=u > 0)
             phase(ph, "gather_63_peers",
-                  lambda u=u: zs.gather_params(L, u, u + 1, peers + [None], full_unit))
+                  lambda u=u: zs.gather_params(L, u, u + 1, peers + [None], full_unit),
+                  chain=True)
 
     ms, kern = timed(args, torch, step)
     fb, gb = (2 * N + 26) * S, 4 * (N - 1) * S

@@ -116,3 +116,56 @@ def test_bench_rank_grads_in_the_chunked_format(E):
             n = min(n, S - off)
             assert torch.equal(rg.rank(q, off, n), draws[q][off:off + n]), (q, off, n)
             assert torch.equal(views[q][off:off + n], draws[q][off:off + n])
+
+
+def test_phases_chain_shares_boundary_events():
+    # three back-to-back launches of 5, 7 and 11 time units: unchained, six
+    # events; chained after the first, four, with each launch's duration
+    # running from the previous one's end event to its own
+    sys.path.insert(0, ROOT)
+    import bench
+
+    clock = [0.0]
+    recorded = []
+
+    class Event:
+        def __init__(self, enable_timing=False):
+            self.t = None
+
+        def record(self, stream=None):
+            self.t = clock[0]
+            recorded.append(self)
+
+        def elapsed_time(self, end):
+            return end.t - self.t
+
+    class Cuda:
+        pass
+
+    class FakeTorch:
+        cuda = Cuda()
+
+    FakeTorch.cuda.Event = Event
+
+    def launch(d):
+        def fn():
+            clock[0] += d
+        return fn
+
+    for chain, n_events in ((False, 6), (True, 4)):
+        recorded.clear()
+        clock[0] = 0.0
+        ph = bench.Phases(FakeTorch, None)
+        for k, d in enumerate((5.0, 7.0, 11.0)):
+            clock[0] += 0.5                     # host-side gap before each launch
+            bench.phase(ph, "k", launch(d), chain=chain and k > 0)
+        assert len(recorded) == n_events
+        s = ph.summary(1)["k"]
+        assert s["launches_per_step"] == 3
+        if chain:
+            # the gaps before the 2nd and 3rd launches fall inside them
+            assert (s["ms_per_launch_min"], s["ms_per_launch_max"]) == (5.0, 11.5)
+            assert s["ms_per_step"] == 5.0 + 7.5 + 11.5
+        else:
+            assert (s["ms_per_launch_min"], s["ms_per_launch_max"]) == (5.0, 11.0)
+            assert s["ms_per_step"] == 23.0
